@@ -1,0 +1,189 @@
+/*
+ * moe.h -- C ABI of libmoe: the forward pass of a token-choice Mixture-of-Experts
+ * FFN layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (sources are web pages, cited by title and section):
+ *   [MoE-10]  niuwancheng.cn, "10. 混合专家 MoE：总参数与激活参数"
+ *   [Hardest] amazingdata.cn, essay "moe-routing-hardest"
+ *   [Arch]    wuaizhan.com, "MoE 混合专家架构原理拆解"
+ *   [Lesson]  hi-bin.com, "MoE为什么只激活一部分专家"
+ *
+ *   router logits  z = x . W_g^T (+ optional per-expert logit bias)
+ *   gate           softmax over the E experts, or an independent sigmoid per expert
+ *   top-k          the k best experts per token (best first, equal scores -> lower id)
+ *   weights        renormalised over the k selected (optional), times routed_scaling_factor
+ *   capacity       optional: cap = ceil(capacity_factor * T * k / E) assignments per
+ *                  expert; later (token, slot) assignments beyond it are dropped and
+ *                  contribute 0 (the token passes through the residual only)
+ *   dispatch       kept assignments laid out expert-contiguous, in token order
+ *   experts        SwiGLU FFN per expert: down( silu(gate(x)) * up(x) ), grouped GEMM
+ *   shared expert  optional, always active, weight 1, added to the routed sum
+ *   combine        y[t] = sum_j w[t,j] * expert_{idx[t,j]}(x[t]) (+ shared(x[t]))
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or synchronises on these paths.  Every call is asynchronous
+ *     on `stream` (a hipStream_t passed as void*; NULL = the null stream).
+ *   - Row-major, densely packed.  Storage is cfg->dtype for x, the weights, x_perm,
+ *     y_perm, y_shared and y; router_bias and topk_w are float32; every index array
+ *     is int32.  Arithmetic accumulates in float32 (bf16 MFMA or fp32 FMA).
+ *   - Device pointers must be 16-byte aligned.
+ *   - The configuration is checked on the host before anything is enqueued: a
+ *     non-zero status means nothing was launched.  A failed launch is reported as
+ *     MOE_ERR_HIP.  Nothing aborts, prints or throws across the ABI.
+ *   - Calls are stateless; concurrent calls are safe unless they share a
+ *     workspace or output buffers.
+ *
+ * Supported range: T >= 1, 1 <= k <= min(E, 16), E <= 1024, H and I multiples of
+ * 64, T*k + T < 2^31, n_shared in {0, 1} with I_shared == I when n_shared == 1.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* sizes outside the supported range */
+  MOE_ERR_UNSUPPORTED = 3, /* a valid option this build does not implement */
+  MOE_ERR_WORKSPACE = 4,   /* workspace missing or smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 5,         /* a HIP launch or runtime call failed */
+  MOE_ERR_ALIGN = 6        /* a device pointer is not 16-byte aligned */
+} moe_status;
+
+/* Gate of [MoE-10] "路由器怎样选专家：top-k 与两种门控": softmax over all experts
+ * (Mixtral, Qwen3) or an independent sigmoid per expert (DeepSeek-V3). */
+typedef enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 } moe_gate;
+
+/* Storage type of activations and weights; accumulation is always float32. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* The layer's options, named after the config.json fields of [MoE-10]
+ * (num_experts_per_tok, moe_intermediate_size, routed_scaling_factor). */
+typedef struct {
+  int64_t T;                    /* tokens in the batch */
+  int64_t H;                    /* hidden size */
+  int64_t I;                    /* moe_intermediate_size of a routed expert */
+  int64_t E;                    /* routed experts */
+  int64_t k;                    /* num_experts_per_tok */
+  int32_t gate;                 /* moe_gate */
+  int32_t renormalize;          /* 1: selected weights divided by their sum */
+  float routed_scaling_factor;  /* multiplies the routed weights (1.0; 2.5 for DeepSeek-V3) */
+  float capacity_factor;        /* <= 0: no limit; else cap = ceil(cf*T*k/E) */
+  int64_t n_shared;             /* 0 or 1 always-active shared expert */
+  int64_t I_shared;             /* its intermediate size (must equal I) */
+  int32_t dtype;                /* moe_dtype */
+} moe_config;
+
+/* Weights of one layer.  Layouts are [out, in], used as x @ W^T like the router
+ * of [MoE-10] "把一个大 FFN 换成一组小 FFN". */
+typedef struct {
+  const void *w_router;     /* [E, H] */
+  const float *router_bias; /* [E] float32 logit bias, or NULL */
+  const void *w_gate;       /* [E, I, H] */
+  const void *w_up;         /* [E, I, H] */
+  const void *w_down;       /* [E, H, I] */
+  const void *ws_gate;      /* [I_shared, H] shared expert, NULL when n_shared == 0 */
+  const void *ws_up;        /* [I_shared, H] */
+  const void *ws_down;      /* [H, I_shared] */
+} moe_weights;
+
+/* Optional routing outputs of moe_forward; every field may be NULL (then the
+ * workspace holds it). */
+typedef struct {
+  int32_t *topk_idx;     /* [T, k] selected experts, best first */
+  float *topk_w;         /* [T, k] combine weights */
+  int32_t *counts;       /* [E] demand per expert (assignments before capacity) */
+  int32_t *offsets;      /* [E + 1] exclusive scan of the kept load per expert */
+  int32_t *row_of_slot;  /* [T, k] row in expert-contiguous order, -1 if dropped */
+  int32_t *token_of_row; /* [T*k] token of each kept row; first offsets[E] valid */
+} moe_route_out;
+
+/* Human-readable name of a status code (static string). */
+const char *moe_status_str(moe_status s);
+
+/* Host only, touches no GPU: checks cfg against the supported range. */
+moe_status moe_validate(const moe_config *cfg);
+
+/* Host only: bytes of device workspace that moe_forward needs; the same size
+ * also serves moe_dispatch and moe_expert_ffn. */
+moe_status moe_workspace_size(const moe_config *cfg, size_t *bytes);
+
+/* Host only: per-expert capacity, ceil(capacity_factor*T*k/E) computed in double,
+ * or -1 when capacity_factor <= 0 (no limit) or cfg is invalid.
+ * [MoE-10] "负载不均：路由坍缩与丢 token": capacity = tokens / experts x factor,
+ * rounded up in the page's example; "tokens" is read as the T*k assignments. */
+int64_t moe_capacity(const moe_config *cfg);
+
+/* Host only: parameters of one MoE FFN layer from its shape.
+ * [MoE-10] "总参数和激活参数怎样算": total = E*3*H*I + E*H (router) + shared;
+ * active = k*3*H*I + E*H + shared. */
+moe_status moe_layer_params(const moe_config *cfg, int64_t *total, int64_t *active);
+
+/* Router GEMM fused with the gate and top-k ([MoE-10] "路由器怎样选专家",
+ * [Hardest] routing steps).  Reads x [T,H], w_router [E,H], router_bias [E]
+ * (float32, NULL = none); writes topk_idx [T,k] (best first; equal scores ->
+ * lower expert id) and topk_w [T,k] (renormalised if cfg->renormalize, times
+ * routed_scaling_factor). */
+moe_status moe_route(const moe_config *cfg, const void *x, const void *w_router,
+                     const float *router_bias, int32_t *topk_idx, float *topk_w,
+                     void *stream);
+
+/* Histogram, stable scan and capacity, then the gather ([MoE-10] simplified
+ * Mixtral block: the rows of each expert are collected; "负载不均": overflow is
+ * dropped).  Precondition: topk_idx in [0, E).  Writes counts [E] (demand),
+ * offsets [E+1] (kept rows per expert, scanned), row_of_slot [T,k] (-1 =
+ * dropped), token_of_row [T*k] (first offsets[E] valid) and, when x_perm is not
+ * NULL, x_perm [T*k, H] = x[token_of_row[row]] for the first offsets[E] rows.
+ * Ranks within an expert follow (token, slot) order, so every output is
+ * deterministic.  ws: workspace of at least moe_workspace_size() bytes. */
+moe_status moe_dispatch(const moe_config *cfg, const int32_t *topk_idx, const void *x,
+                        int32_t *counts, int32_t *offsets, int32_t *row_of_slot,
+                        int32_t *token_of_row, void *x_perm, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/* Grouped SwiGLU experts ([MoE-10] "把一个大 FFN 换成一组小 FFN": the tokens of
+ * one expert go through one batched GEMM).  Rows offsets[e]..offsets[e+1] of
+ * x_perm [*, H] go through expert e: y_perm[row] = W_down[e] . (silu(W_gate[e] .
+ * x) * (W_up[e] . x)).  offsets [E+1] is a DEVICE array; offsets[E] <= T*k.
+ * The shared expert alone is this call with E = 1, I = I_shared, offsets = {0, T}.
+ * ws: workspace of at least moe_workspace_size() bytes. */
+moe_status moe_expert_ffn(const moe_config *cfg, const void *x_perm, const int32_t *offsets,
+                          const void *w_gate, const void *w_up, const void *w_down,
+                          void *y_perm, void *ws, size_t ws_bytes, void *stream);
+
+/* Deterministic gate-weighted combine ([Lesson] "Router 怎样给 Token 选专家": y_t
+ * is the weighted sum of the selected experts' outputs; [MoE-10]
+ * "细粒度专家与共享专家": the shared output is added as is).
+ * y[t] = sum_{j=0..k-1, row_of_slot[t,j] >= 0} topk_w[t,j] * y_perm[row_of_slot[t,j]]
+ *        (+ y_shared[t] when y_shared is not NULL), accumulated in float32 in
+ * that fixed order, no atomics.  Dropped slots contribute exactly 0. */
+moe_status moe_combine(const moe_config *cfg, const void *y_perm, const int32_t *row_of_slot,
+                       const float *topk_w, const void *y_shared, void *y, void *stream);
+
+/* The whole layer: route, dispatch (gather fused into the expert GEMM's A-tile
+ * loader), grouped gate/up + SwiGLU, grouped down, combine; the shared expert
+ * runs as one more group over all T tokens.  y [T,H] is the FFN output only
+ * (the caller adds the residual).  route_out may be NULL. */
+moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
+                       moe_route_out *route_out, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_forward that also records `events` (an array of MOE_STAGE_EVENTS hipEvent_t
+ * created by the caller, or NULL) on `stream` around its stages, for timing:
+ * [0] before route, [1] after route, [2] after dispatch, [3] after gate/up,
+ * [4] after down, [5] after combine. */
+#define MOE_STAGE_EVENTS 6
+moe_status moe_forward_timed(const moe_config *cfg, const moe_weights *w, const void *x,
+                             void *y, moe_route_out *route_out, void *ws, size_t ws_bytes,
+                             void *stream, void *const *events);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

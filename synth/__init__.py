@@ -5,7 +5,9 @@ the layer's arithmetic (no routing, gating, GEMM or combine): the CPU oracle
 and the HIP library both consume the arrays it returns, bit for bit.
 
 Recipe (one independent PCG64 stream per tensor and per expert):
-    stream(cfg_id, tensor_id, expert_id) = PCG64(SeedSequence([2024, cfg_id, tensor_id, expert_id]))
+    stream(ns, tensor_id, expert_id) = PCG64(SeedSequence([2024, ns, tensor_id, expert_id]))
+with ns the workload's seed namespace (the decode workload reuses the prefill
+layer's weight namespace: the same layer at a different batch size)
     value = round_to_storage( float32(standard_normal) * float32(std) )
 with std = 1 for x, 1/sqrt(H) for the router and the gate/up projections,
 1/sqrt(I) for the down projection (fan-in scaling), and round_to_storage
@@ -51,7 +53,12 @@ class MoEShape:
     I_shared: int = 0
     dtype: int = BF16
     logit_skew: bool = False    # per-expert router bias 0.5*ln(1/(e+1))
-    cfg_id: int = 0             # seed namespace
+    cfg_id: int = 0             # seed namespace of x
+    weight_cfg_id: int = -1     # seed namespace of the weights (-1: same as cfg_id)
+
+    @property
+    def wid(self) -> int:
+        return self.cfg_id if self.weight_cfg_id < 0 else self.weight_cfg_id
 
     def with_(self, **kw) -> "MoEShape":
         return replace(self, **kw)
@@ -69,9 +76,10 @@ CONFIGS = {
     4: MoEShape("deepseek_v3_prefill_bf16", T=8192, H=7168, I=2048, E=256, k=8,
                 gate=GATE_SIGMOID, renormalize=True, routed_scaling_factor=2.5,
                 n_shared=1, I_shared=2048, dtype=BF16, cfg_id=4),
+    # decode through the same layer (same weights) as the prefill workload
     5: MoEShape("deepseek_v3_decode_bf16", T=16, H=7168, I=2048, E=256, k=8,
                 gate=GATE_SIGMOID, renormalize=True, routed_scaling_factor=2.5,
-                n_shared=1, I_shared=2048, dtype=BF16, cfg_id=5),
+                n_shared=1, I_shared=2048, dtype=BF16, cfg_id=5, weight_cfg_id=4),
 }
 
 
@@ -146,7 +154,7 @@ def make_inputs(s: MoEShape, *, with_experts: bool = True,
     T, H, I, E = s.T, s.H, s.I, s.E
     sd = _storage_dtype(s.dtype)
     x = draw(s.cfg_id, T_X, 0, (T, H), 1.0, s.dtype)
-    w_router = draw(s.cfg_id, T_ROUTER, 0, (E, H), 1.0 / math.sqrt(H), s.dtype)
+    w_router = draw(s.wid, T_ROUTER, 0, (E, H), 1.0 / math.sqrt(H), s.dtype)
     bias = router_skew_bias(E) if s.logit_skew else None
 
     if with_experts:
@@ -157,9 +165,7 @@ def make_inputs(s: MoEShape, *, with_experts: bool = True,
         w_gate = w_up = w_down = None
 
     def one(e):
-        g = draw(s.cfg_id, T_GATE, e, (I, H), 1.0 / math.sqrt(H), s.dtype)
-        u = draw(s.cfg_id, T_UP, e, (I, H), 1.0 / math.sqrt(H), s.dtype)
-        d = draw(s.cfg_id, T_DOWN, e, (H, I), 1.0 / math.sqrt(I), s.dtype)
+        g, u, d = expert_weights(s, e)
         if with_experts:
             w_gate[e] = g
             w_up[e] = u
@@ -178,14 +184,14 @@ def make_inputs(s: MoEShape, *, with_experts: bool = True,
     inp = MoEInputs(s, x, w_router, bias, w_gate, w_up, w_down)
     if s.n_shared:
         Is = s.I_shared or I
-        inp.ws_gate = draw(s.cfg_id, T_SGATE, 0, (Is, H), 1.0 / math.sqrt(H), s.dtype)
-        inp.ws_up = draw(s.cfg_id, T_SUP, 0, (Is, H), 1.0 / math.sqrt(H), s.dtype)
-        inp.ws_down = draw(s.cfg_id, T_SDOWN, 0, (H, Is), 1.0 / math.sqrt(Is), s.dtype)
+        inp.ws_gate = draw(s.wid, T_SGATE, 0, (Is, H), 1.0 / math.sqrt(H), s.dtype)
+        inp.ws_up = draw(s.wid, T_SUP, 0, (Is, H), 1.0 / math.sqrt(H), s.dtype)
+        inp.ws_down = draw(s.wid, T_SDOWN, 0, (H, Is), 1.0 / math.sqrt(Is), s.dtype)
     return inp
 
 
 def expert_weights(s: MoEShape, e: int):
     """Re-draw routed expert ``e``'s (w_gate, w_up, w_down) alone."""
-    return (draw(s.cfg_id, T_GATE, e, (s.I, s.H), 1.0 / math.sqrt(s.H), s.dtype),
-            draw(s.cfg_id, T_UP, e, (s.I, s.H), 1.0 / math.sqrt(s.H), s.dtype),
-            draw(s.cfg_id, T_DOWN, e, (s.H, s.I), 1.0 / math.sqrt(s.I), s.dtype))
+    return (draw(s.wid, T_GATE, e, (s.I, s.H), 1.0 / math.sqrt(s.H), s.dtype),
+            draw(s.wid, T_UP, e, (s.I, s.H), 1.0 / math.sqrt(s.H), s.dtype),
+            draw(s.wid, T_DOWN, e, (s.H, s.I), 1.0 / math.sqrt(s.I), s.dtype))

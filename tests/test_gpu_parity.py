@@ -1,0 +1,261 @@
+"""GPU parity: every entry point of the C ABI against the float64 oracle.
+
+Small shapes span several tiles and a ragged tail; the five layer workloads run
+at full size with outputs compared on sampled tokens (routing and dispatch on
+all tokens).  Comparison rules are documented in tests/moe_gpu.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_ref as ref
+import top_routing_expert_gemm_amd as moe
+from moe_gpu import (TOL, alloc_route, bits, check_rows, compare_dispatch, compare_routing, full_parity,
+                     gpu_forward, oracle_kwargs, require_gpu, widen_out, workspace)
+from synth import BF16, CONFIGS, F32, GATE_SIGMOID, GATE_SOFTMAX, MoEShape, make_inputs
+from synth.device import to_torch, upload
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "bf16_softmax_ragged": MoEShape("bf16_softmax_ragged", T=300, H=256, I=192, E=8, k=2, cfg_id=101),
+    "bf16_sigmoid_shared_2chunks": MoEShape("bf16_sigmoid_shared_2chunks", T=1000, H=512, I=320, E=16, k=4,
+                                            gate=GATE_SIGMOID, routed_scaling_factor=2.5, n_shared=1,
+                                            I_shared=320, cfg_id=102),
+    "bf16_capacity_skew": MoEShape("bf16_capacity_skew", T=777, H=128, I=128, E=64, k=1, renormalize=False,
+                                   capacity_factor=1.25, logit_skew=True, cfg_id=103),
+    "bf16_capacity_k3": MoEShape("bf16_capacity_k3", T=513, H=192, I=256, E=12, k=3, gate=GATE_SIGMOID,
+                                 capacity_factor=0.8, cfg_id=104),
+    "fp32_tiny": CONFIGS[1],
+    "fp32_sigmoid_shared_capacity": MoEShape("fp32_sigmoid_shared_capacity", T=200, H=192, I=128, E=8, k=3,
+                                             gate=GATE_SIGMOID, capacity_factor=1.0, n_shared=1, I_shared=128,
+                                             dtype=F32, cfg_id=105),
+    "bf16_single_token": MoEShape("bf16_single_token", T=1, H=64, I=64, E=1, k=1, cfg_id=106),
+    "fp32_single_token": MoEShape("fp32_single_token", T=1, H=64, I=64, E=1, k=1, dtype=F32, cfg_id=107),
+    "bf16_k_equals_E": MoEShape("bf16_k_equals_E", T=130, H=128, I=64, E=16, k=16, renormalize=False,
+                                cfg_id=108),
+    "bf16_max_E_max_k": MoEShape("bf16_max_E_max_k", T=70, H=128, I=64, E=1024, k=16, gate=GATE_SIGMOID,
+                                 cfg_id=109),
+    "fp32_E300": MoEShape("fp32_E300", T=40, H=64, I=64, E=300, k=5, dtype=F32, cfg_id=110),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(name):
+    s = SMALL[name]
+    inp = make_inputs(s)
+    res = full_parity(s, inp)
+    print(f"{name}: ties={res['ties']} worst_row_rel_err={res['worst']:.3e}")
+
+
+@pytest.mark.parametrize("name", ["bf16_softmax_ragged", "bf16_max_E_max_k", "fp32_E300",
+                                  "bf16_capacity_skew"])
+def test_route_stage(name):
+    s = SMALL[name]
+    inp = make_inputs(s, with_experts=False)
+    dev = {"x": to_torch(inp.x, "cuda"), "w_router": to_torch(inp.w_router, "cuda")}
+    bias = to_torch(inp.router_bias, "cuda") if inp.router_bias is not None else None
+    cfg = moe.config_from_shape(s)
+    r = alloc_route(s)
+    moe.route(cfg, dev["x"], dev["w_router"], bias, r["topk_idx"], r["topk_w"])
+    torch.cuda.synchronize()
+    rr = ref.route(inp.x, inp.w_router, inp.router_bias, s.k, s.gate, s.renormalize,
+                   float(np.float32(s.routed_scaling_factor)))
+    compare_routing(s, rr, bits(r["topk_idx"]), bits(r["topk_w"]))
+    # best first: GPU weights of one token never increase along the slots
+    w = bits(r["topk_w"])
+    assert np.all(np.diff(w, axis=1) <= 1e-6)
+
+
+def _dispatch_case(s, idx, with_gather=True):
+    """GPU moe_dispatch vs oracle dispatch on the same selection: bit-exact."""
+    inp = make_inputs(s, with_experts=False)
+    cfg = moe.config_from_shape(s)
+    idx_t = torch.from_numpy(idx.astype(np.int32)).cuda()
+    x = to_torch(inp.x, "cuda")
+    r = alloc_route(s)
+    dt = torch.bfloat16 if s.dtype == BF16 else torch.float32
+    xp = torch.full((s.T * s.k, s.H), -1.0, dtype=dt, device="cuda") if with_gather else None
+    ws = workspace(cfg)
+    moe.dispatch(cfg, idx_t, x if with_gather else None, r["counts"], r["offsets"], r["row_of_slot"],
+                 r["token_of_row"], xp, ws)
+    torch.cuda.synchronize()
+    cap = ref.expert_capacity(s.T, s.k, s.E, float(np.float32(s.capacity_factor)))
+    d = ref.dispatch(idx, s.E, cap)
+    assert np.array_equal(bits(r["counts"]), d["counts"])
+    assert np.array_equal(bits(r["offsets"]), d["offsets"])
+    assert np.array_equal(bits(r["row_of_slot"]), d["row_of_slot"])
+    R = int(d["offsets"][-1])
+    assert np.array_equal(bits(r["token_of_row"])[:R], d["token_of_row"])
+    if with_gather:
+        assert np.array_equal(bits(xp)[:R], ref.gather_rows(inp.x, d["token_of_row"]))
+    return d
+
+
+@pytest.mark.parametrize("case", ["uniform", "skewed_capacity", "one_expert", "tiny_capacity", "many_blocks"])
+def test_dispatch_stage(case):
+    rng = np.random.default_rng(hash(case) % 2 ** 32)
+    if case == "uniform":
+        s = MoEShape(case, T=1000, H=64, I=64, E=16, k=4, cfg_id=120)
+        idx = np.stack([rng.permutation(16)[:4] for _ in range(s.T)])
+    elif case == "skewed_capacity":
+        s = MoEShape(case, T=3000, H=128, I=64, E=64, k=1, capacity_factor=1.25, cfg_id=121)
+        idx = np.minimum(rng.geometric(0.08, size=(s.T, 1)) - 1, 63)
+    elif case == "one_expert":
+        s = MoEShape(case, T=700, H=64, I=64, E=8, k=1, cfg_id=122)
+        idx = np.full((s.T, 1), 5)
+    elif case == "tiny_capacity":
+        s = MoEShape(case, T=500, H=64, I=64, E=10, k=2, capacity_factor=0.01, cfg_id=123)
+        idx = np.stack([rng.permutation(10)[:2] for _ in range(s.T)])
+    else:  # more assignments than one histogram block, odd tail
+        s = MoEShape(case, T=9000, H=64, I=64, E=200, k=3, capacity_factor=1.1, cfg_id=124)
+        p = rng.dirichlet(np.ones(200) * 0.3)
+        idx = np.stack([rng.choice(200, 3, replace=False, p=p) for _ in range(s.T)])
+    d = _dispatch_case(s, idx)
+    if case == "tiny_capacity":
+        assert np.all(d["load"] <= 1)
+
+
+def test_expert_ffn_stage():
+    for s in (SMALL["bf16_sigmoid_shared_2chunks"], SMALL["fp32_sigmoid_shared_capacity"]):
+        inp = make_inputs(s)
+        dev = upload(inp)
+        cfg = moe.config_from_shape(s)
+        rr = ref.route(inp.x, inp.w_router, inp.router_bias, s.k, s.gate, s.renormalize, s.routed_scaling_factor)
+        d = ref.dispatch(rr["topk_idx"], s.E, ref.expert_capacity(s.T, s.k, s.E, s.capacity_factor))
+        R = int(d["offsets"][-1])
+        xp_host = np.zeros((s.T * s.k, s.H), dtype=inp.x.dtype)
+        xp_host[:R] = ref.gather_rows(inp.x, d["token_of_row"])
+        xp = to_torch(xp_host, "cuda")
+        off = torch.from_numpy(d["offsets"].astype(np.int32)).cuda()
+        dt = torch.bfloat16 if s.dtype == BF16 else torch.float32
+        yp = torch.zeros((s.T * s.k, s.H), dtype=dt, device="cuda")
+        ws = workspace(cfg)
+        moe.expert_ffn(cfg, xp, off, dev["w_gate"], dev["w_up"], dev["w_down"], yp, ws)
+        torch.cuda.synchronize()
+        want = ref.grouped_expert_ffn(xp_host[:R], d["offsets"], inp.w_gate, inp.w_up, inp.w_down)
+        check_rows(widen_out(yp)[:R], want, s.dtype, "expert_ffn " + s.name)
+        # the shared expert alone: E = 1, k = 1, I = I_shared, offsets = {0, T}
+        c1 = moe.make_config(s.T, s.H, s.I_shared, 1, 1, dtype=s.dtype)
+        ys = torch.zeros((s.T, s.H), dtype=dt, device="cuda")
+        off1 = torch.tensor([0, s.T], dtype=torch.int32, device="cuda")
+        moe.expert_ffn(c1, dev["x"], off1, dev["ws_gate"], dev["ws_up"], dev["ws_down"], ys, workspace(c1))
+        torch.cuda.synchronize()
+        check_rows(widen_out(ys), ref.swiglu_ffn(inp.x, inp.ws_gate, inp.ws_up, inp.ws_down), s.dtype,
+                   "shared expert " + s.name)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_combine_stage(dtype):
+    rng = np.random.default_rng(5)
+    T, H, k, R = 333, 256, 3, 900
+    s = MoEShape("combine", T=T, H=H, I=64, E=8, k=k, dtype=dtype)
+    yp = rng.normal(size=(T * k, H)).astype(np.float32)
+    ysh = rng.normal(size=(T, H)).astype(np.float32)
+    if dtype == BF16:
+        from synth import f32_to_bf16_bits
+        yp, ysh = f32_to_bf16_bits(yp), f32_to_bf16_bits(ysh)
+    ros = rng.permutation(T * k)[: T * k].reshape(T, k).astype(np.int32)
+    ros[ros >= R] = -1                       # about a third of the slots dropped
+    tw = rng.random((T, k)).astype(np.float32)
+    cfg = moe.config_from_shape(s)
+    dt = torch.bfloat16 if dtype == BF16 else torch.float32
+    for with_shared in (False, True):
+        y = torch.full((T, H), float("nan"), dtype=dt, device="cuda")
+        moe.combine(cfg, to_torch(yp, "cuda"), torch.from_numpy(ros).cuda(), torch.from_numpy(tw).cuda(),
+                    to_torch(ysh, "cuda") if with_shared else None, y)
+        torch.cuda.synchronize()
+        want = ref.combine(yp, ros, tw, ysh if with_shared else None)
+        tol = 8e-3 if dtype == BF16 else 1e-5   # bf16 output rounding only
+        e = check_rows(widen_out(y), want, dtype, "combine")
+        assert e <= tol
+
+
+def test_forward_is_deterministic():
+    s = SMALL["bf16_sigmoid_shared_2chunks"]
+    inp = make_inputs(s)
+    dev = upload(inp)
+    y1, r1 = gpu_forward(s, dev)
+    y2, r2 = gpu_forward(s, dev)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    for n in r1:
+        assert torch.equal(r1[n], r2[n]), n
+
+
+def test_all_tokens_to_one_expert():
+    s = MoEShape("hot_expert", T=600, H=128, I=128, E=8, k=1, cfg_id=130)
+    inp = make_inputs(s)
+    inp.router_bias = np.zeros(8, dtype=np.float32)
+    inp.router_bias[3] = 100.0
+    res = full_parity(s, inp)
+    assert np.all(bits(res["route"]["topk_idx"]) == 3)
+
+
+def test_tiny_capacity_drops_to_exact_zero():
+    s = MoEShape("tiny_cap", T=400, H=128, I=64, E=8, k=2, capacity_factor=0.02, cfg_id=131)
+    inp = make_inputs(s)
+    res = full_parity(s, inp)
+    y = widen_out(res["y"])
+    ros = bits(res["route"]["row_of_slot"])
+    dropped = np.all(ros < 0, axis=1)
+    assert dropped.sum() > 300 and np.all(y[dropped] == 0)
+
+
+def test_errors_launch_nothing():
+    s = SMALL["bf16_softmax_ragged"]
+    cfg = moe.config_from_shape(s)
+    x = torch.zeros((s.T, s.H), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros_like(x)
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(moe.MoeError) as ei:
+        moe.forward(cfg, {"w_router": x, "w_gate": x, "w_up": x, "w_down": x}, x, y, small_ws)
+    assert ei.value.status == 4
+    bad = moe.config_from_shape(s, k=9)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.forward(bad, {"w_router": x, "w_gate": x, "w_up": x, "w_down": x}, x, y, small_ws)
+    assert ei.value.status == 2
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y) == 0
+
+
+# ------------------------------------------------------- full-size workloads
+
+_cache = {}
+
+
+def _inputs(cid):
+    """Inputs of one workload; keeps at most one weight namespace resident."""
+    s = CONFIGS[cid]
+    if _cache.get("wid") != s.wid:
+        _cache.clear()
+        torch.cuda.empty_cache()
+        inp = make_inputs(s)
+        _cache.update(wid=s.wid, inp=inp, dev=upload(inp))
+        return s, inp, _cache["dev"]
+    base = _cache["inp"]
+    inp = make_inputs(s, with_experts=False)
+    for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+        setattr(inp, n, getattr(base, n))
+    dev = dict(_cache["dev"])
+    dev["x"] = to_torch(inp.x, "cuda")
+    return s, inp, dev
+
+
+@pytest.mark.parametrize("cid,n_sample", [(1, None), (2, 96), (3, 32), (4, 16), (5, None)])
+def test_forward_workload(cid, n_sample):
+    s, inp, dev = _inputs(cid)
+    res = full_parity(s, inp, dev=dev, n_sample=n_sample)
+    print(f"{s.name}: ties={res['ties']} worst_row_rel_err={res['worst']:.3e}")
+    if cid == 2:
+        ros = bits(res["route"]["row_of_slot"])
+        assert (ros < 0).sum() > 0, "the skewed capacity workload should drop tokens"
+    if cid == 5:
+        touched = int((bits(res["route"]["counts"]) > 0).sum())
+        print(f"decode: {touched} distinct experts touched (uniform model: "
+              f"{ref.expected_touched_experts(256, 8, 16):.1f})")
+        assert 80 <= touched <= 128

@@ -1,0 +1,316 @@
+// C ABI of libmoe: host-side validation, workspace layout and launch sequence.
+// The operations and their sources are documented in include/moe.h.
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline size_t esize(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
+
+// Device workspace of moe_forward; the stage entry points use the same layout.
+struct Layout {
+  size_t topk_idx, topk_w, counts, offsets, row_of_slot, token_of_row, dscratch, chunks, n_chunks, h, y_perm,
+      total;
+  int64_t rows;        // permuted row space: T*k routed rows, then T shared rows
+  int64_t max_chunks;  // chunk-list capacity
+};
+
+Layout layout(const moe_config* c) {
+  Layout L;
+  const int64_t Tk = c->T * c->k;
+  const int64_t sh = c->n_shared ? c->T : 0;
+  L.rows = Tk + sh;
+  L.max_chunks = max_chunks(Tk, c->E, sh, gemm_bm(c->dtype));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L.topk_idx = take((size_t)Tk * 4);
+  L.topk_w = take((size_t)Tk * 4);
+  L.counts = take((size_t)c->E * 4);
+  L.offsets = take((size_t)(c->E + 1) * 4);
+  L.row_of_slot = take((size_t)Tk * 4);
+  L.token_of_row = take((size_t)Tk * 4);
+  L.dscratch = take(dispatch_scratch_bytes(Tk, c->E));
+  L.chunks = take((size_t)L.max_chunks * sizeof(Chunk));
+  L.n_chunks = take(4);
+  L.h = take((size_t)L.rows * c->I * esize(c));
+  L.y_perm = take((size_t)L.rows * c->H * esize(c));
+  L.total = off;
+  return L;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+template <typename P>
+inline char* at(P* base, size_t off) {
+  return static_cast<char*>(static_cast<void*>(base)) + off;
+}
+
+inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
+
+moe_status check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
+  if (ws == nullptr) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < layout(c).total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                          \
+  do {                                         \
+    moe_status _s = (expr);                    \
+    if (_s != MOE_OK) return _s;               \
+  } while (0)
+#define HIP_TRY(expr)                          \
+  do {                                         \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+moe_status need(const void* p) { return p == nullptr ? MOE_ERR_NULL : (aligned16(p) ? MOE_OK : MOE_ERR_ALIGN); }
+moe_status opt(const void* p) { return p == nullptr || aligned16(p) ? MOE_OK : MOE_ERR_ALIGN; }
+
+int64_t cap_of(const moe_config* c) {
+  if (!(c->capacity_factor > 0.f)) return -1;
+  const double v = ceil((double)c->capacity_factor * (double)c->T * (double)c->k / (double)c->E);
+  return (int64_t)v;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer";
+    case MOE_ERR_SHAPE: return "shape outside the supported range";
+    case MOE_ERR_UNSUPPORTED: return "unsupported option";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+    case MOE_ERR_ALIGN: return "device pointer not 16-byte aligned";
+  }
+  return "unknown status";
+}
+
+moe_status moe_validate(const moe_config* c) {
+  if (c == nullptr) return MOE_ERR_NULL;
+  if (c->T < 1 || c->E < 1 || c->E > kMaxE || c->k < 1 || c->k > kMaxK || c->k > c->E) return MOE_ERR_SHAPE;
+  if (c->H < 64 || c->H % 64 != 0 || c->I < 64 || c->I % 64 != 0) return MOE_ERR_SHAPE;
+  if (c->gate != MOE_GATE_SOFTMAX && c->gate != MOE_GATE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_SHAPE;
+  if (!isfinite(c->routed_scaling_factor) || !isfinite(c->capacity_factor)) return MOE_ERR_SHAPE;
+  if (c->n_shared < 0 || c->n_shared > 1) return MOE_ERR_UNSUPPORTED;
+  if (c->n_shared == 1 && c->I_shared != c->I) return MOE_ERR_UNSUPPORTED;
+  const int64_t rows = c->T * c->k + c->T;
+  if (c->T > (int64_t(1) << 31) || rows >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  if (c->H > (int64_t(1) << 20) || c->I > (int64_t(1) << 20)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_size(const moe_config* c, size_t* bytes) {
+  MOE_TRY(moe_validate(c));
+  if (bytes == nullptr) return MOE_ERR_NULL;
+  *bytes = layout(c).total;
+  return MOE_OK;
+}
+
+int64_t moe_capacity(const moe_config* c) {
+  if (moe_validate(c) != MOE_OK) return -1;
+  return cap_of(c);
+}
+
+moe_status moe_layer_params(const moe_config* c, int64_t* total, int64_t* active) {
+  MOE_TRY(moe_validate(c));
+  if (total == nullptr || active == nullptr) return MOE_ERR_NULL;
+  const int64_t per_expert = 3 * c->H * c->I;
+  const int64_t router = c->E * c->H;
+  const int64_t shared = c->n_shared * 3 * c->H * c->I_shared;
+  *total = c->E * per_expert + router + shared;
+  *active = c->k * per_expert + router + shared;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* c, const void* x, const void* w_router, const float* router_bias,
+                     int32_t* topk_idx, float* topk_w, void* stream) {
+  MOE_TRY(moe_validate(c));
+  MOE_TRY(need(x));
+  MOE_TRY(need(w_router));
+  MOE_TRY(need(topk_idx));
+  MOE_TRY(need(topk_w));
+  MOE_TRY(opt(router_bias));
+  HIP_TRY(launch_route(*c, x, w_router, router_bias, topk_idx, topk_w, S(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_dispatch(const moe_config* c, const int32_t* topk_idx, const void* x, int32_t* counts,
+                        int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row, void* x_perm, void* ws,
+                        size_t ws_bytes, void* stream) {
+  MOE_TRY(moe_validate(c));
+  MOE_TRY(need(topk_idx));
+  MOE_TRY(need(counts));
+  MOE_TRY(need(offsets));
+  MOE_TRY(need(row_of_slot));
+  MOE_TRY(need(token_of_row));
+  MOE_TRY(opt(x_perm));
+  if (x_perm != nullptr) MOE_TRY(need(x));
+  MOE_TRY(check_ws(c, ws, ws_bytes));
+  const Layout L = layout(c);
+  HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), topk_idx, counts, offsets, row_of_slot, token_of_row,
+                          at(ws, L.dscratch), reinterpret_cast<Chunk*>(at(ws, L.chunks)),
+                          reinterpret_cast<int32_t*>(at(ws, L.n_chunks)), gemm_bm(c->dtype), 0, 0, S(stream)));
+  if (x_perm != nullptr)
+    HIP_TRY(launch_gather(x, token_of_row, offsets, c->E, c->T * c->k, c->H, c->dtype, x_perm, S(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* offsets, const void* w_gate,
+                          const void* w_up, const void* w_down, void* y_perm, void* ws, size_t ws_bytes,
+                          void* stream) {
+  MOE_TRY(moe_validate(c));
+  MOE_TRY(need(x_perm));
+  MOE_TRY(need(offsets));
+  MOE_TRY(need(w_gate));
+  MOE_TRY(need(w_up));
+  MOE_TRY(need(w_down));
+  MOE_TRY(need(y_perm));
+  MOE_TRY(check_ws(c, ws, ws_bytes));
+  const Layout L = layout(c);
+  const int bm = gemm_bm(c->dtype);
+  Chunk* chunks = reinterpret_cast<Chunk*>(at(ws, L.chunks));
+  int32_t* nch = reinterpret_cast<int32_t*>(at(ws, L.n_chunks));
+  HIP_TRY(launch_chunks_from_offsets(offsets, c->E, chunks, nch, bm, S(stream)));
+  GemmArgs g{};
+  g.A = x_perm;
+  g.gather = nullptr;
+  g.shared_row0 = 0;
+  g.chunks = chunks;
+  g.n_chunks = nch;
+  g.max_chunks = max_chunks(c->T * c->k, c->E, 0, bm);
+  g.w0 = w_gate;
+  g.w1 = w_up;
+  g.E = c->E;
+  g.K = c->H;
+  g.N = c->I;
+  g.out = at(ws, L.h);
+  HIP_TRY(launch_gateup(g, c->dtype, S(stream)));
+  g.A = at(ws, L.h);
+  g.w0 = w_down;
+  g.w1 = nullptr;
+  g.K = c->I;
+  g.N = c->H;
+  g.out = y_perm;
+  HIP_TRY(launch_down(g, c->dtype, S(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_config* c, const void* y_perm, const int32_t* row_of_slot, const float* topk_w,
+                       const void* y_shared, void* y, void* stream) {
+  MOE_TRY(moe_validate(c));
+  MOE_TRY(need(y_perm));
+  MOE_TRY(need(row_of_slot));
+  MOE_TRY(need(topk_w));
+  MOE_TRY(opt(y_shared));
+  MOE_TRY(need(y));
+  HIP_TRY(launch_combine(y_perm, row_of_slot, topk_w, y_shared, y, c->T, c->H, c->k, c->dtype, S(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const void* x, void* y,
+                             moe_route_out* ro, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  MOE_TRY(moe_validate(c));
+  if (w == nullptr) return MOE_ERR_NULL;
+  MOE_TRY(need(x));
+  MOE_TRY(need(y));
+  MOE_TRY(need(w->w_router));
+  MOE_TRY(opt(w->router_bias));
+  MOE_TRY(need(w->w_gate));
+  MOE_TRY(need(w->w_up));
+  MOE_TRY(need(w->w_down));
+  if (c->n_shared) {
+    MOE_TRY(need(w->ws_gate));
+    MOE_TRY(need(w->ws_up));
+    MOE_TRY(need(w->ws_down));
+  }
+  MOE_TRY(check_ws(c, ws, ws_bytes));
+  const Layout L = layout(c);
+  moe_route_out r{};
+  if (ro != nullptr) r = *ro;
+  if (r.topk_idx == nullptr) r.topk_idx = reinterpret_cast<int32_t*>(at(ws, L.topk_idx));
+  if (r.topk_w == nullptr) r.topk_w = reinterpret_cast<float*>(at(ws, L.topk_w));
+  if (r.counts == nullptr) r.counts = reinterpret_cast<int32_t*>(at(ws, L.counts));
+  if (r.offsets == nullptr) r.offsets = reinterpret_cast<int32_t*>(at(ws, L.offsets));
+  if (r.row_of_slot == nullptr) r.row_of_slot = reinterpret_cast<int32_t*>(at(ws, L.row_of_slot));
+  if (r.token_of_row == nullptr) r.token_of_row = reinterpret_cast<int32_t*>(at(ws, L.token_of_row));
+  MOE_TRY(need(r.topk_idx));
+  MOE_TRY(need(r.topk_w));
+  MOE_TRY(need(r.counts));
+  MOE_TRY(need(r.offsets));
+  MOE_TRY(need(r.row_of_slot));
+  MOE_TRY(need(r.token_of_row));
+
+  hipStream_t s = S(stream);
+  auto mark = [&](int i) -> hipError_t {
+    if (events == nullptr || events[i] == nullptr) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+  };
+  const int bm = gemm_bm(c->dtype);
+  const int64_t Tk = c->T * c->k;
+  const int64_t sh = c->n_shared ? c->T : 0;
+  Chunk* chunks = reinterpret_cast<Chunk*>(at(ws, L.chunks));
+  int32_t* nch = reinterpret_cast<int32_t*>(at(ws, L.n_chunks));
+
+  HIP_TRY(mark(0));
+  HIP_TRY(launch_route(*c, x, w->w_router, w->router_bias, r.topk_idx, r.topk_w, s));
+  HIP_TRY(mark(1));
+  HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), r.topk_idx, r.counts, r.offsets, r.row_of_slot,
+                          r.token_of_row, at(ws, L.dscratch), chunks, nch, bm, sh, Tk, s));
+  HIP_TRY(mark(2));
+  GemmArgs g{};
+  g.A = x;
+  g.gather = r.token_of_row;
+  g.shared_row0 = Tk;
+  g.chunks = chunks;
+  g.n_chunks = nch;
+  g.max_chunks = L.max_chunks;
+  g.w0 = w->w_gate;
+  g.w1 = w->w_up;
+  g.ws0 = w->ws_gate;
+  g.ws1 = w->ws_up;
+  g.E = c->E;
+  g.K = c->H;
+  g.N = c->I;
+  g.out = at(ws, L.h);
+  HIP_TRY(launch_gateup(g, c->dtype, s));
+  HIP_TRY(mark(3));
+  g.A = at(ws, L.h);
+  g.gather = nullptr;
+  g.w0 = w->w_down;
+  g.w1 = nullptr;
+  g.ws0 = w->ws_down;
+  g.ws1 = nullptr;
+  g.K = c->I;
+  g.N = c->H;
+  g.out = at(ws, L.y_perm);
+  HIP_TRY(launch_down(g, c->dtype, s));
+  HIP_TRY(mark(4));
+  const void* ysh = c->n_shared ? static_cast<const void*>(at(ws, L.y_perm + (size_t)Tk * c->H * esize(c))) : nullptr;
+  HIP_TRY(launch_combine(at(ws, L.y_perm), r.row_of_slot, r.topk_w, ysh, y, c->T, c->H, c->k, c->dtype, s));
+  HIP_TRY(mark(5));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* c, const moe_weights* w, const void* x, void* y, moe_route_out* ro,
+                       void* ws, size_t ws_bytes, void* stream) {
+  return moe_forward_timed(c, w, x, y, ro, ws, ws_bytes, stream, nullptr);
+}
+
+}  // extern "C"

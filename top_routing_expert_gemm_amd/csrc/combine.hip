@@ -1,0 +1,119 @@
+// Deterministic gate-weighted combine back to token order (gfx950).
+//
+// Sources: hi-bin.com "MoE为什么只激活一部分专家", section "Router 怎样给 Token
+// 选专家" (y_t is the weighted sum of the selected experts' outputs);
+// niuwancheng.cn "10. 混合专家 MoE：总参数与激活参数", section
+// "细粒度专家与共享专家" (the shared expert's output is added directly) and
+// section "负载不均：路由坍缩与丢 token" (a dropped token skips the expert).
+//
+// One workgroup per token (grid-stride): the k (row, weight) pairs of the token
+// are read once, then every thread accumulates 16-byte column vectors of the
+// selected y_perm rows in float32 in slot order j = 0..k-1, adds the shared row,
+// and stores.  A gather, not a scatter: no atomics, so the result is bitwise
+// reproducible.  HBM bound: reads (kept slots + shared) rows, writes one row.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ void acc_bf16x8(float (&acc)[8], const uint4& v, float w) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] = fmaf(w, __uint_as_float(u[i] << 16), acc[2 * i]);
+    acc[2 * i + 1] = fmaf(w, __uint_as_float(u[i] & 0xffff0000u), acc[2 * i + 1]);
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __restrict__ yp,
+                                                           const int32_t* __restrict__ ros,
+                                                           const float* __restrict__ tw,
+                                                           const uint16_t* __restrict__ ysh,
+                                                           uint16_t* __restrict__ y, int64_t T, int64_t H, int k) {
+  __shared__ int s_row[kMaxK];
+  __shared__ float s_w[kMaxK];
+  const int64_t hv = H / 8;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    if (threadIdx.x < k) {
+      s_row[threadIdx.x] = ros[t * k + threadIdx.x];
+      s_w[threadIdx.x] = tw[t * k + threadIdx.x];
+    }
+    __syncthreads();
+    for (int64_t c = threadIdx.x; c < hv; c += blockDim.x) {
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int row = s_row[j];
+        if (row < 0) continue;  // dropped slot: contributes exactly 0
+        acc_bf16x8(acc, reinterpret_cast<const uint4*>(yp + (int64_t)row * H)[c], s_w[j]);
+      }
+      if (ysh != nullptr) acc_bf16x8(acc, reinterpret_cast<const uint4*>(ysh + t * H)[c], 1.f);
+      uint4 o;
+      o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+      o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+      o.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
+      o.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+      reinterpret_cast<uint4*>(y + t * H)[c] = o;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restrict__ yp,
+                                                          const int32_t* __restrict__ ros,
+                                                          const float* __restrict__ tw,
+                                                          const float* __restrict__ ysh, float* __restrict__ y,
+                                                          int64_t T, int64_t H, int k) {
+  __shared__ int s_row[kMaxK];
+  __shared__ float s_w[kMaxK];
+  const int64_t hv = H / 4;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    if (threadIdx.x < k) {
+      s_row[threadIdx.x] = ros[t * k + threadIdx.x];
+      s_w[threadIdx.x] = tw[t * k + threadIdx.x];
+    }
+    __syncthreads();
+    for (int64_t c = threadIdx.x; c < hv; c += blockDim.x) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < k; ++j) {
+        const int row = s_row[j];
+        if (row < 0) continue;
+        const float4 v = reinterpret_cast<const float4*>(yp + (int64_t)row * H)[c];
+        const float w = s_w[j];
+        acc.x = fmaf(w, v.x, acc.x);
+        acc.y = fmaf(w, v.y, acc.y);
+        acc.z = fmaf(w, v.z, acc.z);
+        acc.w = fmaf(w, v.w, acc.w);
+      }
+      if (ysh != nullptr) {
+        const float4 v = reinterpret_cast<const float4*>(ysh + t * H)[c];
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+      reinterpret_cast<float4*>(y + t * H)[c] = acc;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y_perm, const int32_t* row_of_slot, const float* topk_w,
+                          const void* y_shared, void* y, int64_t T, int64_t H, int64_t k, int dtype,
+                          hipStream_t s) {
+  const unsigned grid = (unsigned)std::min<int64_t>(T, 8192);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_bf16_kernel, dim3(grid), dim3(256), 0, s, static_cast<const uint16_t*>(y_perm),
+                       row_of_slot, topk_w, static_cast<const uint16_t*>(y_shared), static_cast<uint16_t*>(y), T,
+                       H, (int)k);
+  else
+    hipLaunchKernelGGL(combine_f32_kernel, dim3(grid), dim3(256), 0, s, static_cast<const float*>(y_perm),
+                       row_of_slot, topk_w, static_cast<const float*>(y_shared), static_cast<float*>(y), T, H,
+                       (int)k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

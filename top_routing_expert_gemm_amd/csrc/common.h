@@ -1,0 +1,97 @@
+// Internal declarations shared by the HIP translation units of libmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kMaxK = 16;
+constexpr int kMaxE = 1024;
+
+// Row-chunk of one expert group handled by one grouped-GEMM M-tile.
+struct Chunk {
+  int32_t group;  // expert id; == E for the shared expert
+  int32_t row0;   // first row in the permuted row space
+  int32_t nrows;  // rows in this chunk (1..BM)
+  int32_t pad;
+};
+
+// M-tile height of the bf16 grouped GEMM; chunk lists are cut to it.
+constexpr int kGemmBM = 256;
+// M-tile height of the fp32 grouped GEMM.
+constexpr int kGemmBMf32 = 64;
+
+inline int gemm_bm(int dtype) { return dtype == MOE_BF16 ? kGemmBM : kGemmBMf32; }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = static_cast<__bf16>(f);  // gfx950: v_cvt_pk_bf16_f32, round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// ---- launches (each returns hipGetLastError() of its launch) ----
+
+// Router GEMM + gate + top-k.  x, w: bf16 or fp32 per dtype.
+hipError_t launch_route(const moe_config& c, const void* x, const void* w, const float* bias,
+                        int32_t* topk_idx, float* topk_w, hipStream_t s);
+
+// Dispatch scratch sizes (bytes) for T*k assignments and E experts.
+size_t dispatch_scratch_bytes(int64_t Tk, int64_t E);
+// Max chunk-list entries for `rows_max` routed rows over E groups (+ shared rows).
+int64_t max_chunks(int64_t rows_max, int64_t E, int64_t shared_rows, int bm);
+
+// Histogram + scan + capacity + row maps; also writes the chunk list of the
+// routed groups (and the shared group when shared_rows > 0, starting at
+// shared_row0 in the row space).
+hipError_t launch_dispatch(int64_t T, int64_t k, int64_t E, int64_t cap, const int32_t* topk_idx,
+                           int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                           int32_t* token_of_row, void* scratch, Chunk* chunks, int32_t* n_chunks,
+                           int bm, int64_t shared_rows, int64_t shared_row0, hipStream_t s);
+
+// Chunk list from a device offsets array (stage API).
+hipError_t launch_chunks_from_offsets(const int32_t* offsets, int64_t E, Chunk* chunks,
+                                      int32_t* n_chunks, int bm, hipStream_t s);
+
+// x_perm[row] = x[token_of_row[row]] for row < offsets[E].
+hipError_t launch_gather(const void* x, const int32_t* token_of_row, const int32_t* offsets,
+                         int64_t E, int64_t rows_max, int64_t H, int dtype, void* x_perm,
+                         hipStream_t s);
+
+struct GemmArgs {
+  const void* A;            // activations: x (gathered) or x_perm / h (direct rows)
+  const int32_t* gather;    // token_of_row, or NULL: row r of A is row r of the row space
+  int64_t shared_row0;      // first row of the shared group in the row space (gather mode)
+  const Chunk* chunks;
+  const int32_t* n_chunks;  // device count of valid chunks
+  int64_t max_chunks;       // grid bound
+  const void* w0;           // gate (gate/up pass) or down weights, [E, N, K]
+  const void* w1;           // up weights (gate/up pass)
+  const void* ws0;          // shared expert's gate or down
+  const void* ws1;          // shared expert's up
+  int64_t E;
+  int64_t K;                // contraction length (H or I)
+  int64_t N;                // output columns (I or H)
+  void* out;                // [rows, N]
+};
+
+hipError_t launch_gateup(const GemmArgs& a, int dtype, hipStream_t s);
+hipError_t launch_down(const GemmArgs& a, int dtype, hipStream_t s);
+
+hipError_t launch_combine(const void* y_perm, const int32_t* row_of_slot, const float* topk_w,
+                          const void* y_shared, void* y, int64_t T, int64_t H, int64_t k,
+                          int dtype, hipStream_t s);
+
+}  // namespace moe

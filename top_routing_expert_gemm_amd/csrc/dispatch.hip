@@ -1,0 +1,242 @@
+// Histogram + stable scan + capacity, row maps, chunk lists and the row gather.
+//
+// Sources: niuwancheng.cn "10. 混合专家 MoE：总参数与激活参数", section
+// "把一个大 FFN 换成一组小 FFN" (the rows of each expert are collected and run as
+// one batched GEMM) and section "负载不均：路由坍缩与丢 token" (capacity =
+// tokens / experts x factor, rounded up; overflow tokens skip the expert);
+// amazingdata.cn "moe-routing-hardest" (expert-capacity paragraph).
+//
+// Determinism: the rank of an assignment inside its expert is the number of
+// earlier (token, slot) assignments to that expert.  It is computed without
+// relying on the order of atomics:
+//   1. hist_rank   one wave per block of CH consecutive assignments walks them in
+//                  order, 64 at a time; lanes with equal experts are grouped by a
+//                  ballot match and ranked by lane order; a per-block LDS counter
+//                  per expert carries the count across steps.  Emits the local rank
+//                  and the block histogram.
+//   2. scan        one workgroup: per expert, exclusive scan of the block histograms
+//                  (block bases), demand counts, load = min(count, cap), offsets =
+//                  exclusive scan of load, and the GEMM chunk list.
+//   3. finalize    rank = block base + local rank; kept iff rank < cap;
+//                  row_of_slot / token_of_row.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kScanThreads = 1024;
+
+inline int64_t hist_chunk(int64_t Tk) {
+  int64_t ch = 1024;
+  while ((Tk + ch - 1) / ch > 4096) ch *= 2;
+  return ch;
+}
+inline int64_t hist_blocks(int64_t Tk) {
+  const int64_t ch = hist_chunk(Tk);
+  return Tk == 0 ? 1 : (Tk + ch - 1) / ch;
+}
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+__global__ __launch_bounds__(64) void hist_rank_kernel(const int32_t* __restrict__ idx, int64_t Tk,
+                                                       int E, int64_t CH, int32_t* __restrict__ blk_counts,
+                                                       int32_t* __restrict__ rank_tmp) {
+  __shared__ int32_t cnt[kMaxE];
+  const int lane = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  __syncthreads();
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const int64_t begin = b * CH, end = min(begin + CH, Tk);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t base = begin; base < end; base += 64) {
+    const int64_t i = base + lane;
+    int e = i < end ? idx[i] : 0;
+    const bool valid = i < end && e >= 0 && e < E;  // out-of-range ids (a violated precondition) are skipped
+    if (!valid) e = 0;
+    uint64_t peers = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = (e >> bit) & 1;
+      const uint64_t bal = __ballot(valid && on);
+      peers &= on ? bal : ~bal;
+    }
+    const int before = __popcll(peers & lt);
+    const int old = valid ? cnt[e] : 0;
+    __syncthreads();  // every lane has read its counter before the leaders update
+    if (valid && before == 0) cnt[e] = old + __popcll(peers);
+    if (valid) rank_tmp[i] = old + before;
+    __syncthreads();
+  }
+  for (int e = lane; e < E; e += 64) blk_counts[b * E + e] = cnt[e];
+}
+
+// Inclusive scan over the block (one value per thread, blockDim.x == kScanThreads).
+__device__ int block_inclusive_scan(int v, int* tmp) {
+  const int tid = threadIdx.x;
+  tmp[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int add = tid >= off ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  const int r = tmp[tid];
+  __syncthreads();
+  return r;
+}
+
+// Chunk list of E groups with given loads and first rows, then (optionally) the
+// shared group over rows shared_row0 .. shared_row0 + shared_rows - 1.
+__device__ void emit_chunks(int e_valid, int load, int row0, int E, int bm, int64_t shared_rows,
+                            int64_t shared_row0, Chunk* chunks, int32_t* n_chunks, int* tmp) {
+  const int tid = threadIdx.x;
+  const int nch = e_valid ? (load + bm - 1) / bm : 0;
+  const int incl = block_inclusive_scan(nch, tmp);
+  const int base = incl - nch;
+  for (int c = 0; c < nch; ++c) {
+    Chunk ck;
+    ck.group = tid;
+    ck.row0 = row0 + c * bm;
+    ck.nrows = min(bm, load - c * bm);
+    ck.pad = 0;
+    chunks[base + c] = ck;
+  }
+  __shared__ int total;
+  if (tid == kScanThreads - 1) total = incl;
+  __syncthreads();
+  const int nsh = (int)((shared_rows + bm - 1) / bm);
+  for (int c = tid; c < nsh; c += kScanThreads) {
+    Chunk ck;
+    ck.group = E;
+    ck.row0 = (int)(shared_row0 + (int64_t)c * bm);
+    ck.nrows = (int)min((int64_t)bm, shared_rows - (int64_t)c * bm);
+    ck.pad = 0;
+    chunks[total + c] = ck;
+  }
+  if (tid == 0) *n_chunks = total + nsh;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(
+    int32_t* __restrict__ blk_counts, int64_t nb, int E, int64_t cap, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, Chunk* __restrict__ chunks, int32_t* __restrict__ n_chunks, int bm,
+    int64_t shared_rows, int64_t shared_row0) {
+  __shared__ int tmp[kScanThreads];
+  const int tid = threadIdx.x;
+  const int e = tid;
+  int load = 0;
+  if (e < E) {
+    int run = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+      const int c = blk_counts[b * E + e];
+      blk_counts[b * E + e] = run;  // exclusive block base
+      run += c;
+    }
+    counts[e] = run;
+    load = cap < 0 ? run : (int)min((int64_t)run, cap);
+  }
+  const int incl = block_inclusive_scan(load, tmp);
+  const int excl = incl - load;
+  if (e < E) offsets[e] = excl;
+  if (e == E - 1) offsets[E] = incl;
+  emit_chunks(e < E, load, excl, E, bm, shared_rows, shared_row0, chunks, n_chunks, tmp);
+}
+
+__global__ __launch_bounds__(256) void finalize_kernel(const int32_t* __restrict__ idx, int64_t Tk, int k,
+                                                       int E, int64_t CH, int64_t cap,
+                                                       const int32_t* __restrict__ blk_base,
+                                                       const int32_t* __restrict__ rank_tmp,
+                                                       const int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ row_of_slot,
+                                                       int32_t* __restrict__ token_of_row) {
+  const int64_t b = blockIdx.x;
+  const int64_t begin = b * CH, end = min(begin + CH, Tk);
+  for (int64_t i = begin + threadIdx.x; i < end; i += blockDim.x) {
+    const int e = idx[i];
+    if (e < 0 || e >= E) {  // violated precondition: never index with it
+      row_of_slot[i] = -1;
+      continue;
+    }
+    const int64_t r = (int64_t)blk_base[b * E + e] + rank_tmp[i];
+    if (cap < 0 || r < cap) {
+      const int row = offsets[e] + (int)r;
+      row_of_slot[i] = row;
+      token_of_row[row] = (int)(i / k);
+    } else {
+      row_of_slot[i] = -1;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void chunks_from_offsets_kernel(
+    const int32_t* __restrict__ offsets, int E, Chunk* __restrict__ chunks, int32_t* __restrict__ n_chunks,
+    int bm) {
+  __shared__ int tmp[kScanThreads];
+  const int e = threadIdx.x;
+  const int row0 = e < E ? offsets[e] : 0;
+  const int load = e < E ? offsets[e + 1] - row0 : 0;
+  emit_chunks(e < E, load, row0, E, bm, 0, 0, chunks, n_chunks, tmp);
+}
+
+template <typename V>
+__global__ __launch_bounds__(256) void gather_kernel(const V* __restrict__ x, const int32_t* __restrict__ tor,
+                                                     const int32_t* __restrict__ offsets, int E,
+                                                     int64_t rows_max, int64_t hv, V* __restrict__ xp) {
+  const int64_t n = offsets[E];
+  for (int64_t row = blockIdx.x; row < n && row < rows_max; row += gridDim.x) {
+    const V* src = x + (int64_t)tor[row] * hv;
+    V* dst = xp + row * hv;
+    for (int64_t c = threadIdx.x; c < hv; c += blockDim.x) dst[c] = src[c];
+  }
+}
+
+}  // namespace
+
+size_t dispatch_scratch_bytes(int64_t Tk, int64_t E) {
+  return align256((size_t)hist_blocks(Tk) * E * 4) + align256((size_t)(Tk > 0 ? Tk : 1) * 4);
+}
+
+int64_t max_chunks(int64_t rows_max, int64_t E, int64_t shared_rows, int bm) {
+  return E + (rows_max + bm - 1) / bm + (shared_rows + bm - 1) / bm + 1;
+}
+
+hipError_t launch_dispatch(int64_t T, int64_t k, int64_t E, int64_t cap, const int32_t* topk_idx,
+                           int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                           int32_t* token_of_row, void* scratch, Chunk* chunks, int32_t* n_chunks,
+                           int bm, int64_t shared_rows, int64_t shared_row0, hipStream_t s) {
+  const int64_t Tk = T * k;
+  const int64_t ch = hist_chunk(Tk);
+  const int64_t nb = hist_blocks(Tk);
+  int32_t* blk = static_cast<int32_t*>(scratch);
+  int32_t* rank_tmp = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + align256((size_t)nb * E * 4));
+  hipLaunchKernelGGL(hist_rank_kernel, dim3((unsigned)nb), dim3(64), 0, s, topk_idx, Tk, (int)E, ch, blk,
+                     rank_tmp);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk, nb, (int)E, cap, counts, offsets,
+                     chunks, n_chunks, bm, shared_rows, shared_row0);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)nb), dim3(256), 0, s, topk_idx, Tk, (int)k, (int)E, ch,
+                     cap, blk, rank_tmp, offsets, row_of_slot, token_of_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunks_from_offsets(const int32_t* offsets, int64_t E, Chunk* chunks, int32_t* n_chunks,
+                                      int bm, hipStream_t s) {
+  hipLaunchKernelGGL(chunks_from_offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, offsets, (int)E, chunks,
+                     n_chunks, bm);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void* x, const int32_t* token_of_row, const int32_t* offsets, int64_t E,
+                         int64_t rows_max, int64_t H, int dtype, void* x_perm, hipStream_t s) {
+  const int64_t bytes = H * (dtype == MOE_BF16 ? 2 : 4);
+  const int64_t hv = bytes / 16;  // H is a multiple of 64: rows are whole 16-byte vectors
+  const unsigned grid = (unsigned)std::min<int64_t>(std::max<int64_t>(rows_max, 1), 8192);
+  hipLaunchKernelGGL(gather_kernel<uint4>, dim3(grid), dim3(256), 0, s, static_cast<const uint4*>(x),
+                     token_of_row, offsets, (int)E, rows_max, hv, static_cast<uint4*>(x_perm));
+  return hipGetLastError();
+}
+
+}  // namespace moe

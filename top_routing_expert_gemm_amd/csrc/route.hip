@@ -1,0 +1,300 @@
+// Router GEMM fused with the gate and the top-k selection (gfx950).
+//
+// Sources: niuwancheng.cn "10. 混合专家 MoE：总参数与激活参数", sections
+// "把一个大 FFN 换成一组小 FFN" (router = one linear layer x @ W_router.T) and
+// "路由器怎样选专家：top-k 与两种门控" (softmax / sigmoid gate, top-k,
+// renormalisation, routed_scaling_factor); amazingdata.cn "moe-routing-hardest"
+// (the routing steps).
+//
+// bf16 path: one workgroup = 32 tokens x all E experts.  The 32 x 64 token tile is
+// staged in LDS (double buffered, XOR-swizzled 16-byte chunks) and shared by the
+// four waves; each wave streams its own 32-expert blocks of W_router straight
+// into MFMA operand registers and accumulates z = x . W^T with
+// v_mfma_f32_32x32x16_bf16 in fp32.  The logits tile goes to LDS only; each wave
+// then runs the gate and top-k for 8 tokens with wave-wide reductions and writes
+// just topk_idx / topk_w.
+#include <math.h>
+
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRBM = 32;   // tokens per workgroup
+constexpr int kRBK = 64;   // K step
+constexpr int kRThreads = 256;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+// Larger value wins; equal values -> lower expert index.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    float v2 = __shfl_xor(v, off, kWave);
+    int i2 = __shfl_xor(i, off, kWave);
+    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+  }
+}
+
+// Gate + top-k of one token, run by one whole wave.  z[v] holds the logit of
+// expert lane + 64 v (-inf past E).  Both gates are increasing functions of z,
+// so the k best scores are the k largest logits; selection is done on z, which
+// keeps full fp32 resolution.
+template <int VPL>
+__device__ void topk_token(float (&z)[VPL], int E, int k, int gate, int renorm, float scale,
+                           int32_t* out_idx, float* out_w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  bool taken[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) taken[v] = false;
+  float selz = -INFINITY;
+  int seli = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = lane + kWave * v;
+      if (e < E && !taken[v] && (z[v] > bv || bi == 0x7fffffff)) { bv = z[v]; bi = e; }
+    }
+    wave_argmax(bv, bi);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (lane + kWave * v == bi) taken[v] = true;
+    if (lane == j) { selz = bv; seli = bi; }
+  }
+  const bool mine = lane < k;
+  float w;
+  if (gate == MOE_GATE_SOFTMAX) {
+    if (renorm) {
+      // p_j / sum_sel p = exp(z_j - z_best) / sum_sel exp(z - z_best)
+      const float zbest = __shfl(selz, 0, kWave);
+      const float ex = mine ? expf(selz - zbest) : 0.f;
+      w = ex / wave_sum(ex);
+    } else {
+      // full softmax over all E experts
+      float m = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        if (lane + kWave * v < E) m = fmaxf(m, z[v]);
+      m = wave_max(m);
+      float s = 0.f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        if (lane + kWave * v < E) s += expf(z[v] - m);
+      s = wave_sum(s);
+      w = mine ? expf(selz - m) / s : 0.f;
+    }
+  } else {
+    const float sg = mine ? 1.f / (1.f + expf(-selz)) : 0.f;
+    w = renorm ? sg / wave_sum(sg) : sg;
+  }
+  if (mine) {
+    out_idx[lane] = seli;
+    out_w[lane] = w * scale;
+  }
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// NBW: 32-expert blocks per wave (E <= 128 * NBW).
+template <int NBW>
+__global__ __launch_bounds__(kRThreads) void route_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias,
+    int T, int H, int E, int k, int gate, int renorm, float scale, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
+  constexpr int VPL = 2 * NBW;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  uint16_t* As = reinterpret_cast<uint16_t*>(smem);                 // [2][32][64] bf16
+  float* lg = reinterpret_cast<float*>(smem + 2 * kRBM * kRBK * 2);  // [32][lde]
+  const int nblk = (E + 31) / 32;
+  const int lde = nblk * 32 + 4;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * kRBM;
+
+  // A staging: thread -> (row tid/8, 16-byte chunk tid%8)
+  const int ar = tid >> 3, ac = tid & 7;
+  const uint16_t* aptr = x + (int64_t)min(t0 + ar, T - 1) * H + ac * 8;
+  const int a_lds = ar * kRBK + ((ac ^ (ar & 7)) * 8);
+
+  // B operand rows of this wave's blocks: lane -> expert (lane & 31), k half (lane >> 5)
+  const uint16_t* bptr[NBW];
+  bool bval[NBW];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const int blk = wave + 4 * i;
+    bval[i] = blk < nblk;
+    const int e = min(blk * 32 + (lane & 31), E - 1);
+    bptr[i] = w + (int64_t)e * H + (lane >> 5) * 32;
+  }
+
+  f32x16 acc[NBW];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+
+  const int nk = H / kRBK;
+  uint4 apf = ldg16(aptr);
+  uint4 bcur[NBW][4];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i)
+    if (bval[i])
+#pragma unroll
+      for (int s = 0; s < 4; ++s) bcur[i][s] = ldg16(bptr[i] + s * 8);
+  *reinterpret_cast<uint4*>(As + a_lds) = apf;
+  __syncthreads();
+
+  const int arow = lane & 31;
+  for (int kt = 0; kt < nk; ++kt) {
+    uint4 bnext[NBW][4];
+    const bool more = kt + 1 < nk;
+    if (more) {
+      apf = ldg16(aptr + (kt + 1) * kRBK);
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+        if (bval[i])
+#pragma unroll
+          for (int s = 0; s < 4; ++s) bnext[i][s] = ldg16(bptr[i] + (kt + 1) * kRBK + s * 8);
+    }
+    const uint16_t* Ab = As + (kt & 1) * kRBM * kRBK;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      // substep s, lane half h: k = h*32 + s*8 .. +8 (same permutation as the B loads)
+      const int chunk = (lane >> 5) * 4 + s;
+      const uint4 a = *reinterpret_cast<const uint4*>(Ab + arow * kRBK + ((chunk ^ (arow & 7)) * 8));
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+        if (bval[i])
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, bcur[i][s]),
+                                                           acc[i], 0, 0, 0);
+    }
+    if (more) {
+      *reinterpret_cast<uint4*>(As + ((kt + 1) & 1) * kRBM * kRBK + a_lds) = apf;
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bcur[i][s] = bnext[i][s];
+    }
+    __syncthreads();
+  }
+
+  // logits tile -> LDS: lane holds expert column (lane & 31) of each block and
+  // token rows 8g + 4*(lane >> 5) + r of the 32x32 MFMA result.
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    if (!bval[i]) continue;
+    const int e = (wave + 4 * i) * 32 + (lane & 31);
+    const float b = (bias != nullptr && e < E) ? bias[e] : 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 8 * g + 4 * (lane >> 5) + r;
+        lg[row * lde + e] = acc[i][4 * g + r] + b;
+      }
+  }
+  __syncthreads();
+
+  for (int row = wave; row < kRBM; row += 4) {
+    const int t = t0 + row;
+    if (t >= T) break;
+    float z[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = lane + kWave * v;
+      z[v] = e < E ? lg[row * lde + e] : -INFINITY;
+    }
+    topk_token<VPL>(z, E, k, gate, renorm, scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
+  }
+}
+
+// fp32 path: one wave per token computes its E logits with lane-strided dot
+// products and a fixed-order wave reduction, then runs the same gate / top-k.
+template <int VPL>
+__global__ __launch_bounds__(kRThreads) void route_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias, int T,
+    int H, int E, int k, int gate, int renorm, float scale, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kRThreads / kWave) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float4* xr = reinterpret_cast<const float4*>(x + (int64_t)t * H);
+  float z[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    z[v] = -INFINITY;
+    for (int el = 0; el < kWave; ++el) {
+      const int e = v * kWave + el;
+      if (e >= E) break;
+      const float4* wr = reinterpret_cast<const float4*>(w + (int64_t)e * H);
+      float s = 0.f;
+      for (int h4 = lane; h4 < H / 4; h4 += kWave) {
+        const float4 a = xr[h4], b = wr[h4];
+        s = fmaf(a.x, b.x, s);
+        s = fmaf(a.y, b.y, s);
+        s = fmaf(a.z, b.z, s);
+        s = fmaf(a.w, b.w, s);
+      }
+      s = wave_sum(s);
+      if (bias != nullptr) s += bias[e];
+      if (lane == el) z[v] = s;
+    }
+  }
+  topk_token<VPL>(z, E, k, gate, renorm, scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
+}
+
+template <int NBW>
+hipError_t launch_route_bf16(const moe_config& c, const void* x, const void* w, const float* bias,
+                             int32_t* idx, float* tw, hipStream_t s) {
+  const int nblk = (int)((c.E + 31) / 32);
+  const size_t lds = 2 * kRBM * kRBK * 2 + (size_t)kRBM * (nblk * 32 + 4) * 4;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_bf16_kernel<NBW>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int grid = (int)((c.T + kRBM - 1) / kRBM);
+  hipLaunchKernelGGL(route_bf16_kernel<NBW>, dim3(grid), dim3(kRThreads), lds, s,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias, (int)c.T,
+                     (int)c.H, (int)c.E, (int)c.k, c.gate, c.renormalize, c.routed_scaling_factor, idx, tw);
+  return hipGetLastError();
+}
+
+template <int VPL>
+hipError_t launch_route_f32(const moe_config& c, const void* x, const void* w, const float* bias,
+                            int32_t* idx, float* tw, hipStream_t s) {
+  const int per = kRThreads / kWave;
+  const int grid = (int)((c.T + per - 1) / per);
+  hipLaunchKernelGGL(route_f32_kernel<VPL>, dim3(grid), dim3(kRThreads), 0, s,
+                     static_cast<const float*>(x), static_cast<const float*>(w), bias, (int)c.T,
+                     (int)c.H, (int)c.E, (int)c.k, c.gate, c.renormalize, c.routed_scaling_factor, idx, tw);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const moe_config& c, const void* x, const void* w, const float* bias,
+                        int32_t* topk_idx, float* topk_w, hipStream_t s) {
+  if (c.dtype == MOE_BF16) {
+    if (c.E <= 128) return launch_route_bf16<1>(c, x, w, bias, topk_idx, topk_w, s);
+    if (c.E <= 256) return launch_route_bf16<2>(c, x, w, bias, topk_idx, topk_w, s);
+    if (c.E <= 512) return launch_route_bf16<4>(c, x, w, bias, topk_idx, topk_w, s);
+    return launch_route_bf16<8>(c, x, w, bias, topk_idx, topk_w, s);
+  }
+  if (c.E <= 64) return launch_route_f32<1>(c, x, w, bias, topk_idx, topk_w, s);
+  if (c.E <= 256) return launch_route_f32<4>(c, x, w, bias, topk_idx, topk_w, s);
+  return launch_route_f32<16>(c, x, w, bias, topk_idx, topk_w, s);
+}
+
+}  // namespace moe
