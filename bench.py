@@ -1,0 +1,198 @@
+"""Benchmark: MoE-layer tokens/s and grouped-GEMM TFLOP/s on one MI355X.
+
+Workload: the DeepSeek-V3-shaped prefill layer (T=8192 tokens, H=7168,
+moe_intermediate=2048, 256 routed experts top-8 sigmoid x2.5 + 1 shared expert,
+bf16 storage, fp32 accumulation), synthetic seeded inputs resident in HBM.
+A step is one moe_forward: route, dispatch, gate/up + SwiGLU, down, combine.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+
+Prints one JSON line.  The dominant kernel (the gate/up grouped GEMM) is timed
+with HIP events recorded on the layer's stream around it in every timed step.
+The decode layer (T=16 through the same weights) is timed too and reported
+under "decode".  The CPU baseline is the float64 oracle on a bounded sample of
+the same workload, on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_traffic_deepseek_v3_prefill.json")
+GEMM_SRC = os.path.join(ROOT, "top_routing_expert_gemm_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--cpu-sample-tokens", type=int, default=16)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    return p.parse_args()
+
+
+def src_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_entry(kernel_ms):
+    """HBM bytes per launch of the gate/up GEMM from the committed counter runs, if still current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha256") != src_sha(GEMM_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def timed_forward(moe, torch, cfg, dev, x, y, ws, route, steps, warmup):
+    """Warmup, then `steps` timed moe_forward calls with stage events; returns (seconds, stage ms lists)."""
+    for _ in range(warmup):
+        moe.forward(cfg, dev, x, y, ws, route_out=route)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.STAGE_EVENTS)] for _ in range(steps)]
+    for row in evs:   # materialise the HIP events before they are handed to the library
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moe.forward(cfg, dev, x, y, ws, route_out=route, events=evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    names = ["route", "dispatch", "gateup", "down", "combine"]
+    stages = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)] for j, n in enumerate(names)}
+    return t1 - t0, stages
+
+
+def cpu_baseline(inp, s, n_tok):
+    """The float64 oracle, as it stands, on the first n_tok tokens of the batch as a layer of their own."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle.moe_ref as ref
+    x = inp.x[:n_tok]
+    shared = (inp.ws_gate, inp.ws_up, inp.ws_down)
+    t0 = time.perf_counter()
+    ref.moe_forward(x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down, k=s.k, gate=s.gate,
+                    renormalize=s.renormalize, routed_scaling_factor=s.routed_scaling_factor,
+                    capacity_factor=s.capacity_factor, shared=shared)
+    dt = time.perf_counter() - t0
+    blas = [i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tok} tokens of the {s.T}-token batch run through the whole layer "
+                      f"(route, dispatch, touched experts + shared, combine) in float64; {dt:.1f} s; "
+                      f"host cpus {len(os.sched_getaffinity(0))}, BLAS threads {cores}"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print("bench.py: only --gpus 1 is supported (single-GPU layer; no collectives)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import top_routing_expert_gemm_amd as moe
+    from synth import CONFIGS, make_inputs
+    from synth.device import bits, to_torch, upload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.lib()
+    s = CONFIGS[4]
+    t_gen = time.perf_counter()
+    inp = make_inputs(s)
+    dev = upload(inp)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] inputs generated and uploaded in {t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    cfg = moe.config_from_shape(s)
+    x = dev["x"]
+    y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    route = {"topk_idx": torch.empty((s.T, s.k), dtype=torch.int32, device="cuda"),
+             "topk_w": torch.empty((s.T, s.k), dtype=torch.float32, device="cuda"),
+             "counts": torch.empty((s.E,), dtype=torch.int32, device="cuda"),
+             "offsets": torch.empty((s.E + 1,), dtype=torch.int32, device="cuda"),
+             "row_of_slot": torch.empty((s.T, s.k), dtype=torch.int32, device="cuda"),
+             "token_of_row": torch.empty((s.T * s.k,), dtype=torch.int32, device="cuda")}
+
+    secs, st = timed_forward(moe, torch, cfg, dev, x, y, ws, route, a.steps, a.warmup)
+    ms_step = secs / a.steps * 1e3
+    tokens_per_s = s.T * a.steps / secs
+    print(f"[bench] {a.steps} steps in {secs:.3f} s", file=sys.stderr, flush=True)
+
+    counts = bits(route["counts"])
+    R = int(bits(route["offsets"])[-1])
+    rows = R + s.T * s.n_shared
+    fl_gateup = 2.0 * rows * s.H * 2 * s.I
+    fl_down = 2.0 * rows * s.I * s.H
+    avg = {n: float(np.mean(v)) for n, v in st.items()}
+    gateup_tflops = fl_gateup / (avg["gateup"] * 1e-3) / 1e12
+    gemm_tflops = (fl_gateup + fl_down) / ((avg["gateup"] + avg["down"]) * 1e-3) / 1e12
+    traffic = traffic_entry(avg["gateup"])
+
+    out = {
+        "metric": "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), DeepSeek-V3 shape",
+        "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": s.name, "T": s.T, "H": s.H, "moe_intermediate": s.I, "E": s.E, "k": s.k,
+                   "gate": "sigmoid", "routed_scaling_factor": s.routed_scaling_factor, "n_shared": s.n_shared,
+                   "capacity_factor": None, "global_batch": s.T, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_bf16<gate/up+SwiGLU>",
+                     "achieved": gateup_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gateup_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "flops_per_launch": fl_gateup, "avg_launch_ms": avg["gateup"]},
+        "grouped_gemm": {"tflops": gemm_tflops, "frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS,
+                         "flops": fl_gateup + fl_down, "ms": avg["gateup"] + avg["down"]},
+        "stages_ms": avg,
+        "routing": {"kept_rows": R, "max_rows_per_expert": int(counts.max()), "min_rows_per_expert": int(counts.min())},
+    }
+
+    if not a.no_decode:
+        s5 = CONFIGS[5]
+        from synth import make_inputs as mk
+        inp5 = mk(s5, with_experts=False)
+        dev5 = dict(dev)
+        dev5["x"] = to_torch(inp5.x, "cuda")
+        cfg5 = moe.config_from_shape(s5)
+        y5 = torch.empty((s5.T, s5.H), dtype=torch.bfloat16, device="cuda")
+        ws5 = torch.empty(moe.workspace_size(cfg5), dtype=torch.uint8, device="cuda")
+        r5 = {"counts": torch.empty((s5.E,), dtype=torch.int32, device="cuda")}
+        steps5 = max(a.steps, 20)
+        secs5, st5 = timed_forward(moe, torch, cfg5, dev5, dev5["x"], y5, ws5, r5, steps5, a.warmup)
+        c5 = bits(r5["counts"])
+        touched = int((c5 > 0).sum())
+        per_expert = 3 * s5.H * s5.I * 2
+        wbytes = (touched + s5.n_shared) * per_expert + s5.E * s5.H * 2
+        ms5 = secs5 / steps5 * 1e3
+        gbps = wbytes / (ms5 * 1e-3) / 1e9
+        out["decode"] = {"workload": s5.name, "ms_per_step": ms5, "tokens_per_s": s5.T * steps5 / secs5,
+                         "touched_experts": touched, "weight_bytes": wbytes, "achieved_GBps": gbps,
+                         "frac_hbm_peak": gbps / PEAK_HBM_GBPS,
+                         "stages_ms": {n: float(np.mean(v)) for n, v in st5.items()}}
+
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, s, a.cpu_sample_tokens)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
