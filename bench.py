@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=16)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="also run one plain device copy of this many MiB (reference for HBM counters)")
     return p.parse_args()
 
 
@@ -132,6 +134,14 @@ def main():
              "offsets": torch.empty((s.E + 1,), dtype=torch.int32, device="cuda"),
              "row_of_slot": torch.empty((s.T, s.k), dtype=torch.int32, device="cuda"),
              "token_of_row": torch.empty((s.T * s.k,), dtype=torch.int32, device="cuda")}
+
+    if a.copy_calibration_mib > 0:
+        n = a.copy_calibration_mib * 2 ** 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     secs, st = timed_forward(moe, torch, cfg, dev, x, y, ws, route, a.steps, a.warmup)
     ms_step = secs / a.steps * 1e3

@@ -21,14 +21,16 @@ constexpr int kMaxE = 1024;
 
 // Row-chunk of one expert group handled by one grouped-GEMM M-tile.
 struct Chunk {
-  int32_t group;  // expert id; == E for the shared expert
-  int32_t row0;   // first row in the permuted row space
-  int32_t nrows;  // rows in this chunk (1..BM)
-  int32_t pad;
+  int32_t group;   // expert id; == E for the shared expert
+  int32_t row0;    // first row in the permuted row space
+  int32_t nrows;   // rows in this chunk (1..BM)
+  int32_t gfirst;  // index of the first chunk of this group in the list
+  int32_t gcount;  // chunks of this group
+  int32_t pad[3];
 };
 
 // M-tile height of the bf16 grouped GEMM; chunk lists are cut to it.
-constexpr int kGemmBM = 256;
+constexpr int kGemmBM = 320;
 // M-tile height of the fp32 grouped GEMM.
 constexpr int kGemmBMf32 = 64;
 

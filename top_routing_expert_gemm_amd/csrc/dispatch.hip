@@ -99,7 +99,9 @@ __device__ void emit_chunks(int e_valid, int load, int row0, int E, int bm, int6
     ck.group = tid;
     ck.row0 = row0 + c * bm;
     ck.nrows = min(bm, load - c * bm);
-    ck.pad = 0;
+    ck.gfirst = base;
+    ck.gcount = nch;
+    ck.pad[0] = ck.pad[1] = ck.pad[2] = 0;
     chunks[base + c] = ck;
   }
   __shared__ int total;
@@ -111,7 +113,9 @@ __device__ void emit_chunks(int e_valid, int load, int row0, int E, int bm, int6
     ck.group = E;
     ck.row0 = (int)(shared_row0 + (int64_t)c * bm);
     ck.nrows = (int)min((int64_t)bm, shared_rows - (int64_t)c * bm);
-    ck.pad = 0;
+    ck.gfirst = total;
+    ck.gcount = nsh;
+    ck.pad[0] = ck.pad[1] = ck.pad[2] = 0;
     chunks[total + c] = ck;
   }
   if (tid == 0) *n_chunks = total + nsh;

@@ -14,15 +14,22 @@
 // device-side tile count exit at once, so the grid is sized on the host for the
 // worst case and no host synchronisation is needed.
 //
-// bf16 tile: BM = 256 rows x BN = 128 weight rows x BK = 64, four waves in a
-// 2 x 2 grid, each wave 128 x 64 of v_mfma_f32_32x32x16_bf16 (fp32 accumulators).
-// Gate/up pass: the 128 weight rows are 64 gate rows and the same 64 up rows, and
-// every wave owns 32 gate columns and the matching 32 up columns, so each lane
-// holds gate and up of the same (row, i) and applies silu(g) * u in registers.
-// The A tile is gathered straight from x through token_of_row (the gather of the
-// dispatch step is fused into this loader) and both tiles are staged in LDS,
-// double buffered, with 16-byte chunks XOR-swizzled by row to avoid bank
-// conflicts on the MFMA operand reads.
+// bf16 tile: BM = 320 rows x BN = 256 weight rows x BK = 32, eight waves (two
+// per SIMD) in a 2 x 4 grid, each wave up to 160 x 64 of v_mfma_f32_32x32x16_bf16
+// (fp32 accumulators).  A 320-row chunk holds a whole routed expert of the large
+// workloads, so each expert's weights stream through one workgroup per n-tile.  Gate/up pass: the 256 weight rows are 128 gate rows and
+// the same 128 up rows; every wave owns 32 gate columns and the matching 32 up
+// columns, so each lane holds gate and up of the same (row, i) and applies
+// silu(g) * u in registers.  Down pass: 256 output columns.  The A tile is
+// gathered straight from x through token_of_row (the gather of the dispatch step
+// is fused into this loader).  Both tiles move global -> LDS with direct
+// (global_load_lds_dwordx4) loads through a four-stage pipeline, with 16-byte
+// chunks XOR-swizzled by row so the MFMA operand reads are free of bank
+// conflicts.
+//
+// Tile order: within one expert the chunks of an n-tile are adjacent (groups of
+// up to four chunks), so a second row chunk of an expert reads the same weight
+// tile right after the first, from L2.
 #include <math.h>
 
 #include "common.h"
@@ -30,14 +37,59 @@
 namespace moe {
 namespace {
 
-constexpr int BM = kGemmBM;  // 256
-constexpr int BN = 128;
-constexpr int BK = 64;
-constexpr int NT = 256;
-constexpr int A_LOADS = BM * BK / 8 / NT;  // 16-byte chunks per thread per K step (8)
-constexpr int B_LOADS = BN * BK / 8 / NT;  // (4)
+constexpr int BM = kGemmBM;  // 320 rows: one chunk holds a whole routed expert of the large workloads
+constexpr int BMW = BM / 2;  // rows per wave-row
+constexpr int RB = BMW / 32; // 32-row MFMA blocks per wave (5)
+constexpr int BN = 256;
+constexpr int NT = 512;
+constexpr int NWAVES = NT / 64;
+constexpr int SUPER = 4;     // chunks of one group interleaved per n-tile
+constexpr int BK = 32;
+constexpr int STAGES = 4;
+constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row (4)
+constexpr int RPB = 64 / CPR;               // tile rows per 1 KB direct-to-LDS block (16)
+constexpr int A_BLK = 3;                    // A blocks per wave per stage: 8 x 3 x 16 = 384 >= BM rows
+constexpr int BM_LD = NWAVES * A_BLK * RPB; // A rows staged per stage (rows >= BM are never read)
+constexpr int B_BLK = BN / RPB / NWAVES;    // (2)
+constexpr int LOADS_PER_STAGE = A_BLK + B_BLK;
+static_assert(BM_LD >= BM && BM % 32 == 0, "A staging");
+static_assert(STAGES * (BM_LD + BN) * BK * 2 <= 160 * 1024, "LDS");
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// One LDS array per pipeline stage: distinct objects let the compiler tell the
+// in-flight direct-to-LDS writes of one stage from the reads of another.
+__shared__ __attribute__((aligned(1024))) uint16_t sA0[BM_LD * BK];
+__shared__ __attribute__((aligned(1024))) uint16_t sA1[BM_LD * BK];
+__shared__ __attribute__((aligned(1024))) uint16_t sA2[BM_LD * BK];
+__shared__ __attribute__((aligned(1024))) uint16_t sA3[BM_LD * BK];
+__shared__ __attribute__((aligned(1024))) uint16_t sB0[BN * BK];
+__shared__ __attribute__((aligned(1024))) uint16_t sB1[BN * BK];
+__shared__ __attribute__((aligned(1024))) uint16_t sB2[BN * BK];
+__shared__ __attribute__((aligned(1024))) uint16_t sB3[BN * BK];
+
+template <int S>
+__device__ __forceinline__ uint16_t* stA() {
+  if constexpr (S == 0) return sA0;
+  else if constexpr (S == 1) return sA1;
+  else if constexpr (S == 2) return sA2;
+  else return sA3;
+}
+template <int S>
+__device__ __forceinline__ uint16_t* stB() {
+  if constexpr (S == 0) return sB0;
+  else if constexpr (S == 1) return sB1;
+  else if constexpr (S == 2) return sB2;
+  else return sB3;
+}
+
+// XOR swizzle of the four 16-byte chunks of a 64-byte tile row: the 16 lanes of
+// one ds_read_b128 cycle (rows r..r+15, one logical chunk) hit distinct banks on
+// a 64-bank LDS, and the 8 lanes of a 32-bank cycle do too.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 // Physical workgroup id -> logical tile id, XCD-contiguous; false past V.
 __device__ __forceinline__ bool xcd_map(int p, int V, int& L) {
@@ -48,155 +100,203 @@ __device__ __forceinline__ bool xcd_map(int p, int V, int& L) {
   return true;
 }
 
-__device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// Logical tile -> (chunk, n-tile): groups of up to SUPER chunks of one expert
+// take the n-tiles in turn, so they share each weight tile.
+__device__ __forceinline__ void tile_of(int L, int n_tiles, const Chunk* chunks, int& ci, int& nt) {
+  const int c0 = L / n_tiles;
+  const Chunk g = chunks[c0];
+  const int sb = (c0 - g.gfirst) / SUPER;
+  const int base = g.gfirst + sb * SUPER;
+  const int cnt = min(SUPER, g.gcount - sb * SUPER);
+  const int q = L - base * n_tiles;
+  nt = q / cnt;
+  ci = base + q % cnt;
+}
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + expf(-g)); }
 
+// Wait until at most N of this wave's vector-memory loads are outstanding and
+// its LDS reads are done, then barrier (no other fence: the stage buffers are
+// the only shared state).  The wait is the s_waitcnt builtin (not inline asm) so
+// the compiler's own wait-count tracking sees it and adds no wait of its own on
+// the direct-to-LDS loads still in flight for other stages.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));  // vmcnt(N) expcnt(7) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct Frag {
+  const uint16_t* ga[A_BLK];  // per-lane global source of each direct-to-LDS block
+  const uint16_t* gb[B_BLK];
+};
+
+template <int S>
+__device__ __forceinline__ void issue_stage(const Frag& f, int kt, int wave) {
+  const int ko = kt * BK;
+#pragma unroll
+  for (int i = 0; i < A_BLK; ++i)
+    __builtin_amdgcn_global_load_lds((glb_void*)(f.ga[i] + ko), (lds_void*)(stA<S>() + (wave * A_BLK + i) * 512),
+                                     16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < B_BLK; ++i)
+    __builtin_amdgcn_global_load_lds((glb_void*)(f.gb[i] + ko), (lds_void*)(stB<S>() + (wave * B_BLK + i) * 512),
+                                     16, 0, 0);
+}
+
+// NRB 32-row blocks x two 32-column blocks of this wave, one K step.
+template <int S, int NRB>
+__device__ __forceinline__ void compute_stage(f32x16 (&acc)[RB][2], int wrow0, const int (&brow)[2], int lane) {
+  const uint16_t* Ab = stA<S>();
+  const uint16_t* Bb = stB<S>();
+#pragma unroll
+  for (int s = 0; s < BK / 16; ++s) {
+    const int chunk = s * 2 + (lane >> 5);  // k = s*16 + (lane>>5)*8 .. +8
+    bf16x8 bv[2], av[NRB];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = brow[j];
+      bv[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bb + r * BK + ((chunk ^ swz(r)) * 8)));
+    }
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      const int r = wrow0 + i * 32 + (lane & 31);
+      av[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ab + r * BK + ((chunk ^ swz(r)) * 8)));
+    }
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// One pipeline step for k-step kt held in stage S: wait for its data, refill the
+// stage consumed one step earlier with k-step kt + STAGES - 1 (clamped to the
+// last k-step: every step issues exactly one stage of loads, so the number of
+// loads issued after k-step kt is always (STAGES - 2) stages and the wait count
+// is a constant), then compute.  Loads complete in issue order.
+template <int S, int NRB>
+__device__ __forceinline__ void pipe_step(const Frag& f, f32x16 (&acc)[RB][2], int kt, int nk, int wrow0,
+                                          const int (&brow)[2], int lane, int wave) {
+  stage_barrier<(STAGES - 2) * LOADS_PER_STAGE>();
+  issue_stage<(S + STAGES - 1) % STAGES>(f, min(kt + STAGES - 1, nk - 1), wave);
+  if constexpr (NRB > 0) compute_stage<S, NRB>(acc, wrow0, brow, lane);
+}
+
+// The pipelined K loop of one wave computing NRB row blocks.  Every variant runs
+// the same barriers and loads, so waves with different NRB stay in step.
+template <int NRB>
+__device__ __forceinline__ void k_loop(const Frag& f, f32x16 (&acc)[RB][2], int nk, int wrow0,
+                                       const int (&brow)[2], int lane, int wave) {
+  issue_stage<0>(f, 0, wave);
+  issue_stage<1>(f, min(1, nk - 1), wave);
+  issue_stage<2>(f, min(2, nk - 1), wave);
+  int kt = 0;
+  // whole groups of STAGES steps: no conditional memory traffic inside the loop
+  for (; kt + STAGES <= nk; kt += STAGES) {
+    pipe_step<0, NRB>(f, acc, kt, nk, wrow0, brow, lane, wave);
+    pipe_step<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
+    pipe_step<2, NRB>(f, acc, kt + 2, nk, wrow0, brow, lane, wave);
+    pipe_step<3, NRB>(f, acc, kt + 3, nk, wrow0, brow, lane, wave);
+  }
+  // tail (nk not a multiple of STAGES)
+  if (kt < nk) pipe_step<0, NRB>(f, acc, kt, nk, wrow0, brow, lane, wave);
+  if (kt + 1 < nk) pipe_step<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
+  if (kt + 2 < nk) pipe_step<2, NRB>(f, acc, kt + 2, nk, wrow0, brow, lane, wave);
+  // the clamped refills of the last steps are still in flight: let them land
+  // before the wave can retire
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+}
+
 template <int MODE>
 __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  uint16_t* As = reinterpret_cast<uint16_t*>(smem);          // [2][BM][BK]
-  uint16_t* Bs = As + 2 * BM * BK;                           // [2][BN][BK]
-
   const int V = *a.n_chunks * n_tiles;
   int L;
   if (!xcd_map(blockIdx.x, V, L)) return;
-  const int ci = L / n_tiles, nt = L % n_tiles;
+  int ci, nt;
+  tile_of(L, n_tiles, a.chunks, ci, nt);
   const Chunk ch = a.chunks[ci];
   const bool shared = ch.group == a.E;
   const int64_t K = a.K, N = a.N;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
-  // ---- global source pointers (fixed for the whole K loop) ----
-  const int lc = tid & 7;   // 16-byte chunk within the 64-wide K step
-  const int lr = tid >> 3;  // first tile row of this thread (+32 per load)
+  // ---- per-lane sources of the direct-to-LDS blocks ----
+  // block b holds tile rows b*RPB .. +RPB; lane -> row b*RPB + lane/CPR, physical
+  // chunk lane%CPR, which holds logical chunk (lane%CPR) ^ swz(row).  Rows past
+  // the chunk are clamped to its last row (loaded, never used).
+  Frag f;
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
-  const uint16_t* ap[A_LOADS];
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int r = min(lr + 32 * i, ch.nrows - 1);
-    const int64_t row = (int64_t)ch.row0 + r;
+  for (int i = 0; i < A_BLK; ++i) {
+    const int r = (wave * A_BLK + i) * RPB + lane / CPR;
+    const int c = (lane % CPR) ^ swz(r);
+    const int rc = min(r, ch.nrows - 1);
+    const int64_t row = (int64_t)ch.row0 + rc;
     int64_t src = row;
     if (a.gather != nullptr) src = shared ? row - a.shared_row0 : (int64_t)a.gather[row];
-    ap[i] = A + src * K + lc * 8;
+    f.ga[i] = A + src * K + c * 8;
   }
-  const uint16_t* bp[B_LOADS];
-  if (MODE == MODE_GATEUP) {
-    const uint16_t* Wg = static_cast<const uint16_t*>(shared ? a.ws0 : a.w0) +
-                         (shared ? 0 : (int64_t)ch.group * N * K);
-    const uint16_t* Wu = static_cast<const uint16_t*>(shared ? a.ws1 : a.w1) +
-                         (shared ? 0 : (int64_t)ch.group * N * K);
+  const int64_t goff = shared ? 0 : (int64_t)ch.group * N * K;
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-      const int r = lr + 32 * i;  // 0..127: rows < 64 gate, >= 64 up
-      const int64_t n = (int64_t)nt * 64 + (r & 63);
-      bp[i] = (r < 64 ? Wg : Wu) + n * K + lc * 8;
+  for (int i = 0; i < B_BLK; ++i) {
+    const int r = (wave * B_BLK + i) * RPB + lane / CPR;
+    const int c = (lane % CPR) ^ swz(r);
+    const uint16_t* W;
+    int64_t n;
+    if (MODE == MODE_GATEUP) {  // rows < 128: gate, >= 128: up, same 128 columns of I
+      W = static_cast<const uint16_t*>(r < 128 ? (shared ? a.ws0 : a.w0) : (shared ? a.ws1 : a.w1)) + goff;
+      n = min((int64_t)nt * 128 + (r & 127), N - 1);
+    } else {
+      W = static_cast<const uint16_t*>(shared ? a.ws0 : a.w0) + goff;
+      n = min((int64_t)nt * BN + r, N - 1);
     }
-  } else {
-    const uint16_t* Wd = static_cast<const uint16_t*>(shared ? a.ws0 : a.w0) +
-                         (shared ? 0 : (int64_t)ch.group * N * K);
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-      const int64_t n = min((int64_t)nt * BN + lr + 32 * i, N - 1);
-      bp[i] = Wd + n * K + lc * 8;
-    }
-  }
-  int a_st[A_LOADS], b_st[B_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int r = lr + 32 * i;
-    a_st[i] = r * BK + ((lc ^ (r & 7)) * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) {
-    const int r = lr + 32 * i;
-    b_st[i] = r * BK + ((lc ^ (r & 7)) * 8);
+    f.gb[i] = W + n * K + c * 8;
   }
 
-  // rows of this wave that hold real data (32-row blocks)
-  const int wrow0 = wm * 128;
-  const int nrb = max(0, min(4, (ch.nrows - wrow0 + 31) / 32));
+  // this wave's rows: wave-row wm covers tile rows wm*BMW .. +BMW; only the 32-row
+  // blocks that hold data are computed (NRB is a template argument of the loop)
+  const int wrow0 = wm * BMW;
+  const int nrb = max(0, min(RB, (ch.nrows - wrow0 + 31) / 32));
 
-  f32x16 acc[4][2];
+  f32x16 acc[RB][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // B operand tile rows of this wave
   int brow[2];
   if (MODE == MODE_GATEUP) {
-    brow[0] = wn * 32 + (lane & 31);       // gate
-    brow[1] = 64 + wn * 32 + (lane & 31);  // up
+    brow[0] = wn * 32 + (lane & 31);        // gate
+    brow[1] = 128 + wn * 32 + (lane & 31);  // up
   } else {
     brow[0] = wn * 64 + (lane & 31);
     brow[1] = wn * 64 + 32 + (lane & 31);
   }
 
   const int nk = (int)(K / BK);
-  uint4 ra[A_LOADS], rb[B_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) ra[i] = ldg16(ap[i]);
-#pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) rb[i] = ldg16(bp[i]);
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<uint4*>(As + a_st[i]) = ra[i];
-#pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<uint4*>(Bs + b_st[i]) = rb[i];
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int64_t ko = (int64_t)(kt + 1) * BK;
-#pragma unroll
-      for (int i = 0; i < A_LOADS; ++i) ra[i] = ldg16(ap[i] + ko);
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i) rb[i] = ldg16(bp[i] + ko);
-    }
-    const uint16_t* Ab = As + (kt & 1) * BM * BK;
-    const uint16_t* Bb = Bs + (kt & 1) * BN * BK;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int chunk = s * 2 + (lane >> 5);  // k = s*16 + (lane>>5)*8 .. +8
-      bf16x8 bv[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = brow[j];
-        bv[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bb + r * BK + ((chunk ^ (r & 7)) * 8)));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i < nrb) {
-          const int r = wrow0 + i * 32 + (lane & 31);
-          const bf16x8 av =
-              __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ab + r * BK + ((chunk ^ (r & 7)) * 8)));
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[j], acc[i][j], 0, 0, 0);
-        }
-      }
-    }
-    if (more) {
-      uint16_t* An = As + ((kt + 1) & 1) * BM * BK;
-      uint16_t* Bn = Bs + ((kt + 1) & 1) * BN * BK;
-#pragma unroll
-      for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<uint4*>(An + a_st[i]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<uint4*>(Bn + b_st[i]) = rb[i];
-    }
-    __syncthreads();
+  switch (nrb) {
+    case 0: k_loop<0>(f, acc, nk, wrow0, brow, lane, wave); break;
+    case 1: k_loop<1>(f, acc, nk, wrow0, brow, lane, wave); break;
+    case 2: k_loop<2>(f, acc, nk, wrow0, brow, lane, wave); break;
+    case 3: k_loop<3>(f, acc, nk, wrow0, brow, lane, wave); break;
+    case 4: k_loop<4>(f, acc, nk, wrow0, brow, lane, wave); break;
+    default: k_loop<5>(f, acc, nk, wrow0, brow, lane, wave); break;
   }
+  static_assert(RB == 5, "k_loop dispatch");
 
   // ---- epilogue: lane holds column (lane & 31), rows 8g + 4*(lane>>5) + r ----
   uint16_t* out = static_cast<uint16_t*>(a.out);
   const int col = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < RB; ++i) {
     if (i >= nrb) continue;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -207,8 +307,8 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
         const int64_t orow = (int64_t)ch.row0 + row;
         const int v = 4 * g + r;
         if (MODE == MODE_GATEUP) {
-          const int64_t n = (int64_t)nt * 64 + wn * 32 + col;
-          out[orow * N + n] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
+          const int64_t n = (int64_t)nt * 128 + wn * 32 + col;
+          if (n < N) out[orow * N + n] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
         } else {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
@@ -315,13 +415,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs a, int n_tiles)
 template <int MODE>
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
   if (dtype == MOE_BF16) {
-    const int n_tiles = (int)(MODE == MODE_GATEUP ? a.N / 64 : (a.N + BN - 1) / BN);
+    const int n_tiles = (int)(MODE == MODE_GATEUP ? (a.N + 127) / 128 : (a.N + BN - 1) / BN);
     const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
-    const size_t lds = (size_t)2 * (BM + BN) * BK * 2;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_bf16<MODE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(grouped_gemm_bf16<MODE>, dim3((unsigned)grid), dim3(NT), lds, s, a, n_tiles);
+    hipLaunchKernelGGL(grouped_gemm_bf16<MODE>, dim3((unsigned)grid), dim3(NT), 0, s, a, n_tiles);
   } else {
     const int n_tiles = (int)(MODE == MODE_GATEUP ? a.N / 32 : (a.N + 63) / 64);
     const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
