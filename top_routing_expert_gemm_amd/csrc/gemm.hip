@@ -44,14 +44,18 @@ constexpr int BN = 256;
 constexpr int NT = 512;
 constexpr int NWAVES = NT / 64;
 constexpr int SUPER = 4;     // chunks of one group interleaved per n-tile
-constexpr int BK = 32;
-constexpr int STAGES = 4;
-constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row (4)
-constexpr int RPB = 64 / CPR;               // tile rows per 1 KB direct-to-LDS block (16)
-constexpr int A_BLK = 3;                    // A blocks per wave per stage: 8 x 3 x 16 = 384 >= BM rows
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 32
+#endif
+constexpr int BK = MOE_GEMM_BK;
+constexpr int STAGES = BK == 64 ? 2 : 4;     // LDS: 2 x (320 + 256) x 128 B or 4 x (384 + 256) x 64 B
+constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row
+constexpr int RPB = 64 / CPR;               // tile rows per 1 KB direct-to-LDS block
+constexpr int A_BLK = (BM + NWAVES * RPB - 1) / (NWAVES * RPB);  // A blocks per wave per stage
 constexpr int BM_LD = NWAVES * A_BLK * RPB; // A rows staged per stage (rows >= BM are never read)
-constexpr int B_BLK = BN / RPB / NWAVES;    // (2)
+constexpr int B_BLK = BN / RPB / NWAVES;
 constexpr int LOADS_PER_STAGE = A_BLK + B_BLK;
+static_assert(BK == 32 || BK == 64, "BK");
 static_assert(BM_LD >= BM && BM % 32 == 0, "A staging");
 static_assert(STAGES * (BM_LD + BN) * BK * 2 <= 160 * 1024, "LDS");
 
@@ -64,12 +68,12 @@ typedef __attribute__((address_space(1))) void glb_void;
 // in-flight direct-to-LDS writes of one stage from the reads of another.
 __shared__ __attribute__((aligned(1024))) uint16_t sA0[BM_LD * BK];
 __shared__ __attribute__((aligned(1024))) uint16_t sA1[BM_LD * BK];
-__shared__ __attribute__((aligned(1024))) uint16_t sA2[BM_LD * BK];
-__shared__ __attribute__((aligned(1024))) uint16_t sA3[BM_LD * BK];
+__shared__ __attribute__((aligned(1024))) uint16_t sA2[STAGES > 2 ? BM_LD * BK : 8];
+__shared__ __attribute__((aligned(1024))) uint16_t sA3[STAGES > 3 ? BM_LD * BK : 8];
 __shared__ __attribute__((aligned(1024))) uint16_t sB0[BN * BK];
 __shared__ __attribute__((aligned(1024))) uint16_t sB1[BN * BK];
-__shared__ __attribute__((aligned(1024))) uint16_t sB2[BN * BK];
-__shared__ __attribute__((aligned(1024))) uint16_t sB3[BN * BK];
+__shared__ __attribute__((aligned(1024))) uint16_t sB2[STAGES > 2 ? BN * BK : 8];
+__shared__ __attribute__((aligned(1024))) uint16_t sB3[STAGES > 3 ? BN * BK : 8];
 
 template <int S>
 __device__ __forceinline__ uint16_t* stA() {
@@ -86,10 +90,13 @@ __device__ __forceinline__ uint16_t* stB() {
   else return sB3;
 }
 
-// XOR swizzle of the four 16-byte chunks of a 64-byte tile row: the 16 lanes of
-// one ds_read_b128 cycle (rows r..r+15, one logical chunk) hit distinct banks on
-// a 64-bank LDS, and the 8 lanes of a 32-bank cycle do too.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// XOR swizzle of the 16-byte chunks of a tile row: the 16 lanes of one
+// ds_read_b128 cycle (rows r..r+15, one logical chunk) hit distinct banks on a
+// 64-bank LDS, and the 8 lanes of a 32-bank cycle do too.
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);  // 8 chunks per 128-byte row
+  else return ((r >> 1) ^ (r >> 2)) & 3;                     // 4 chunks per 64-byte row
+}
 
 // Physical workgroup id -> logical tile id, XCD-contiguous; false past V.
 __device__ __forceinline__ bool xcd_map(int p, int V, int& L) {
@@ -182,7 +189,7 @@ __device__ __forceinline__ void compute_stage(f32x16 (&acc)[RB][2], int wrow0, c
 template <int S, int NRB>
 __device__ __forceinline__ void pipe_step(const Frag& f, f32x16 (&acc)[RB][2], int kt, int nk, int wrow0,
                                           const int (&brow)[2], int lane, int wave) {
-  stage_barrier<(STAGES - 2) * LOADS_PER_STAGE>();
+  stage_barrier<(STAGES > 2 ? STAGES - 2 : 0) * LOADS_PER_STAGE>();
   issue_stage<(S + STAGES - 1) % STAGES>(f, min(kt + STAGES - 1, nk - 1), wave);
   if constexpr (NRB > 0) compute_stage<S, NRB>(acc, wrow0, brow, lane);
 }
@@ -193,20 +200,22 @@ template <int NRB>
 __device__ __forceinline__ void k_loop(const Frag& f, f32x16 (&acc)[RB][2], int nk, int wrow0,
                                        const int (&brow)[2], int lane, int wave) {
   issue_stage<0>(f, 0, wave);
-  issue_stage<1>(f, min(1, nk - 1), wave);
-  issue_stage<2>(f, min(2, nk - 1), wave);
+  if constexpr (STAGES > 2) issue_stage<1>(f, min(1, nk - 1), wave);
+  if constexpr (STAGES > 3) issue_stage<2>(f, min(2, nk - 1), wave);
   int kt = 0;
   // whole groups of STAGES steps: no conditional memory traffic inside the loop
   for (; kt + STAGES <= nk; kt += STAGES) {
     pipe_step<0, NRB>(f, acc, kt, nk, wrow0, brow, lane, wave);
     pipe_step<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
-    pipe_step<2, NRB>(f, acc, kt + 2, nk, wrow0, brow, lane, wave);
-    pipe_step<3, NRB>(f, acc, kt + 3, nk, wrow0, brow, lane, wave);
+    if constexpr (STAGES > 2) pipe_step<2, NRB>(f, acc, kt + 2, nk, wrow0, brow, lane, wave);
+    if constexpr (STAGES > 3) pipe_step<3, NRB>(f, acc, kt + 3, nk, wrow0, brow, lane, wave);
   }
   // tail (nk not a multiple of STAGES)
   if (kt < nk) pipe_step<0, NRB>(f, acc, kt, nk, wrow0, brow, lane, wave);
-  if (kt + 1 < nk) pipe_step<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
-  if (kt + 2 < nk) pipe_step<2, NRB>(f, acc, kt + 2, nk, wrow0, brow, lane, wave);
+  if constexpr (STAGES > 2)
+    if (kt + 1 < nk) pipe_step<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
+  if constexpr (STAGES > 3)
+    if (kt + 2 < nk) pipe_step<2, NRB>(f, acc, kt + 2, nk, wrow0, brow, lane, wave);
   // the clamped refills of the last steps are still in flight: let them land
   // before the wave can retire
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
