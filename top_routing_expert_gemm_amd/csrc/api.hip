@@ -15,8 +15,8 @@ inline size_t esize(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; 
 
 // Device workspace of moe_forward; the stage entry points use the same layout.
 struct Layout {
-  size_t topk_idx, topk_w, counts, offsets, row_of_slot, token_of_row, dscratch, chunks, n_chunks, h, y_perm,
-      total;
+  size_t topk_idx, topk_w, counts, offsets, row_of_slot, token_of_row, dscratch, rscratch, chunks, n_chunks, h,
+      y_perm, total;
   int64_t rows;        // permuted row space: T*k routed rows, then T shared rows
   int64_t max_chunks;  // chunk-list capacity
 };
@@ -40,6 +40,7 @@ Layout layout(const moe_config* c) {
   L.row_of_slot = take((size_t)Tk * 4);
   L.token_of_row = take((size_t)Tk * 4);
   L.dscratch = take(dispatch_scratch_bytes(Tk, c->E));
+  L.rscratch = take(route_scratch_bytes(*c));
   L.chunks = take((size_t)L.max_chunks * sizeof(Chunk));
   L.n_chunks = take(4);
   L.h = take((size_t)L.rows * c->I * esize(c));
@@ -269,7 +270,7 @@ moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const vo
   int32_t* nch = reinterpret_cast<int32_t*>(at(ws, L.n_chunks));
 
   HIP_TRY(mark(0));
-  HIP_TRY(launch_route(*c, x, w->w_router, w->router_bias, r.topk_idx, r.topk_w, s));
+  HIP_TRY(launch_route_split(*c, x, w->w_router, w->router_bias, r.topk_idx, r.topk_w, at(ws, L.rscratch), s));
   HIP_TRY(mark(1));
   HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), r.topk_idx, r.counts, r.offsets, r.row_of_slot,
                           r.token_of_row, at(ws, L.dscratch), chunks, nch, bm, sh, Tk, s));

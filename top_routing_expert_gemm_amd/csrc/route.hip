@@ -107,7 +107,103 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// NBW: 32-expert blocks per wave (E <= 128 * NBW).
+// Router GEMM core shared by the fused and the split-K kernels: RBT blocks of
+// 32 tokens (rows t0 ..) x all E experts, contraction over x columns
+// [kb*64, ke*64).  The token tile is staged in LDS (As: 2 x RBT*32 x 64 bf16,
+// double buffered, 16-byte chunks XOR-swizzled by row); each wave streams its
+// 32-expert blocks of W_router straight into MFMA operand registers.
+template <int NBW, int RBT>
+__device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T,
+                                            int H, int E, int t0, int kb, int ke, uint16_t* As,
+                                            f32x16 (&acc)[RBT][NBW], bool (&bval)[NBW]) {
+  const int nblk = (E + 31) / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int ROWS = RBT * kRBM;
+
+  // token tile staging: thread -> (row tid/8 + 32 i, 16-byte chunk tid%8)
+  const int ar = tid >> 3, ac = tid & 7;
+  const uint16_t* aptr[RBT];
+  int a_lds[RBT];
+#pragma unroll
+  for (int i = 0; i < RBT; ++i) {
+    const int r = ar + 32 * i;
+    aptr[i] = x + (int64_t)min(t0 + r, T - 1) * H + ac * 8;
+    a_lds[i] = r * kRBK + ((ac ^ (r & 7)) * 8);
+  }
+  // B operand rows of this wave's blocks: lane -> expert (lane & 31), k half (lane >> 5)
+  const uint16_t* bptr[NBW];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const int blk = wave + 4 * i;
+    bval[i] = blk < nblk;
+    const int e = min(blk * 32 + (lane & 31), E - 1);
+    bptr[i] = w + (int64_t)e * H + (lane >> 5) * 32;
+  }
+#pragma unroll
+  for (int r = 0; r < RBT; ++r)
+#pragma unroll
+    for (int i = 0; i < NBW; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[r][i][v] = 0.f;
+
+  uint4 apf[RBT];
+  uint4 bcur[NBW][4];
+#pragma unroll
+  for (int i = 0; i < RBT; ++i) apf[i] = ldg16(aptr[i] + kb * kRBK);
+#pragma unroll
+  for (int i = 0; i < NBW; ++i)
+    if (bval[i])
+#pragma unroll
+      for (int s = 0; s < 4; ++s) bcur[i][s] = ldg16(bptr[i] + kb * kRBK + s * 8);
+#pragma unroll
+  for (int i = 0; i < RBT; ++i) *reinterpret_cast<uint4*>(As + a_lds[i]) = apf[i];
+  __syncthreads();
+
+  const int arow = lane & 31;
+  for (int kt = kb; kt < ke; ++kt) {
+    uint4 bnext[NBW][4];
+    const bool more = kt + 1 < ke;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < RBT; ++i) apf[i] = ldg16(aptr[i] + (kt + 1) * kRBK);
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+        if (bval[i])
+#pragma unroll
+          for (int s = 0; s < 4; ++s) bnext[i][s] = ldg16(bptr[i] + (kt + 1) * kRBK + s * 8);
+    }
+    const uint16_t* Ab = As + ((kt - kb) & 1) * ROWS * kRBK;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      // substep s, lane half h: k = h*32 + s*8 .. +8 (same permutation as the B loads)
+      const int chunk = (lane >> 5) * 4 + s;
+#pragma unroll
+      for (int r = 0; r < RBT; ++r) {
+        const int row = r * 32 + arow;
+        const bf16x8 av = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(Ab + row * kRBK + ((chunk ^ (row & 7)) * 8)));
+#pragma unroll
+        for (int i = 0; i < NBW; ++i)
+          if (bval[i])
+            acc[r][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, bcur[i][s]),
+                                                                acc[r][i], 0, 0, 0);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < RBT; ++i)
+        *reinterpret_cast<uint4*>(As + (((kt - kb) + 1) & 1) * ROWS * kRBK + a_lds[i]) = apf[i];
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bcur[i][s] = bnext[i][s];
+    }
+    __syncthreads();
+  }
+}
+
+// Fused router: one workgroup = 32 tokens x all E experts over the whole of H;
+// logits go to LDS only, then each wave runs the gate / top-k of 8 tokens.
 template <int NBW>
 __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias,
@@ -119,77 +215,12 @@ __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(
   float* lg = reinterpret_cast<float*>(smem + 2 * kRBM * kRBK * 2);  // [32][lde]
   const int nblk = (E + 31) / 32;
   const int lde = nblk * 32 + 4;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kRBM;
 
-  // A staging: thread -> (row tid/8, 16-byte chunk tid%8)
-  const int ar = tid >> 3, ac = tid & 7;
-  const uint16_t* aptr = x + (int64_t)min(t0 + ar, T - 1) * H + ac * 8;
-  const int a_lds = ar * kRBK + ((ac ^ (ar & 7)) * 8);
-
-  // B operand rows of this wave's blocks: lane -> expert (lane & 31), k half (lane >> 5)
-  const uint16_t* bptr[NBW];
+  f32x16 acc[1][NBW];
   bool bval[NBW];
-#pragma unroll
-  for (int i = 0; i < NBW; ++i) {
-    const int blk = wave + 4 * i;
-    bval[i] = blk < nblk;
-    const int e = min(blk * 32 + (lane & 31), E - 1);
-    bptr[i] = w + (int64_t)e * H + (lane >> 5) * 32;
-  }
-
-  f32x16 acc[NBW];
-#pragma unroll
-  for (int i = 0; i < NBW; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
-
-  const int nk = H / kRBK;
-  uint4 apf = ldg16(aptr);
-  uint4 bcur[NBW][4];
-#pragma unroll
-  for (int i = 0; i < NBW; ++i)
-    if (bval[i])
-#pragma unroll
-      for (int s = 0; s < 4; ++s) bcur[i][s] = ldg16(bptr[i] + s * 8);
-  *reinterpret_cast<uint4*>(As + a_lds) = apf;
-  __syncthreads();
-
-  const int arow = lane & 31;
-  for (int kt = 0; kt < nk; ++kt) {
-    uint4 bnext[NBW][4];
-    const bool more = kt + 1 < nk;
-    if (more) {
-      apf = ldg16(aptr + (kt + 1) * kRBK);
-#pragma unroll
-      for (int i = 0; i < NBW; ++i)
-        if (bval[i])
-#pragma unroll
-          for (int s = 0; s < 4; ++s) bnext[i][s] = ldg16(bptr[i] + (kt + 1) * kRBK + s * 8);
-    }
-    const uint16_t* Ab = As + (kt & 1) * kRBM * kRBK;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      // substep s, lane half h: k = h*32 + s*8 .. +8 (same permutation as the B loads)
-      const int chunk = (lane >> 5) * 4 + s;
-      const uint4 a = *reinterpret_cast<const uint4*>(Ab + arow * kRBK + ((chunk ^ (arow & 7)) * 8));
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-#pragma unroll
-      for (int i = 0; i < NBW; ++i)
-        if (bval[i])
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, bcur[i][s]),
-                                                           acc[i], 0, 0, 0);
-    }
-    if (more) {
-      *reinterpret_cast<uint4*>(As + ((kt + 1) & 1) * kRBM * kRBK + a_lds) = apf;
-#pragma unroll
-      for (int i = 0; i < NBW; ++i)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bcur[i][s] = bnext[i][s];
-    }
-    __syncthreads();
-  }
+  router_tile<NBW, 1>(x, w, T, H, E, t0, 0, H / kRBK, As, acc, bval);
 
   // logits tile -> LDS: lane holds expert column (lane & 31) of each block and
   // token rows 8g + 4*(lane >> 5) + r of the 32x32 MFMA result.
@@ -203,7 +234,7 @@ __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 8 * g + 4 * (lane >> 5) + r;
-        lg[row * lde + e] = acc[i][4 * g + r] + b;
+        lg[row * lde + e] = acc[0][i][4 * g + r] + b;
       }
   }
   __syncthreads();
@@ -219,6 +250,67 @@ __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(
     }
     topk_token<VPL>(z, E, k, gate, renorm, scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
   }
+}
+
+// Split-K router, part 1: workgroup (m, s) computes the partial logits of RBT*32
+// tokens over the s-th slice of H and stores them to part[s][t][0..Epad).
+template <int NBW, int RBT>
+__global__ __launch_bounds__(kRThreads) void route_partial_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T, int H, int E, int ksteps_per_split,
+    float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2 * RBT * kRBM * kRBK];
+  const int nblk = (E + 31) / 32, Epad = nblk * 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * RBT * kRBM;
+  const int ks = blockIdx.y;
+  const int kb = ks * ksteps_per_split;
+  const int ke = min(kb + ksteps_per_split, H / kRBK);
+  f32x16 acc[RBT][NBW];
+  bool bval[NBW];
+  router_tile<NBW, RBT>(x, w, T, H, E, t0, kb, ke, As, acc, bval);
+  float* out = part + (int64_t)ks * T * Epad;
+#pragma unroll
+  for (int r = 0; r < RBT; ++r)
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+      if (!bval[i]) continue;
+      const int e = (wave + 4 * i) * 32 + (lane & 31);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = t0 + r * 32 + 8 * g + 4 * (lane >> 5) + q;
+          if (t < T) out[(int64_t)t * Epad + e] = acc[r][i][4 * g + q];
+        }
+    }
+}
+
+// Split-K router, part 2: one wave per token sums the partial logits in slice
+// order (fixed, so the result is reproducible), adds the bias and runs the gate
+// and top-k.
+template <int VPL>
+__global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __restrict__ part, int nsplit, int T,
+                                                               int E, const float* __restrict__ bias, int k,
+                                                               int gate, int renorm, float scale,
+                                                               int32_t* __restrict__ topk_idx,
+                                                               float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kRThreads / kWave) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int Epad = (E + 31) / 32 * 32;
+  float z[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = lane + kWave * v;
+    if (e < E) {
+      float s = 0.f;
+      for (int ks = 0; ks < nsplit; ++ks) s += part[((int64_t)ks * T + t) * Epad + e];
+      z[v] = bias != nullptr ? s + bias[e] : s;
+    } else {
+      z[v] = -INFINITY;
+    }
+  }
+  topk_token<VPL>(z, E, k, gate, renorm, scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
 }
 
 // fp32 path: one wave per token computes its E logits with lane-strided dot
@@ -282,7 +374,65 @@ hipError_t launch_route_f32(const moe_config& c, const void* x, const void* w, c
   return hipGetLastError();
 }
 
+// Split factor of the K dimension: enough workgroups to cover the chip twice,
+// each slice at least 4 K steps long.
+// Token blocks per workgroup: 64 tokens for large batches (halves the router
+// weight traffic), 32 otherwise and for E > 512 (register budget).
+inline int route_rbt(int64_t T, int64_t E) { return T >= 4096 && E <= 512 ? 2 : 1; }
+inline int route_nsplit(int64_t T, int64_t H, int64_t E) {
+  const int64_t rows = route_rbt(T, E) * kRBM;
+  const int64_t mt = (T + rows - 1) / rows;
+  const int64_t nk = H / kRBK;
+  int64_t ns = (512 + mt - 1) / mt;
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, nk / 4));
+  return (int)std::max<int64_t>(1, ns);
+}
+
+template <int NBW, int RBT>
+hipError_t launch_route_split_t(const moe_config& c, const void* x, const void* w, const float* bias,
+                                int32_t* idx, float* tw, float* part, hipStream_t s) {
+  const int nsplit = route_nsplit(c.T, c.H, c.E);
+  const int nk = (int)(c.H / kRBK);
+  const int per = (nk + nsplit - 1) / nsplit;
+  const int nsplit_eff = (nk + per - 1) / per;
+  dim3 grid((unsigned)((c.T + RBT * kRBM - 1) / (RBT * kRBM)), (unsigned)nsplit_eff);
+  hipLaunchKernelGGL((route_partial_bf16_kernel<NBW, RBT>), grid, dim3(kRThreads), 0, s,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), (int)c.T, (int)c.H,
+                     (int)c.E, per, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int tpb = kRThreads / kWave;
+  hipLaunchKernelGGL(route_topk_kernel<2 * NBW>, dim3((unsigned)((c.T + tpb - 1) / tpb)), dim3(kRThreads), 0, s,
+                     part, nsplit_eff, (int)c.T, (int)c.E, bias, (int)c.k, c.gate, c.renormalize,
+                     c.routed_scaling_factor, idx, tw);
+  return hipGetLastError();
+}
+
+template <int NBW>
+hipError_t launch_route_split_n(const moe_config& c, const void* x, const void* w, const float* bias,
+                                int32_t* idx, float* tw, float* part, hipStream_t s) {
+  if constexpr (NBW <= 4)
+    if (route_rbt(c.T, c.E) == 2) return launch_route_split_t<NBW, 2>(c, x, w, bias, idx, tw, part, s);
+  return launch_route_split_t<NBW, 1>(c, x, w, bias, idx, tw, part, s);
+}
+
 }  // namespace
+
+size_t route_scratch_bytes(const moe_config& c) {
+  if (c.dtype != MOE_BF16) return 0;
+  const int64_t Epad = (c.E + 31) / 32 * 32;
+  return (size_t)route_nsplit(c.T, c.H, c.E) * c.T * Epad * 4;
+}
+
+hipError_t launch_route_split(const moe_config& c, const void* x, const void* w, const float* bias,
+                              int32_t* topk_idx, float* topk_w, void* scratch, hipStream_t s) {
+  if (c.dtype != MOE_BF16) return launch_route(c, x, w, bias, topk_idx, topk_w, s);
+  float* part = static_cast<float*>(scratch);
+  if (c.E <= 128) return launch_route_split_n<1>(c, x, w, bias, topk_idx, topk_w, part, s);
+  if (c.E <= 256) return launch_route_split_n<2>(c, x, w, bias, topk_idx, topk_w, part, s);
+  if (c.E <= 512) return launch_route_split_n<4>(c, x, w, bias, topk_idx, topk_w, part, s);
+  return launch_route_split_n<8>(c, x, w, bias, topk_idx, topk_w, part, s);
+}
 
 hipError_t launch_route(const moe_config& c, const void* x, const void* w, const float* bias,
                         int32_t* topk_idx, float* topk_w, hipStream_t s) {
