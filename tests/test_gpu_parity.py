@@ -37,6 +37,11 @@ SMALL = {
     "bf16_max_E_max_k": MoEShape("bf16_max_E_max_k", T=70, H=128, I=64, E=1024, k=16, gate=GATE_SIGMOID,
                                  cfg_id=109),
     "fp32_E300": MoEShape("fp32_E300", T=40, H=64, I=64, E=300, k=5, dtype=F32, cfg_id=110),
+    # batches of <= 16 tokens take the weight-streaming path
+    "bf16_decode_T16_shared": MoEShape("bf16_decode_T16_shared", T=16, H=512, I=256, E=32, k=4,
+                                       gate=GATE_SIGMOID, routed_scaling_factor=2.5, n_shared=1, I_shared=256,
+                                       cfg_id=111),
+    "bf16_decode_T5_softmax": MoEShape("bf16_decode_T5_softmax", T=5, H=192, I=64, E=8, k=3, cfg_id=112),
 }
 
 
@@ -148,6 +153,25 @@ def test_expert_ffn_stage():
         torch.cuda.synchronize()
         check_rows(widen_out(ys), ref.swiglu_ffn(inp.x, inp.ws_gate, inp.ws_up, inp.ws_down), s.dtype,
                    "shared expert " + s.name)
+
+
+def test_expert_ffn_stream_multichunk():
+    """Small-batch streaming path with groups longer than one 16-row chunk (caller offsets)."""
+    s = MoEShape("stream_multi", T=16, H=256, I=128, E=3, k=3, cfg_id=140)
+    inp = make_inputs(s)
+    dev = upload(inp)
+    cfg = moe.config_from_shape(s)
+    offsets = np.array([0, 30, 31, 48], dtype=np.int64)       # 30, 1 and 17 rows
+    rng = np.random.default_rng(3)
+    from synth import f32_to_bf16_bits
+    xp_host = f32_to_bf16_bits(rng.normal(size=(s.T * s.k, s.H)).astype(np.float32))
+    xp = to_torch(xp_host, "cuda")
+    off = torch.from_numpy(offsets.astype(np.int32)).cuda()
+    yp = torch.zeros((s.T * s.k, s.H), dtype=torch.bfloat16, device="cuda")
+    moe.expert_ffn(cfg, xp, off, dev["w_gate"], dev["w_up"], dev["w_down"], yp, workspace(cfg))
+    torch.cuda.synchronize()
+    want = ref.grouped_expert_ffn(xp_host[:48], offsets, inp.w_gate, inp.w_up, inp.w_down)
+    check_rows(widen_out(yp)[:48], want, BF16, "stream multichunk")
 
 
 @pytest.mark.parametrize("dtype", [BF16, F32])

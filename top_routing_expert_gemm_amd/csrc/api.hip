@@ -26,7 +26,7 @@ Layout layout(const moe_config* c) {
   const int64_t Tk = c->T * c->k;
   const int64_t sh = c->n_shared ? c->T : 0;
   L.rows = Tk + sh;
-  L.max_chunks = max_chunks(Tk, c->E, sh, gemm_bm(c->dtype));
+  L.max_chunks = max_chunks(Tk, c->E, sh, gemm_bm(*c));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -167,7 +167,7 @@ moe_status moe_dispatch(const moe_config* c, const int32_t* topk_idx, const void
   const Layout L = layout(c);
   HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), topk_idx, counts, offsets, row_of_slot, token_of_row,
                           at(ws, L.dscratch), reinterpret_cast<Chunk*>(at(ws, L.chunks)),
-                          reinterpret_cast<int32_t*>(at(ws, L.n_chunks)), gemm_bm(c->dtype), 0, 0, S(stream)));
+                          reinterpret_cast<int32_t*>(at(ws, L.n_chunks)), gemm_bm(*c), 0, 0, S(stream)));
   if (x_perm != nullptr)
     HIP_TRY(launch_gather(x, token_of_row, offsets, c->E, c->T * c->k, c->H, c->dtype, x_perm, S(stream)));
   return MOE_OK;
@@ -185,7 +185,7 @@ moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t
   MOE_TRY(need(y_perm));
   MOE_TRY(check_ws(c, ws, ws_bytes));
   const Layout L = layout(c);
-  const int bm = gemm_bm(c->dtype);
+  const int bm = gemm_bm(*c);
   Chunk* chunks = reinterpret_cast<Chunk*>(at(ws, L.chunks));
   int32_t* nch = reinterpret_cast<int32_t*>(at(ws, L.n_chunks));
   HIP_TRY(launch_chunks_from_offsets(offsets, c->E, chunks, nch, bm, S(stream)));
@@ -196,6 +196,7 @@ moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t
   g.chunks = chunks;
   g.n_chunks = nch;
   g.max_chunks = max_chunks(c->T * c->k, c->E, 0, bm);
+  g.bm = bm;
   g.w0 = w_gate;
   g.w1 = w_up;
   g.E = c->E;
@@ -263,7 +264,7 @@ moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const vo
     if (events == nullptr || events[i] == nullptr) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
   };
-  const int bm = gemm_bm(c->dtype);
+  const int bm = gemm_bm(*c);
   const int64_t Tk = c->T * c->k;
   const int64_t sh = c->n_shared ? c->T : 0;
   Chunk* chunks = reinterpret_cast<Chunk*>(at(ws, L.chunks));
@@ -282,6 +283,7 @@ moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const vo
   g.chunks = chunks;
   g.n_chunks = nch;
   g.max_chunks = L.max_chunks;
+  g.bm = bm;
   g.w0 = w->w_gate;
   g.w1 = w->w_up;
   g.ws0 = w->ws_gate;

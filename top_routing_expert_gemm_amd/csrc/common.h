@@ -33,8 +33,16 @@ struct Chunk {
 constexpr int kGemmBM = 320;
 // M-tile height of the fp32 grouped GEMM.
 constexpr int kGemmBMf32 = 64;
+// Row chunks of the bf16 weight-streaming path used for small batches (decode).
+constexpr int kGemvBM = 16;
+constexpr int64_t kGemvMaxT = 16;
 
-inline int gemm_bm(int dtype) { return dtype == MOE_BF16 ? kGemmBM : kGemmBMf32; }
+// Chunk height for a layer: the streaming path when every expert group fits one
+// 16-row chunk (T <= 16), the 320-row MFMA tile otherwise; fp32 uses 64.
+inline int gemm_bm(const moe_config& c) {
+  if (c.dtype != MOE_BF16) return kGemmBMf32;
+  return c.T <= kGemvMaxT ? kGemvBM : kGemmBM;
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -93,6 +101,7 @@ struct GemmArgs {
   int64_t K;                // contraction length (H or I)
   int64_t N;                // output columns (I or H)
   void* out;                // [rows, N]
+  int bm;                   // chunk height the list was cut to (selects the kernel)
 };
 
 hipError_t launch_gateup(const GemmArgs& a, int dtype, hipStream_t s);

@@ -329,6 +329,120 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
   }
 }
 
+// ------------------------------------------------------ bf16 streaming path
+// Small batches (decode): every expert group has at most 16 rows, so the work is
+// streaming each touched expert's weights once.  One wave owns 16 output columns
+// (16 weight rows; gate/up: 16 gate + the same 16 up rows) of one chunk and runs
+// v_mfma_f32_16x16x32_bf16 with the token rows padded to 16.  No LDS and no
+// barriers: each lane streams 32 contiguous bytes of its weight row per 64-wide
+// K block straight into registers, with SP blocks in flight, so many waves per
+// CU keep a deep queue of HBM reads.  The token rows (A) are tiny and cached.
+#ifndef MOE_STREAM_SKB
+#define MOE_STREAM_SKB 64
+#endif
+#ifndef MOE_STREAM_SP
+#define MOE_STREAM_SP 4
+#endif
+constexpr int SW = 4;                 // waves per workgroup
+constexpr int SKB = MOE_STREAM_SKB;   // K per block (SKB / 32 MFMA substeps)
+constexpr int SP = MOE_STREAM_SP;     // K blocks in flight per wave
+constexpr int NV = SKB / 32;          // 16-byte loads per lane per matrix per block
+static_assert(SKB == 64 || SKB == 128, "SKB");
+
+__device__ __forceinline__ void ldv(uint4 (&r)[NV], const uint16_t* p) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) r[i] = *reinterpret_cast<const uint4*>(p + 8 * i);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(SW * 64) void grouped_stream_bf16(GemmArgs a, int n_wt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int V = *a.n_chunks * n_wt;
+  const int gw = blockIdx.x * SW + wave;
+  if (gw >= V) return;  // whole wave; no barriers below
+  const int ci = gw / n_wt, nt = gw % n_wt;
+  const Chunk ch = a.chunks[ci];
+  const bool shared = ch.group == a.E;
+  const int64_t K = a.K, N = a.N;
+  const int r16 = lane & 15, g4 = lane >> 4;
+
+  // A: token row r16 of the chunk (clamped); lane group g4 covers k = (SKB/4) g4 .. + SKB/4 of each block
+  const int rc = min(r16, ch.nrows - 1);
+  const int64_t row = (int64_t)ch.row0 + rc;
+  int64_t src = row;
+  if (a.gather != nullptr) src = shared ? row - a.shared_row0 : (int64_t)a.gather[row];
+  const uint16_t* pa = static_cast<const uint16_t*>(a.A) + src * K + g4 * (SKB / 4);
+  // B: weight row n = 16 nt + r16 (N is a multiple of 64)
+  const int64_t goff = shared ? 0 : (int64_t)ch.group * N * K;
+  const int64_t n = (int64_t)nt * 16 + r16;
+  const uint16_t* p0 = static_cast<const uint16_t*>(shared ? a.ws0 : a.w0) + goff + n * K + g4 * (SKB / 4);
+  const uint16_t* p1 = MODE == MODE_GATEUP
+                           ? static_cast<const uint16_t*>(shared ? a.ws1 : a.w1) + goff + n * K + g4 * (SKB / 4)
+                           : p0;
+
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int nkb = (int)(K / SKB);  // K is a multiple of 64; a 64-wide tail block is handled below
+  uint4 ra[SP][NV], rb0[SP][NV], rb1[SP][NV];
+  if (nkb > 0) {  // (a K shorter than one block has only the tail below)
+#pragma unroll
+  for (int p = 0; p < SP; ++p) {
+    const int64_t ko = (int64_t)min(p, nkb - 1) * SKB;
+    ldv(ra[p], pa + ko);
+    ldv(rb0[p], p0 + ko);
+    if (MODE == MODE_GATEUP) ldv(rb1[p], p1 + ko);
+  }
+  for (int kb0 = 0; kb0 < nkb; kb0 += SP) {
+#pragma unroll
+    for (int p = 0; p < SP; ++p) {
+      const int kb = kb0 + p;
+      if (kb < nkb) {
+        // substep s: lane group g4 supplies k = (SKB/4) g4 + 8 s .. +8 of this block, for A and B alike
+#pragma unroll
+        for (int s2 = 0; s2 < NV; ++s2) {
+          const bf16x8 av = __builtin_bit_cast(bf16x8, ra[p][s2]);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, rb0[p][s2]), acc0, 0, 0, 0);
+          if (MODE == MODE_GATEUP)
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, rb1[p][s2]), acc1, 0, 0, 0);
+        }
+        const int64_t ko = (int64_t)min(kb + SP, nkb - 1) * SKB;
+        ldv(ra[p], pa + ko);
+        ldv(rb0[p], p0 + ko);
+        if (MODE == MODE_GATEUP) ldv(rb1[p], p1 + ko);
+      }
+    }
+  }
+  }
+  if constexpr (SKB == 128) {
+    if (K % SKB != 0) {  // one 64-wide tail block: lane group g4 takes k = 16 g4 .. +16 of it
+      const int64_t kt = (int64_t)nkb * SKB;
+      const uint16_t* ta = pa - g4 * (SKB / 4) + kt + g4 * 16;
+      const uint16_t* t0 = p0 - g4 * (SKB / 4) + kt + g4 * 16;
+      const uint16_t* t1 = p1 - g4 * (SKB / 4) + kt + g4 * 16;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ta + 8 * s2));
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            av, __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(t0 + 8 * s2)), acc0, 0, 0, 0);
+        if (MODE == MODE_GATEUP)
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              av, __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(t1 + 8 * s2)), acc1, 0, 0, 0);
+      }
+    }
+  }
+  // lane holds output column 16 nt + r16 for token rows 4 g4 + q
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rr = 4 * g4 + q;
+    if (rr >= ch.nrows) continue;
+    const int64_t orow = (int64_t)ch.row0 + rr;
+    if (MODE == MODE_GATEUP)
+      out[orow * N + n] = f32_to_bf16(silu_f(acc0[q]) * acc1[q]);
+    else
+      out[orow * N + n] = f32_to_bf16(acc0[q]);
+  }
+}
+
 // ---------------------------------------------------------------- fp32 path
 // SIMT tiles of 64 rows: gate/up -> 32 output columns (32 gate + 32 up weight
 // rows), down -> 64 output columns; 256 threads, 4 rows x (2+2 | 4) columns each.
@@ -423,7 +537,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs a, int n_tiles)
 
 template <int MODE>
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
-  if (dtype == MOE_BF16) {
+  if (dtype == MOE_BF16 && a.bm == kGemvBM) {
+    const int n_wt = (int)(a.N / 16);
+    const int64_t grid = (a.max_chunks * n_wt + SW - 1) / SW;
+    hipLaunchKernelGGL(grouped_stream_bf16<MODE>, dim3((unsigned)grid), dim3(SW * 64), 0, s, a, n_wt);
+  } else if (dtype == MOE_BF16) {
     const int n_tiles = (int)(MODE == MODE_GATEUP ? (a.N + 127) / 128 : (a.N + BN - 1) / BN);
     const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
     hipLaunchKernelGGL(grouped_gemm_bf16<MODE>, dim3((unsigned)grid), dim3(NT), 0, s, a, n_tiles);

@@ -303,8 +303,19 @@ __global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __re
   for (int v = 0; v < VPL; ++v) {
     const int e = lane + kWave * v;
     if (e < E) {
+      // loads issued eight at a time, added strictly in slice order
+      const float* pp = part + (int64_t)t * Epad + e;
+      const int64_t stride = (int64_t)T * Epad;
       float s = 0.f;
-      for (int ks = 0; ks < nsplit; ++ks) s += part[((int64_t)ks * T + t) * Epad + e];
+      int ks = 0;
+      for (; ks + 8 <= nsplit; ks += 8) {
+        float q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = pp[(ks + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += q[u];
+      }
+      for (; ks < nsplit; ++ks) s += pp[ks * stride];
       z[v] = bias != nullptr ? s + bias[e] : s;
     } else {
       z[v] = -INFINITY;
