@@ -301,31 +301,77 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
   }
   static_assert(RB == 5, "k_loop dispatch");
 
-  // ---- epilogue: lane holds column (lane & 31), rows 8g + 4*(lane>>5) + r ----
-  uint16_t* out = static_cast<uint16_t*>(a.out);
-  const int col = lane & 31;
+  // ---- epilogue ----
+  // Lane holds column (lane & 31) and rows 8g + 4*(lane>>5) + r of each 32x32
+  // block.  The wave's output sub-tile goes through a wave-private LDS region
+  // (its own stage buffer, free once every wave is past the K loop): lane pairs
+  // swap one value so each lane writes two adjacent columns as one dword, then
+  // rows leave as 16-byte stores.  Three row blocks per pass fit the smallest
+  // stage buffer.
+  __syncthreads();
+  if (nrb > 0) {
+    constexpr int NJ = MODE == MODE_GATEUP ? 1 : 2;  // 32-column output blocks of this wave
+    constexpr int LDSR = NJ * 32 + 8;                // LDS row stride (elements), padded
+    constexpr int PB = 3;                            // row blocks per pass
+    static_assert(PB * 32 * LDSR * 2 <= BN * BK * 2, "epilogue pass fits a stage buffer");
+    uint16_t* tile;
+    switch (wave) {
+      case 0: tile = sA0; break;
+      case 1: tile = sA1; break;
+      case 2: tile = sA2; break;
+      case 3: tile = sA3; break;
+      case 4: tile = sB0; break;
+      case 5: tile = sB1; break;
+      case 6: tile = sB2; break;
+      default: tile = sB3; break;
+    }
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    const int64_t n0 = MODE == MODE_GATEUP ? (int64_t)nt * 128 + wn * 32 : (int64_t)nt * BN + wn * 64;
+    const int col = lane & 31, h = lane >> 5;
+    const bool odd = col & 1;
 #pragma unroll
-  for (int i = 0; i < RB; ++i) {
-    if (i >= nrb) continue;
+    for (int pass = 0; pass < RB; pass += PB) {
+      if (pass >= nrb) break;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+      for (int i = pass; i < pass + PB && i < RB; ++i) {
+        if (i >= nrb) break;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wrow0 + i * 32 + 8 * g + 4 * (lane >> 5) + r;
-        if (row >= ch.nrows) continue;
-        const int64_t orow = (int64_t)ch.row0 + row;
-        const int v = 4 * g + r;
-        if (MODE == MODE_GATEUP) {
-          const int64_t n = (int64_t)nt * 128 + wn * 32 + col;
-          if (n < N) out[orow * N + n] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
-        } else {
+        for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int64_t n = (int64_t)nt * BN + wn * 64 + j * 32 + col;
-            if (n < N) out[orow * N + n] = f32_to_bf16(acc[i][j][v]);
-          }
-        }
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int p = 0; p < 4; p += 2) {
+              float va, vb;
+              if (MODE == MODE_GATEUP) {
+                va = silu_f(acc[i][0][4 * g + p]) * acc[i][1][4 * g + p];
+                vb = silu_f(acc[i][0][4 * g + p + 1]) * acc[i][1][4 * g + p + 1];
+              } else {
+                va = acc[i][jj][4 * g + p];
+                vb = acc[i][jj][4 * g + p + 1];
+              }
+              // even lane: (row ra, cols c, c+1); odd lane: (row ra+1, cols c-1, c)
+              const float x = __shfl_xor(odd ? va : vb, 1, kWave);
+              const int ra = (i - pass) * 32 + 8 * g + 4 * h + p;
+              const uint32_t w = odd ? ((uint32_t)f32_to_bf16(x) | ((uint32_t)f32_to_bf16(vb) << 16))
+                                     : ((uint32_t)f32_to_bf16(va) | ((uint32_t)f32_to_bf16(x) << 16));
+              const int lr = odd ? ra + 1 : ra;
+              const int lc = jj * 32 + (col & ~1);
+              *reinterpret_cast<uint32_t*>(tile + lr * LDSR + lc) = w;
+            }
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+      const int nrows_pass = min(PB, nrb - pass) * 32;
+      constexpr int CPRW = NJ * 4;  // 16-byte chunks per sub-tile row
+      for (int idx = lane; idx < nrows_pass * CPRW; idx += kWave) {
+        const int lr = idx / CPRW, c16 = idx % CPRW;
+        const int row = wrow0 + pass * 32 + lr;
+        const int64_t n = n0 + c16 * 8;
+        if (row < ch.nrows && n < N)
+          *reinterpret_cast<uint4*>(out + ((int64_t)ch.row0 + row) * N + n) =
+              *reinterpret_cast<const uint4*>(tile + lr * LDSR + c16 * 8);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass overwrites the region
+    }
   }
 }
 
