@@ -79,6 +79,12 @@ typedef struct {
   int64_t n_shared;             /* 0 or 1 always-active shared expert */
   int64_t I_shared;             /* its intermediate size (must equal I) */
   int32_t dtype;                /* moe_dtype */
+  /* DeepSeek-V3 group-limited selection ([MoE-10] "DeepSeek-V3 的无辅助损失偏置",
+   * config n_group / topk_group): the E experts form n_group equal groups; a
+   * group's score is the sum of its two best ranking scores; only the
+   * topk_group best groups are eligible.  n_group = 0: no grouping. */
+  int32_t n_group;              /* 0, or 1..64 dividing E */
+  int32_t topk_group;           /* 1..n_group; k <= topk_group * E / n_group */
 } moe_config;
 
 /* Weights of one layer.  Layouts are [out, in], used as x @ W^T like the router
@@ -92,6 +98,10 @@ typedef struct {
   const void *ws_gate;      /* [I_shared, H] shared expert, NULL when n_shared == 0 */
   const void *ws_up;        /* [I_shared, H] */
   const void *ws_down;      /* [H, I_shared] */
+  /* Selection-only expert bias ([MoE-10] "DeepSeek-V3 的无辅助损失偏置",
+   * e_score_correction_bias): experts are ranked by gate score + score_bias,
+   * the combine weights use the unbiased scores.  [E] float32 or NULL. */
+  const float *score_bias;
 } moe_weights;
 
 /* Optional routing outputs of moe_forward; every field may be NULL (then the
@@ -134,6 +144,14 @@ moe_status moe_layer_params(const moe_config *cfg, int64_t *total, int64_t *acti
 moe_status moe_route(const moe_config *cfg, const void *x, const void *w_router,
                      const float *router_bias, int32_t *topk_idx, float *topk_w,
                      void *stream);
+
+/* moe_route with a selection-only expert bias (score_bias [E] float32 or NULL;
+ * see moe_weights.score_bias) and the group limit of cfg->n_group /
+ * cfg->topk_group ([MoE-10] "DeepSeek-V3 的无辅助损失偏置").  Ties of ranking
+ * scores go to the lower expert id, of group scores to the lower group id. */
+moe_status moe_route_sel(const moe_config *cfg, const void *x, const void *w_router,
+                         const float *router_bias, const float *score_bias, int32_t *topk_idx,
+                         float *topk_w, void *stream);
 
 /* Histogram, stable scan and capacity, then the gather ([MoE-10] simplified
  * Mixtral block: the rows of each expert are collected; "负载不均": overflow is

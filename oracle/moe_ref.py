@@ -50,7 +50,8 @@ __all__ = [
     "GATE_SOFTMAX", "GATE_SIGMOID", "widen", "router_logits", "gate_scores",
     "select_topk", "topk_weights", "route", "expert_capacity", "dispatch",
     "gather_rows", "silu", "swiglu_ffn", "grouped_expert_ffn", "combine",
-    "moe_forward", "moe_layer_params", "expected_touched_experts",
+    "moe_forward", "moe_layer_params", "expected_touched_experts", "select_topk_grouped",
+    "route_grouped", "aux_loss_terms", "bias_update",
 ]
 
 GATE_SOFTMAX = 0
@@ -135,16 +136,69 @@ def topk_weights(scores: np.ndarray, idx: np.ndarray, renormalize: bool,
 
 
 def route(x, w_router, router_bias, k: int, gate: int, renormalize: bool,
-          routed_scaling_factor: float):
+          routed_scaling_factor: float, score_bias=None, n_group: int = 0, topk_group: int = 0):
     """Router -> gate -> top-k -> weights for every token.
 
+    With ``score_bias`` or ``n_group`` the selection is the DeepSeek-V3 one of
+    ``select_topk_grouped``; weights always come from the unbiased scores.
     Returns a dict with logits z, scores, topk_idx [T,k], topk_w [T,k], gap [T].
     """
     z = router_logits(x, w_router, router_bias)
     s = gate_scores(z, gate)
-    idx, gap = select_topk(s, k)
+    if score_bias is None and not n_group:
+        idx, gap = select_topk(s, k)
+    else:
+        idx, gap = select_topk_grouped(s, k, score_bias, n_group, topk_group)
     w = topk_weights(s, idx, renormalize, routed_scaling_factor)
     return {"logits": z, "scores": s, "topk_idx": idx, "topk_w": w, "gap": gap}
+
+
+def select_topk_grouped(scores: np.ndarray, k: int, score_bias=None, n_group: int = 0,
+                        topk_group: int = 0):
+    """DeepSeek-V3 selection (config topk_method noaux_tc).
+
+    [MoE-10] "DeepSeek-V3 的无辅助损失偏置": experts are ranked by s_i + b_i, where
+    b (e_score_correction_bias) is a per-expert buffer that only enters the
+    selection; the weights use the raw s_i gathered back.  The 256 experts form
+    n_group groups; a group's score is the sum of its two highest ranking
+    scores; the topk_group best groups are kept and the k experts are chosen
+    inside them.  Ties go to the lower group / expert index.
+
+    Returns (idx [T,k] best first by ranking score, gap [T]): gap is the smaller
+    of the margin between the k-th and (k+1)-th ranking scores among the kept
+    groups' experts and the margin between the topk_group-th and the next
+    group score (the two decisions a lower-precision implementation could flip).
+    """
+    T, E = scores.shape
+    sel = scores + (widen(score_bias)[None, :] if score_bias is not None else 0.0)
+    if not n_group:
+        return select_topk(sel, k)
+    if E % n_group or not 1 <= topk_group <= n_group:
+        raise ValueError("need n_group | E and 1 <= topk_group <= n_group")
+    G = E // n_group
+    if k > topk_group * G:
+        raise ValueError("k exceeds the experts of the kept groups")
+    grp = sel.reshape(T, n_group, G)
+    top2 = -np.sort(-grp, axis=2)[:, :, :min(2, G)]
+    gscore = top2.sum(axis=2)
+    gorder = np.argsort(-gscore, axis=1, kind="stable")
+    keep = gorder[:, :topk_group]
+    mask = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(mask, keep, True, axis=1)
+    masked = np.where(np.repeat(mask, G, axis=1), sel, -np.inf)
+    idx, gap_e = select_topk(masked, k)
+    if topk_group < n_group:
+        gs = np.take_along_axis(gscore, gorder[:, :topk_group + 1], axis=1)
+        gap_g = gs[:, topk_group - 1] - gs[:, topk_group]
+    else:
+        gap_g = np.full(T, np.inf)
+    gap = np.minimum(np.where(np.isfinite(gap_e), gap_e, np.inf), gap_g)
+    return idx, gap
+
+
+def route_grouped(*a, **kw):
+    """``route`` with the DeepSeek-V3 selection (alias kept for readability)."""
+    return route(*a, **kw)
 
 
 # --------------------------------------------------------------- dispatch ---
@@ -281,7 +335,8 @@ def combine(y_perm, row_of_slot, topk_w, y_shared=None) -> np.ndarray:
 def moe_forward(x, w_router, router_bias, w_gate, w_up, w_down, *, k: int, gate: int,
                 renormalize: bool, routed_scaling_factor: float = 1.0,
                 capacity_factor: float = 0.0, shared=None,
-                tokens: Optional[np.ndarray] = None):
+                tokens: Optional[np.ndarray] = None, score_bias=None, n_group: int = 0,
+                topk_group: int = 0):
     """The whole layer: route, dispatch, experts, combine (+ shared expert).
 
     Routing and dispatch always run over all T tokens (a token's capacity fate
@@ -295,7 +350,8 @@ def moe_forward(x, w_router, router_bias, w_gate, w_up, w_down, *, k: int, gate:
     """
     T, H = np.asarray(x).shape
     E = np.asarray(w_router).shape[0]
-    r = route(x, w_router, router_bias, k, gate, renormalize, routed_scaling_factor)
+    r = route(x, w_router, router_bias, k, gate, renormalize, routed_scaling_factor,
+              score_bias=score_bias, n_group=n_group, topk_group=topk_group)
     cap = expert_capacity(T, k, E, capacity_factor)
     d = dispatch(r["topk_idx"], E, cap)
     r.update(d)
@@ -320,6 +376,32 @@ def moe_forward(x, w_router, router_bias, w_gate, w_up, w_down, *, k: int, gate:
     if shared is not None:
         y += swiglu_ffn(xw[tok], *shared)
     return y, r
+
+
+# -------------------------------------------------------- routing statistics ---
+
+def aux_loss_terms(counts: np.ndarray, scores: np.ndarray, k: int):
+    """Load-balancing statistics of one batch.
+
+    [MoE-10] "辅助损失": f_i is the counted fraction of the batch routed to expert i
+    (here: of the T*k assignments, so f sums to 1), P_i the mean routing
+    probability of expert i over the batch, and the balance term N * sum_i f_i P_i
+    (the loss is alpha times it; 1 when perfectly uniform).
+    Returns (f [E], P [E], N * sum f P).
+    """
+    counts = np.asarray(counts, dtype=np.float64)
+    T, E = scores.shape
+    f = counts / (T * k)
+    P = np.asarray(scores, dtype=np.float64).mean(axis=0)
+    return f, P, E * float((f * P).sum())
+
+
+def bias_update(bias: np.ndarray, load: np.ndarray, gamma: float) -> np.ndarray:
+    """DeepSeek-V3 bias step ([MoE-10] "DeepSeek-V3 的无辅助损失偏置"): an overloaded
+    expert's bias drops by gamma, an underloaded one's rises by gamma, against
+    the mean load; an expert exactly at the mean keeps its bias."""
+    load = np.asarray(load, dtype=np.float64)
+    return widen(bias) + float(gamma) * np.sign(load.mean() - load)
 
 
 # ------------------------------------------------------- closed-form sizes ---

@@ -27,7 +27,7 @@ import numpy as np
 SEED_ROOT = 2024
 
 # tensor ids of the per-tensor streams
-T_X, T_ROUTER, T_GATE, T_UP, T_DOWN, T_SGATE, T_SUP, T_SDOWN = range(8)
+T_X, T_ROUTER, T_GATE, T_UP, T_DOWN, T_SGATE, T_SUP, T_SDOWN, T_SBIAS = range(9)
 
 GATE_SOFTMAX = 0
 GATE_SIGMOID = 1
@@ -53,6 +53,9 @@ class MoEShape:
     I_shared: int = 0
     dtype: int = BF16
     logit_skew: bool = False    # per-expert router bias 0.5*ln(1/(e+1))
+    n_group: int = 0            # expert groups of the group-limited selection (0: none)
+    topk_group: int = 0         # groups kept per token
+    score_bias_std: float = 0.0  # > 0: draw a selection-only per-expert bias N(0, std^2) in fp32
     cfg_id: int = 0             # seed namespace of x
     weight_cfg_id: int = -1     # seed namespace of the weights (-1: same as cfg_id)
 
@@ -80,6 +83,16 @@ CONFIGS = {
     5: MoEShape("deepseek_v3_decode_bf16", T=16, H=7168, I=2048, E=256, k=8,
                 gate=GATE_SIGMOID, renormalize=True, routed_scaling_factor=2.5,
                 n_shared=1, I_shared=2048, dtype=BF16, cfg_id=5, weight_cfg_id=4),
+}
+
+# DeepSeek-V3's own selection on the same layer: 8 groups of 32 experts, 4 kept,
+# and a selection-only per-expert bias drawn N(0, 0.05^2) (the drift of fifty
+# bias steps of 0.001, comparable to the spread of the sigmoid scores).
+NOAUX = {
+    "prefill": CONFIGS[4].with_(name="deepseek_v3_noaux_prefill_bf16", n_group=8, topk_group=4,
+                                score_bias_std=0.05),
+    "decode": CONFIGS[5].with_(name="deepseek_v3_noaux_decode_bf16", n_group=8, topk_group=4,
+                               score_bias_std=0.05),
 }
 
 
@@ -139,6 +152,7 @@ class MoEInputs:
     ws_gate: Optional[np.ndarray] = None   # [I_s, H]
     ws_up: Optional[np.ndarray] = None     # [I_s, H]
     ws_down: Optional[np.ndarray] = None   # [H, I_s]
+    score_bias: Optional[np.ndarray] = None  # [E] float32, selection only
 
 
 def make_inputs(s: MoEShape, *, with_experts: bool = True,
@@ -182,6 +196,8 @@ def make_inputs(s: MoEShape, *, with_experts: bool = True,
             one(e)
 
     inp = MoEInputs(s, x, w_router, bias, w_gate, w_up, w_down)
+    if s.score_bias_std > 0:
+        inp.score_bias = draw(s.wid, T_SBIAS, 0, (E,), s.score_bias_std, F32)
     if s.n_shared:
         Is = s.I_shared or I
         inp.ws_gate = draw(s.wid, T_SGATE, 0, (Is, H), 1.0 / math.sqrt(H), s.dtype)

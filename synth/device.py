@@ -27,6 +27,8 @@ def upload(inp: MoEInputs, device="cuda") -> dict:
     out = {"x": to_torch(inp.x, device), "w_router": to_torch(inp.w_router, device)}
     if inp.router_bias is not None:
         out["router_bias"] = to_torch(inp.router_bias.astype(np.float32), device)
+    if inp.score_bias is not None:
+        out["score_bias"] = to_torch(inp.score_bias.astype(np.float32), device)
     for name in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
         a = getattr(inp, name)
         if a is not None:

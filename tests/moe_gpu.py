@@ -36,10 +36,15 @@ def widen_out(t: torch.Tensor) -> np.ndarray:
     return ref.widen(bits(t))
 
 
-def oracle_kwargs(s):
-    return dict(k=s.k, gate=s.gate, renormalize=s.renormalize,
-                routed_scaling_factor=float(np.float32(s.routed_scaling_factor)),
-                capacity_factor=float(np.float32(s.capacity_factor)))
+def oracle_kwargs(s, inp=None):
+    kw = dict(k=s.k, gate=s.gate, renormalize=s.renormalize,
+              routed_scaling_factor=float(np.float32(s.routed_scaling_factor)),
+              capacity_factor=float(np.float32(s.capacity_factor)))
+    if s.n_group:
+        kw.update(n_group=s.n_group, topk_group=s.topk_group)
+    if inp is not None and inp.score_bias is not None:
+        kw["score_bias"] = inp.score_bias
+    return kw
 
 
 def alloc_route(s, device="cuda"):
@@ -155,7 +160,7 @@ def full_parity(s, inp, dev=None, n_sample=None, check_tokens=None):
     shared = (inp.ws_gate, inp.ws_up, inp.ws_down) if s.n_shared else None
     tok = np.arange(s.T) if n_sample is None else sample_tokens(s.T, n_sample, seed=s.cfg_id)
     yref, r_ref = ref.moe_forward(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down,
-                                  shared=shared, tokens=tok, **oracle_kwargs(s))
+                                  shared=shared, tokens=tok, **oracle_kwargs(s, inp))
     idx_g, w_g = bits(rg["topk_idx"]), bits(rg["topk_w"])
     ties = compare_routing(s, r_ref, idx_g, w_g)
     cap = r_ref["capacity"]

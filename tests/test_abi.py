@@ -60,6 +60,18 @@ def test_validate_ranges():
     assert moe.validate(c) == 2
 
 
+def test_validate_expert_groups():
+    """Group-limited selection: n_group divides E (at most 64 groups), 1 <= topk_group
+    <= n_group, and the kept groups hold at least k experts."""
+    ds = dict(T=8192, H=7168, I=2048, E=256, k=8, gate=moe.GATE_SIGMOID, routed_scaling_factor=2.5,
+              n_shared=1, I_shared=2048)
+    assert moe.validate(moe.make_config(**ds, n_group=8, topk_group=4)) == 0
+    assert moe.validate(moe.make_config(**ds, n_group=256 // 4, topk_group=2)) == 0     # 64 groups of 4, k = 8
+    for ng, tg in ((7, 4), (8, 0), (8, 9), (-1, 1), (128, 4), (64, 1)):
+        assert moe.validate(moe.make_config(**ds, n_group=ng, topk_group=tg)) == 2, (ng, tg)
+    assert moe.validate(moe.make_config(**ds, n_group=0, topk_group=5)) == 0           # no groups: ignored
+
+
 def test_capacity_and_workspace():
     sw = moe.make_config(8192, 1024, 4096, 64, 1, renormalize=False, capacity_factor=1.25)
     assert moe.capacity(sw) == 160
@@ -99,6 +111,8 @@ def test_launch_entry_points_reject_before_launch():
     assert L.moe_route(p(bad), 16, 16, None, 16, 16, None) == 2
     assert L.moe_route(p(good), None, 16, None, 16, 16, None) == 1
     assert L.moe_route(p(good), 8, 16, None, 16, 16, None) == 6          # misaligned pointer
+    assert L.moe_route_sel(p(good), 16, 16, None, 2, 16, 16, None) == 6  # misaligned selection bias
+    assert L.moe_route_sel(p(bad), 16, 16, None, None, 16, 16, None) == 2
     assert L.moe_combine(p(good), 16, None, 16, None, 16, None) == 1
     assert L.moe_dispatch(p(good), 16, 16, 16, 16, 16, 16, None, None, 0, None) == 4   # no workspace
     assert L.moe_expert_ffn(p(good), 16, 16, 16, 16, 16, 16, 16, 8, None) == 4       # workspace too small

@@ -3,7 +3,7 @@
 The layer runs in libmoe.so's HIP kernels behind a C ABI (include/moe.h); this
 package is its thin ctypes binding.  The entry points keep the C names:
 
-    moe_route, moe_dispatch, moe_expert_ffn, moe_combine, moe_forward,
+    moe_route (moe_route_sel), moe_dispatch, moe_expert_ffn, moe_combine, moe_forward,
     moe_validate, moe_workspace_size, moe_capacity, moe_layer_params
 """
 from ._lib import (BF16, EXPORTS, F32, GATE_SIGMOID, GATE_SOFTMAX, STAGE_EVENTS, MoeConfig, MoeError,  # noqa: F401
@@ -11,6 +11,7 @@ from ._lib import (BF16, EXPORTS, F32, GATE_SIGMOID, GATE_SOFTMAX, STAGE_EVENTS,
                    forward, layer_params, lib, make_config, route, status_str, validate, workspace_size)
 
 moe_route = route
+moe_route_sel = route
 moe_dispatch = dispatch
 moe_expert_ffn = expert_ffn
 moe_combine = combine

@@ -22,19 +22,21 @@ STAGE_EVENTS = 6
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_capacity", "moe_layer_params",
-           "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_timed")
+           "moe_route", "moe_route_sel", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
+           "moe_forward_timed")
 
 
 class MoeConfig(ctypes.Structure):
     _fields_ = [("T", c_int64), ("H", c_int64), ("I", c_int64), ("E", c_int64), ("k", c_int64),
                 ("gate", c_int32), ("renormalize", c_int32), ("routed_scaling_factor", c_float),
                 ("capacity_factor", c_float), ("n_shared", c_int64), ("I_shared", c_int64),
-                ("dtype", c_int32)]
+                ("dtype", c_int32), ("n_group", c_int32), ("topk_group", c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [("w_router", c_void_p), ("router_bias", c_void_p), ("w_gate", c_void_p), ("w_up", c_void_p),
-                ("w_down", c_void_p), ("ws_gate", c_void_p), ("ws_up", c_void_p), ("ws_down", c_void_p)]
+                ("w_down", c_void_p), ("ws_gate", c_void_p), ("ws_up", c_void_p), ("ws_down", c_void_p),
+                ("score_bias", c_void_p)]
 
 
 class MoeRouteOut(ctypes.Structure):
@@ -72,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_params.argtypes = [P, POINTER(c_int64), POINTER(c_int64)]
         L.moe_route.restype = c_int32
         L.moe_route.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.moe_route_sel.restype = c_int32
+        L.moe_route_sel.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.moe_dispatch.restype = c_int32
         L.moe_dispatch.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_size_t, c_void_p]
@@ -91,17 +95,18 @@ def lib() -> ctypes.CDLL:
 
 
 def make_config(T, H, I, E, k, gate=GATE_SOFTMAX, renormalize=True, routed_scaling_factor=1.0,
-                capacity_factor=0.0, n_shared=0, I_shared=0, dtype=BF16) -> MoeConfig:
+                capacity_factor=0.0, n_shared=0, I_shared=0, dtype=BF16, n_group=0, topk_group=0) -> MoeConfig:
     return MoeConfig(int(T), int(H), int(I), int(E), int(k), int(gate), int(bool(renormalize)),
                      float(routed_scaling_factor), float(capacity_factor), int(n_shared),
-                     int(I_shared if n_shared else 0), int(dtype))
+                     int(I_shared if n_shared else 0), int(dtype), int(n_group), int(topk_group))
 
 
 def config_from_shape(s, **over) -> MoeConfig:
     """MoeConfig from an object with the MoEShape fields."""
     kw = dict(T=s.T, H=s.H, I=s.I, E=s.E, k=s.k, gate=s.gate, renormalize=s.renormalize,
               routed_scaling_factor=s.routed_scaling_factor, capacity_factor=s.capacity_factor,
-              n_shared=s.n_shared, I_shared=s.I_shared, dtype=s.dtype)
+              n_shared=s.n_shared, I_shared=s.I_shared, dtype=s.dtype,
+              n_group=getattr(s, "n_group", 0), topk_group=getattr(s, "topk_group", 0))
     kw.update(over)
     return make_config(**kw)
 
@@ -150,9 +155,15 @@ def layer_params(cfg: MoeConfig):
     return t.value, a.value
 
 
-def route(cfg, x, w_router, router_bias, topk_idx, topk_w, stream=None):
-    _check(lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(topk_idx),
-                           _ptr(topk_w), _stream(stream)), "moe_route")
+def route(cfg, x, w_router, router_bias, topk_idx, topk_w, stream=None, score_bias=None):
+    """moe_route, or moe_route_sel when a selection-only ``score_bias`` is given."""
+    if score_bias is None:
+        _check(lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(topk_idx),
+                               _ptr(topk_w), _stream(stream)), "moe_route")
+    else:
+        _check(lib().moe_route_sel(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                   _ptr(score_bias), _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
+               "moe_route_sel")
 
 
 def dispatch(cfg, topk_idx, x, counts, offsets, row_of_slot, token_of_row, x_perm, ws, stream=None):
@@ -176,7 +187,7 @@ def weights_struct(w) -> MoeWeights:
     """MoeWeights from a dict of tensors (missing keys -> NULL)."""
     g = lambda n: _ptr(w.get(n))  # noqa: E731
     return MoeWeights(g("w_router"), g("router_bias"), g("w_gate"), g("w_up"), g("w_down"), g("ws_gate"),
-                      g("ws_up"), g("ws_down"))
+                      g("ws_up"), g("ws_down"), g("score_bias"))
 
 
 def route_out_struct(r) -> Optional[MoeRouteOut]:

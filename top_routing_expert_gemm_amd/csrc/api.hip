@@ -114,6 +114,11 @@ moe_status moe_validate(const moe_config* c) {
   const int64_t rows = c->T * c->k + c->T;
   if (c->T > (int64_t(1) << 31) || rows >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
   if (c->H > (int64_t(1) << 20) || c->I > (int64_t(1) << 20)) return MOE_ERR_SHAPE;
+  if (c->n_group < 0 || c->n_group > 64) return MOE_ERR_SHAPE;
+  if (c->n_group > 0) {
+    if (c->E % c->n_group != 0 || c->topk_group < 1 || c->topk_group > c->n_group) return MOE_ERR_SHAPE;
+    if (c->k > (int64_t)c->topk_group * (c->E / c->n_group)) return MOE_ERR_SHAPE;
+  }
   return MOE_OK;
 }
 
@@ -140,16 +145,22 @@ moe_status moe_layer_params(const moe_config* c, int64_t* total, int64_t* active
   return MOE_OK;
 }
 
-moe_status moe_route(const moe_config* c, const void* x, const void* w_router, const float* router_bias,
-                     int32_t* topk_idx, float* topk_w, void* stream) {
+moe_status moe_route_sel(const moe_config* c, const void* x, const void* w_router, const float* router_bias,
+                         const float* score_bias, int32_t* topk_idx, float* topk_w, void* stream) {
   MOE_TRY(moe_validate(c));
   MOE_TRY(need(x));
   MOE_TRY(need(w_router));
   MOE_TRY(need(topk_idx));
   MOE_TRY(need(topk_w));
   MOE_TRY(opt(router_bias));
-  HIP_TRY(launch_route(*c, x, w_router, router_bias, topk_idx, topk_w, S(stream)));
+  MOE_TRY(opt(score_bias));
+  HIP_TRY(launch_route(*c, x, w_router, router_bias, score_bias, topk_idx, topk_w, S(stream)));
   return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* c, const void* x, const void* w_router, const float* router_bias,
+                     int32_t* topk_idx, float* topk_w, void* stream) {
+  return moe_route_sel(c, x, w_router, router_bias, nullptr, topk_idx, topk_w, stream);
 }
 
 moe_status moe_dispatch(const moe_config* c, const int32_t* topk_idx, const void* x, int32_t* counts,
@@ -234,6 +245,7 @@ moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const vo
   MOE_TRY(need(y));
   MOE_TRY(need(w->w_router));
   MOE_TRY(opt(w->router_bias));
+  MOE_TRY(opt(w->score_bias));
   MOE_TRY(need(w->w_gate));
   MOE_TRY(need(w->w_up));
   MOE_TRY(need(w->w_down));
@@ -271,7 +283,8 @@ moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const vo
   int32_t* nch = reinterpret_cast<int32_t*>(at(ws, L.n_chunks));
 
   HIP_TRY(mark(0));
-  HIP_TRY(launch_route_split(*c, x, w->w_router, w->router_bias, r.topk_idx, r.topk_w, at(ws, L.rscratch), s));
+  HIP_TRY(launch_route_split(*c, x, w->w_router, w->router_bias, w->score_bias, r.topk_idx, r.topk_w,
+                             at(ws, L.rscratch), s));
   HIP_TRY(mark(1));
   HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), r.topk_idx, r.counts, r.offsets, r.row_of_slot,
                           r.token_of_row, at(ws, L.dscratch), chunks, nch, bm, sh, Tk, s));

@@ -54,15 +54,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // ---- launches (each returns hipGetLastError() of its launch) ----
 
-// Router GEMM + gate + top-k.  x, w: bf16 or fp32 per dtype.
+// Router GEMM + gate + top-k.  x, w: bf16 or fp32 per dtype.  sbias: the
+// selection-only bias (or NULL); grouping from c.n_group / c.topk_group.
 hipError_t launch_route(const moe_config& c, const void* x, const void* w, const float* bias,
-                        int32_t* topk_idx, float* topk_w, hipStream_t s);
+                        const float* sbias, int32_t* topk_idx, float* topk_w, hipStream_t s);
 
 // Split-K router (bf16): partial logits in `scratch` (route_scratch_bytes), then
 // a per-token reduce + gate + top-k.  fp32 configs fall back to launch_route.
 size_t route_scratch_bytes(const moe_config& c);
 hipError_t launch_route_split(const moe_config& c, const void* x, const void* w, const float* bias,
-                              int32_t* topk_idx, float* topk_w, void* scratch, hipStream_t s);
+                              const float* sbias, int32_t* topk_idx, float* topk_w, void* scratch, hipStream_t s);
 
 // Dispatch scratch sizes (bytes) for T*k assignments and E experts.
 size_t dispatch_scratch_bytes(int64_t Tk, int64_t E);

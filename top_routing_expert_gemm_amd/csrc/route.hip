@@ -44,59 +44,159 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
+// Options of the DeepSeek-V3 selection: selection-only bias and group limit.
+struct SelOpts {
+  const float* sbias;  // [E] or NULL
+  int n_group;         // 0: no groups
+  int topk_group;
+  float* wbuf;         // this wave's LDS scratch of E floats (used when n_group > 0)
+};
+
 // Gate + top-k of one token, run by one whole wave.  z[v] holds the logit of
-// expert lane + 64 v (-inf past E).  Both gates are increasing functions of z,
-// so the k best scores are the k largest logits; selection is done on z, which
-// keeps full fp32 resolution.
+// expert lane + 64 v (-inf past E).
+//  * Plain selection: both gates are increasing functions of z, so the k best
+//    scores are the k largest logits; selection is done on z, which keeps full
+//    fp32 resolution.
+//  * With a selection bias or groups ([MoE-10] "DeepSeek-V3 的无辅助损失偏置"):
+//    experts are ranked by gate score + bias, groups by the sum of their two
+//    best ranking scores, only the topk_group best groups stay eligible, and
+//    the weights are the unbiased scores of the picks.
+// Ties go to the lower expert (or group) index.  Lanes j < k write pick j.
 template <int VPL>
-__device__ void topk_token(float (&z)[VPL], int E, int k, int gate, int renorm, float scale,
+__device__ void topk_token(float (&z)[VPL], int E, int k, int gate, int renorm, float scale, const SelOpts& o,
                            int32_t* out_idx, float* out_w) {
   const int lane = threadIdx.x & (kWave - 1);
+  const bool plain = o.sbias == nullptr && o.n_group == 0;
   bool taken[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) taken[v] = false;
-  float selz = -INFINITY;
+  float selz = -INFINITY, selsc = 0.f;
   int seli = 0;
+
+  if (plain) {
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int e = lane + kWave * v;
+        if (e < E && !taken[v] && (z[v] > bv || bi == 0x7fffffff)) { bv = z[v]; bi = e; }
+      }
+      wave_argmax(bv, bi);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        if (lane + kWave * v == bi) taken[v] = true;
+      if (lane == j) { selz = bv; seli = bi; }
+    }
+    const bool mine = lane < k;
+    float w;
+    if (gate == MOE_GATE_SOFTMAX) {
+      if (renorm) {
+        // p_j / sum_sel p = exp(z_j - z_best) / sum_sel exp(z - z_best)
+        const float zbest = __shfl(selz, 0, kWave);
+        const float ex = mine ? expf(selz - zbest) : 0.f;
+        w = ex / wave_sum(ex);
+      } else {
+        // full softmax over all E experts
+        float m = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+          if (lane + kWave * v < E) m = fmaxf(m, z[v]);
+        m = wave_max(m);
+        float s = 0.f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+          if (lane + kWave * v < E) s += expf(z[v] - m);
+        s = wave_sum(s);
+        w = mine ? expf(selz - m) / s : 0.f;
+      }
+    } else {
+      const float sg = mine ? 1.f / (1.f + expf(-selz)) : 0.f;
+      w = renorm ? sg / wave_sum(sg) : sg;
+    }
+    if (mine) {
+      out_idx[lane] = seli;
+      out_w[lane] = w * scale;
+    }
+    return;
+  }
+
+  // ---- DeepSeek-V3 selection ----
+  float m = -INFINITY, den = 0.f;
+  if (gate == MOE_GATE_SOFTMAX) {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (lane + kWave * v < E) m = fmaxf(m, z[v]);
+    m = wave_max(m);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (lane + kWave * v < E) den += expf(z[v] - m);
+    den = wave_sum(den);
+  }
+  float sc[VPL], sel[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = lane + kWave * v;
+    if (e < E) {
+      sc[v] = gate == MOE_GATE_SOFTMAX ? expf(z[v] - m) / den : 1.f / (1.f + expf(-z[v]));
+      sel[v] = o.sbias != nullptr ? sc[v] + o.sbias[e] : sc[v];
+    } else {
+      sc[v] = 0.f;
+      sel[v] = -INFINITY;
+    }
+  }
+  if (o.n_group > 0) {
+    const int G = E / o.n_group;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = lane + kWave * v;
+      if (e < E) o.wbuf[e] = sel[v];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's scratch writes are done
+    __builtin_amdgcn_wave_barrier();
+    float gs = -INFINITY;
+    if (lane < o.n_group) {  // group score: sum of its two best ranking scores
+      float b1 = -INFINITY, b2 = -INFINITY;
+      for (int i = 0; i < G; ++i) {
+        const float v = o.wbuf[lane * G + i];
+        if (v > b1) { b2 = b1; b1 = v; }
+        else if (v > b2) b2 = v;
+      }
+      gs = G >= 2 ? b1 + b2 : b1;
+    }
+    uint64_t kept = 0;
+    for (int q = 0; q < o.topk_group; ++q) {
+      const bool cand = lane < o.n_group && !((kept >> lane) & 1);
+      float bv = cand ? gs : -INFINITY;
+      int bi = cand ? lane : 0x7fffffff;
+      wave_argmax(bv, bi);
+      kept |= 1ull << bi;
+    }
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = lane + kWave * v;
+      if (e < E && !((kept >> (e / G)) & 1)) sel[v] = -INFINITY;
+    }
+    __builtin_amdgcn_wave_barrier();  // scratch reads done before a later token's writes
+  }
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
+    float bv = -INFINITY, cs = 0.f;
     int bi = 0x7fffffff;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int e = lane + kWave * v;
-      if (e < E && !taken[v] && (z[v] > bv || bi == 0x7fffffff)) { bv = z[v]; bi = e; }
+      if (e < E && !taken[v] && (sel[v] > bv || bi == 0x7fffffff)) { bv = sel[v]; bi = e; cs = sc[v]; }
     }
     wave_argmax(bv, bi);
+    const float wsc = __shfl(cs, bi & (kWave - 1), kWave);  // the owner's local best is the winner
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
       if (lane + kWave * v == bi) taken[v] = true;
-    if (lane == j) { selz = bv; seli = bi; }
+    if (lane == j) { selsc = wsc; seli = bi; }
   }
   const bool mine = lane < k;
-  float w;
-  if (gate == MOE_GATE_SOFTMAX) {
-    if (renorm) {
-      // p_j / sum_sel p = exp(z_j - z_best) / sum_sel exp(z - z_best)
-      const float zbest = __shfl(selz, 0, kWave);
-      const float ex = mine ? expf(selz - zbest) : 0.f;
-      w = ex / wave_sum(ex);
-    } else {
-      // full softmax over all E experts
-      float m = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v)
-        if (lane + kWave * v < E) m = fmaxf(m, z[v]);
-      m = wave_max(m);
-      float s = 0.f;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v)
-        if (lane + kWave * v < E) s += expf(z[v] - m);
-      s = wave_sum(s);
-      w = mine ? expf(selz - m) / s : 0.f;
-    }
-  } else {
-    const float sg = mine ? 1.f / (1.f + expf(-selz)) : 0.f;
-    w = renorm ? sg / wave_sum(sg) : sg;
-  }
+  const float w0 = mine ? selsc : 0.f;
+  const float w = renorm ? w0 / wave_sum(w0) : w0;
   if (mine) {
     out_idx[lane] = seli;
     out_w[lane] = w * scale;
@@ -207,14 +307,15 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x, cons
 template <int NBW>
 __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias,
-    int T, int H, int E, int k, int gate, int renorm, float scale, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w) {
+    int T, int H, int E, int k, int gate, int renorm, float scale, const float* __restrict__ sbias, int n_group,
+    int topk_group, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   constexpr int VPL = 2 * NBW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);                 // [2][32][64] bf16
   float* lg = reinterpret_cast<float*>(smem + 2 * kRBM * kRBK * 2);  // [32][lde]
   const int nblk = (E + 31) / 32;
   const int lde = nblk * 32 + 4;
+  float* wscr = lg + kRBM * lde;                                     // [4][nblk*32] group scratch
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kRBM;
 
@@ -239,6 +340,7 @@ __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(
   }
   __syncthreads();
 
+  const SelOpts o{sbias, n_group, topk_group, wscr + wave * nblk * 32};
   for (int row = wave; row < kRBM; row += 4) {
     const int t = t0 + row;
     if (t >= T) break;
@@ -248,7 +350,7 @@ __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(
       const int e = lane + kWave * v;
       z[v] = e < E ? lg[row * lde + e] : -INFINITY;
     }
-    topk_token<VPL>(z, E, k, gate, renorm, scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
+    topk_token<VPL>(z, E, k, gate, renorm, scale, o, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
   }
 }
 
@@ -292,8 +394,10 @@ template <int VPL>
 __global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __restrict__ part, int nsplit, int T,
                                                                int E, const float* __restrict__ bias, int k,
                                                                int gate, int renorm, float scale,
-                                                               int32_t* __restrict__ topk_idx,
+                                                               const float* __restrict__ sbias, int n_group,
+                                                               int topk_group, int32_t* __restrict__ topk_idx,
                                                                float* __restrict__ topk_w) {
+  __shared__ float wscr[kRThreads / kWave][kMaxE];
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kRThreads / kWave) + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -321,7 +425,8 @@ __global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __re
       z[v] = -INFINITY;
     }
   }
-  topk_token<VPL>(z, E, k, gate, renorm, scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
+  const SelOpts o{sbias, n_group, topk_group, wscr[threadIdx.x >> 6]};
+  topk_token<VPL>(z, E, k, gate, renorm, scale, o, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
 }
 
 // fp32 path: one wave per token computes its E logits with lane-strided dot
@@ -329,8 +434,9 @@ __global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __re
 template <int VPL>
 __global__ __launch_bounds__(kRThreads) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias, int T,
-    int H, int E, int k, int gate, int renorm, float scale, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w) {
+    int H, int E, int k, int gate, int renorm, float scale, const float* __restrict__ sbias, int n_group,
+    int topk_group, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  __shared__ float wscr[kRThreads / kWave][kMaxE];
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kRThreads / kWave) + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -356,32 +462,35 @@ __global__ __launch_bounds__(kRThreads) void route_f32_kernel(
       if (lane == el) z[v] = s;
     }
   }
-  topk_token<VPL>(z, E, k, gate, renorm, scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
+  const SelOpts o{sbias, n_group, topk_group, wscr[threadIdx.x >> 6]};
+  topk_token<VPL>(z, E, k, gate, renorm, scale, o, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
 }
 
 template <int NBW>
 hipError_t launch_route_bf16(const moe_config& c, const void* x, const void* w, const float* bias,
-                             int32_t* idx, float* tw, hipStream_t s) {
+                             const float* sbias, int32_t* idx, float* tw, hipStream_t s) {
   const int nblk = (int)((c.E + 31) / 32);
-  const size_t lds = 2 * kRBM * kRBK * 2 + (size_t)kRBM * (nblk * 32 + 4) * 4;
+  const size_t lds = 2 * kRBM * kRBK * 2 + (size_t)kRBM * (nblk * 32 + 4) * 4 + (size_t)4 * nblk * 32 * 4;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_bf16_kernel<NBW>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int grid = (int)((c.T + kRBM - 1) / kRBM);
   hipLaunchKernelGGL(route_bf16_kernel<NBW>, dim3(grid), dim3(kRThreads), lds, s,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias, (int)c.T,
-                     (int)c.H, (int)c.E, (int)c.k, c.gate, c.renormalize, c.routed_scaling_factor, idx, tw);
+                     (int)c.H, (int)c.E, (int)c.k, c.gate, c.renormalize, c.routed_scaling_factor, sbias, c.n_group,
+                     c.topk_group, idx, tw);
   return hipGetLastError();
 }
 
 template <int VPL>
 hipError_t launch_route_f32(const moe_config& c, const void* x, const void* w, const float* bias,
-                            int32_t* idx, float* tw, hipStream_t s) {
+                            const float* sbias, int32_t* idx, float* tw, hipStream_t s) {
   const int per = kRThreads / kWave;
   const int grid = (int)((c.T + per - 1) / per);
   hipLaunchKernelGGL(route_f32_kernel<VPL>, dim3(grid), dim3(kRThreads), 0, s,
                      static_cast<const float*>(x), static_cast<const float*>(w), bias, (int)c.T,
-                     (int)c.H, (int)c.E, (int)c.k, c.gate, c.renormalize, c.routed_scaling_factor, idx, tw);
+                     (int)c.H, (int)c.E, (int)c.k, c.gate, c.renormalize, c.routed_scaling_factor, sbias, c.n_group,
+                     c.topk_group, idx, tw);
   return hipGetLastError();
 }
 
@@ -401,7 +510,7 @@ inline int route_nsplit(int64_t T, int64_t H, int64_t E) {
 
 template <int NBW, int RBT>
 hipError_t launch_route_split_t(const moe_config& c, const void* x, const void* w, const float* bias,
-                                int32_t* idx, float* tw, float* part, hipStream_t s) {
+                                const float* sbias, int32_t* idx, float* tw, float* part, hipStream_t s) {
   const int nsplit = route_nsplit(c.T, c.H, c.E);
   const int nk = (int)(c.H / kRBK);
   const int per = (nk + nsplit - 1) / nsplit;
@@ -415,16 +524,16 @@ hipError_t launch_route_split_t(const moe_config& c, const void* x, const void* 
   const int tpb = kRThreads / kWave;
   hipLaunchKernelGGL(route_topk_kernel<2 * NBW>, dim3((unsigned)((c.T + tpb - 1) / tpb)), dim3(kRThreads), 0, s,
                      part, nsplit_eff, (int)c.T, (int)c.E, bias, (int)c.k, c.gate, c.renormalize,
-                     c.routed_scaling_factor, idx, tw);
+                     c.routed_scaling_factor, sbias, c.n_group, c.topk_group, idx, tw);
   return hipGetLastError();
 }
 
 template <int NBW>
 hipError_t launch_route_split_n(const moe_config& c, const void* x, const void* w, const float* bias,
-                                int32_t* idx, float* tw, float* part, hipStream_t s) {
+                                const float* sbias, int32_t* idx, float* tw, float* part, hipStream_t s) {
   if constexpr (NBW <= 4)
-    if (route_rbt(c.T, c.E) == 2) return launch_route_split_t<NBW, 2>(c, x, w, bias, idx, tw, part, s);
-  return launch_route_split_t<NBW, 1>(c, x, w, bias, idx, tw, part, s);
+    if (route_rbt(c.T, c.E) == 2) return launch_route_split_t<NBW, 2>(c, x, w, bias, sbias, idx, tw, part, s);
+  return launch_route_split_t<NBW, 1>(c, x, w, bias, sbias, idx, tw, part, s);
 }
 
 }  // namespace
@@ -436,26 +545,26 @@ size_t route_scratch_bytes(const moe_config& c) {
 }
 
 hipError_t launch_route_split(const moe_config& c, const void* x, const void* w, const float* bias,
-                              int32_t* topk_idx, float* topk_w, void* scratch, hipStream_t s) {
-  if (c.dtype != MOE_BF16) return launch_route(c, x, w, bias, topk_idx, topk_w, s);
+                              const float* sbias, int32_t* topk_idx, float* topk_w, void* scratch, hipStream_t s) {
+  if (c.dtype != MOE_BF16) return launch_route(c, x, w, bias, sbias, topk_idx, topk_w, s);
   float* part = static_cast<float*>(scratch);
-  if (c.E <= 128) return launch_route_split_n<1>(c, x, w, bias, topk_idx, topk_w, part, s);
-  if (c.E <= 256) return launch_route_split_n<2>(c, x, w, bias, topk_idx, topk_w, part, s);
-  if (c.E <= 512) return launch_route_split_n<4>(c, x, w, bias, topk_idx, topk_w, part, s);
-  return launch_route_split_n<8>(c, x, w, bias, topk_idx, topk_w, part, s);
+  if (c.E <= 128) return launch_route_split_n<1>(c, x, w, bias, sbias, topk_idx, topk_w, part, s);
+  if (c.E <= 256) return launch_route_split_n<2>(c, x, w, bias, sbias, topk_idx, topk_w, part, s);
+  if (c.E <= 512) return launch_route_split_n<4>(c, x, w, bias, sbias, topk_idx, topk_w, part, s);
+  return launch_route_split_n<8>(c, x, w, bias, sbias, topk_idx, topk_w, part, s);
 }
 
-hipError_t launch_route(const moe_config& c, const void* x, const void* w, const float* bias,
+hipError_t launch_route(const moe_config& c, const void* x, const void* w, const float* bias, const float* sbias,
                         int32_t* topk_idx, float* topk_w, hipStream_t s) {
   if (c.dtype == MOE_BF16) {
-    if (c.E <= 128) return launch_route_bf16<1>(c, x, w, bias, topk_idx, topk_w, s);
-    if (c.E <= 256) return launch_route_bf16<2>(c, x, w, bias, topk_idx, topk_w, s);
-    if (c.E <= 512) return launch_route_bf16<4>(c, x, w, bias, topk_idx, topk_w, s);
-    return launch_route_bf16<8>(c, x, w, bias, topk_idx, topk_w, s);
+    if (c.E <= 128) return launch_route_bf16<1>(c, x, w, bias, sbias, topk_idx, topk_w, s);
+    if (c.E <= 256) return launch_route_bf16<2>(c, x, w, bias, sbias, topk_idx, topk_w, s);
+    if (c.E <= 512) return launch_route_bf16<4>(c, x, w, bias, sbias, topk_idx, topk_w, s);
+    return launch_route_bf16<8>(c, x, w, bias, sbias, topk_idx, topk_w, s);
   }
-  if (c.E <= 64) return launch_route_f32<1>(c, x, w, bias, topk_idx, topk_w, s);
-  if (c.E <= 256) return launch_route_f32<4>(c, x, w, bias, topk_idx, topk_w, s);
-  return launch_route_f32<16>(c, x, w, bias, topk_idx, topk_w, s);
+  if (c.E <= 64) return launch_route_f32<1>(c, x, w, bias, sbias, topk_idx, topk_w, s);
+  if (c.E <= 256) return launch_route_f32<4>(c, x, w, bias, sbias, topk_idx, topk_w, s);
+  return launch_route_f32<16>(c, x, w, bias, sbias, topk_idx, topk_w, s);
 }
 
 }  // namespace moe
