@@ -113,6 +113,8 @@ typedef struct {
   int32_t *offsets;      /* [E + 1] exclusive scan of the kept load per expert */
   int32_t *row_of_slot;  /* [T, k] row in expert-contiguous order, -1 if dropped */
   int32_t *token_of_row; /* [T*k] token of each kept row; first offsets[E] valid */
+  float *scores;         /* [T, E] gate score of every expert (float32), or NULL: not
+                          * written.  The input of moe_balance_stats. */
 } moe_route_out;
 
 /* Human-readable name of a status code (static string). */
@@ -148,10 +150,34 @@ moe_status moe_route(const moe_config *cfg, const void *x, const void *w_router,
 /* moe_route with a selection-only expert bias (score_bias [E] float32 or NULL;
  * see moe_weights.score_bias) and the group limit of cfg->n_group /
  * cfg->topk_group ([MoE-10] "DeepSeek-V3 的无辅助损失偏置").  Ties of ranking
- * scores go to the lower expert id, of group scores to the lower group id. */
+ * scores go to the lower expert id, of group scores to the lower group id.
+ * scores: NULL, or [T, E] float32 that receives every expert's gate score
+ * (softmax over E, or sigmoid per expert; the bias is not added). */
 moe_status moe_route_sel(const moe_config *cfg, const void *x, const void *w_router,
                          const float *router_bias, const float *score_bias, int32_t *topk_idx,
-                         float *topk_w, void *stream);
+                         float *topk_w, float *scores, void *stream);
+
+/* Load-balancing statistics of one routed batch ([MoE-10] "辅助损失": f_i is the
+ * share of the batch routed to expert i, P_i the mean routing probability of
+ * expert i, and the balance term is N * sum_i f_i P_i, 1.0 for a perfectly even
+ * router; an auxiliary loss is alpha times it).  Inputs: counts [E] (int32, the
+ * demand per expert as moe_dispatch writes it) and scores [T, E] (float32, as
+ * moe_route_sel writes it).  Outputs, each optional (NULL = not written):
+ * score_mean [E] = P_i = sum_t scores[t,i] / T, load_frac [E] = f_i =
+ * counts[i] / (T k), balance [1] = E * sum_i f_i P_i.  All float32, summed in a
+ * fixed order (deterministic).  ws: at least ceil(T/256) * E * 4 bytes of device
+ * scratch (moe_workspace_size() bytes always suffice). */
+moe_status moe_balance_stats(const moe_config *cfg, const int32_t *counts, const float *scores,
+                             float *score_mean, float *load_frac, float *balance, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* One step of the auxiliary-loss-free balancing ([MoE-10] "DeepSeek-V3 的无辅助
+ * 损失偏置"): score_bias[i] += gamma when counts[i] is below the mean load
+ * sum(counts) / E, -= gamma when above, unchanged when equal (compared exactly
+ * in integers; the add is float32).  counts [E] int32, score_bias [E] float32,
+ * updated in place on the device. */
+moe_status moe_bias_update(const moe_config *cfg, const int32_t *counts, float gamma,
+                           float *score_bias, void *stream);
 
 /* Histogram, stable scan and capacity, then the gather ([MoE-10] simplified
  * Mixtral block: the rows of each expert are collected; "负载不均": overflow is
@@ -188,7 +214,8 @@ moe_status moe_combine(const moe_config *cfg, const void *y_perm, const int32_t 
 /* The whole layer: route, dispatch (gather fused into the expert GEMM's A-tile
  * loader), grouped gate/up + SwiGLU, grouped down, combine; the shared expert
  * runs as one more group over all T tokens.  y [T,H] is the FFN output only
- * (the caller adds the residual).  route_out may be NULL. */
+ * (the caller adds the residual).  route_out may be NULL; its NULL members are
+ * kept in the workspace instead (scores: not computed). */
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
                        moe_route_out *route_out, void *ws, size_t ws_bytes, void *stream);
 

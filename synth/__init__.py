@@ -206,6 +206,19 @@ def make_inputs(s: MoEShape, *, with_experts: bool = True,
     return inp
 
 
+def balance_inputs(T: int, E: int, k: int, seed: int, gamma_std: float = 0.01):
+    """Seeded inputs of the routing statistics and the bias step, drawn directly:
+    scores [T, E] float32 uniform in [0, 1); counts [E] int32, a multinomial
+    draw of T*k assignments over a skewed Dirichlet(0.5) expert popularity;
+    bias [E] float32 N(0, gamma_std^2)."""
+    g = _stream(seed, T_SBIAS + 1, 0)
+    scores = g.random((T, E), dtype=np.float32)
+    p = g.dirichlet(np.full(E, 0.5))
+    counts = g.multinomial(T * k, p).astype(np.int32)
+    bias = (g.standard_normal(E, dtype=np.float32) * np.float32(gamma_std)).astype(np.float32)
+    return scores, counts, bias
+
+
 def expert_weights(s: MoEShape, e: int):
     """Re-draw routed expert ``e``'s (w_gate, w_up, w_down) alone."""
     return (draw(s.wid, T_GATE, e, (s.I, s.H), 1.0 / math.sqrt(s.H), s.dtype),

@@ -111,8 +111,14 @@ def test_launch_entry_points_reject_before_launch():
     assert L.moe_route(p(bad), 16, 16, None, 16, 16, None) == 2
     assert L.moe_route(p(good), None, 16, None, 16, 16, None) == 1
     assert L.moe_route(p(good), 8, 16, None, 16, 16, None) == 6          # misaligned pointer
-    assert L.moe_route_sel(p(good), 16, 16, None, 2, 16, 16, None) == 6  # misaligned selection bias
-    assert L.moe_route_sel(p(bad), 16, 16, None, None, 16, 16, None) == 2
+    assert L.moe_route_sel(p(good), 16, 16, None, 2, 16, 16, None, None) == 6  # misaligned selection bias
+    assert L.moe_route_sel(p(good), 16, 16, None, None, 16, 16, 4, None) == 6  # misaligned scores
+    assert L.moe_route_sel(p(bad), 16, 16, None, None, 16, 16, None, None) == 2
+    assert L.moe_balance_stats(p(good), 16, 16, None, None, None, None, 0, None) == 4   # no workspace
+    assert L.moe_balance_stats(p(good), 16, 16, None, None, None, 16, 15, None) == 4    # 1 chunk x 4 experts
+    assert L.moe_balance_stats(p(good), None, 16, None, None, None, 16, 16, None) == 1
+    assert L.moe_bias_update(p(good), 16, float("nan"), 16, None) == 2
+    assert L.moe_bias_update(p(good), 16, 0.001, None, None) == 1
     assert L.moe_combine(p(good), 16, None, 16, None, 16, None) == 1
     assert L.moe_dispatch(p(good), 16, 16, 16, 16, 16, 16, None, None, 0, None) == 4   # no workspace
     assert L.moe_expert_ffn(p(good), 16, 16, 16, 16, 16, 16, 16, 8, None) == 4       # workspace too small

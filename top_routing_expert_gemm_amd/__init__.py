@@ -3,15 +3,19 @@
 The layer runs in libmoe.so's HIP kernels behind a C ABI (include/moe.h); this
 package is its thin ctypes binding.  The entry points keep the C names:
 
-    moe_route (moe_route_sel), moe_dispatch, moe_expert_ffn, moe_combine, moe_forward,
-    moe_validate, moe_workspace_size, moe_capacity, moe_layer_params
+    moe_route, moe_route_sel, moe_dispatch, moe_expert_ffn, moe_combine, moe_forward,
+    moe_balance_stats, moe_bias_update, moe_validate, moe_workspace_size, moe_capacity,
+    moe_layer_params
 """
 from ._lib import (BF16, EXPORTS, F32, GATE_SIGMOID, GATE_SOFTMAX, STAGE_EVENTS, MoeConfig, MoeError,  # noqa: F401
-                   MoeRouteOut, MoeWeights, capacity, combine, config_from_shape, dispatch, expert_ffn,
-                   forward, layer_params, lib, make_config, route, status_str, validate, workspace_size)
+                   MoeRouteOut, MoeWeights, balance_stats, bias_update, capacity, combine, config_from_shape,
+                   dispatch, expert_ffn, forward, layer_params, lib, make_config, route, route_sel, status_str,
+                   validate, workspace_size)
 
 moe_route = route
-moe_route_sel = route
+moe_route_sel = route_sel
+moe_balance_stats = balance_stats
+moe_bias_update = bias_update
 moe_dispatch = dispatch
 moe_expert_ffn = expert_ffn
 moe_combine = combine

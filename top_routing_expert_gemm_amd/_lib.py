@@ -22,8 +22,8 @@ STAGE_EVENTS = 6
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_capacity", "moe_layer_params",
-           "moe_route", "moe_route_sel", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "moe_forward_timed")
+           "moe_route", "moe_route_sel", "moe_balance_stats", "moe_bias_update", "moe_dispatch",
+           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_timed")
 
 
 class MoeConfig(ctypes.Structure):
@@ -41,7 +41,7 @@ class MoeWeights(ctypes.Structure):
 
 class MoeRouteOut(ctypes.Structure):
     _fields_ = [("topk_idx", c_void_p), ("topk_w", c_void_p), ("counts", c_void_p), ("offsets", c_void_p),
-                ("row_of_slot", c_void_p), ("token_of_row", c_void_p)]
+                ("row_of_slot", c_void_p), ("token_of_row", c_void_p), ("scores", c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -75,7 +75,13 @@ def lib() -> ctypes.CDLL:
         L.moe_route.restype = c_int32
         L.moe_route.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.moe_route_sel.restype = c_int32
-        L.moe_route_sel.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.moe_route_sel.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_void_p]
+        L.moe_balance_stats.restype = c_int32
+        L.moe_balance_stats.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                        c_void_p]
+        L.moe_bias_update.restype = c_int32
+        L.moe_bias_update.argtypes = [P, c_void_p, c_float, c_void_p, c_void_p]
         L.moe_dispatch.restype = c_int32
         L.moe_dispatch.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_size_t, c_void_p]
@@ -155,15 +161,25 @@ def layer_params(cfg: MoeConfig):
     return t.value, a.value
 
 
-def route(cfg, x, w_router, router_bias, topk_idx, topk_w, stream=None, score_bias=None):
-    """moe_route, or moe_route_sel when a selection-only ``score_bias`` is given."""
-    if score_bias is None:
-        _check(lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(topk_idx),
-                               _ptr(topk_w), _stream(stream)), "moe_route")
-    else:
-        _check(lib().moe_route_sel(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(router_bias),
-                                   _ptr(score_bias), _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
-               "moe_route_sel")
+def route(cfg, x, w_router, router_bias, topk_idx, topk_w, stream=None):
+    _check(lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(topk_idx),
+                           _ptr(topk_w), _stream(stream)), "moe_route")
+
+
+def route_sel(cfg, x, w_router, router_bias, score_bias, topk_idx, topk_w, scores=None, stream=None):
+    _check(lib().moe_route_sel(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(score_bias),
+                               _ptr(topk_idx), _ptr(topk_w), _ptr(scores), _stream(stream)), "moe_route_sel")
+
+
+def balance_stats(cfg, counts, scores, score_mean, load_frac, balance, ws, stream=None):
+    _check(lib().moe_balance_stats(ctypes.byref(cfg), _ptr(counts), _ptr(scores), _ptr(score_mean),
+                                   _ptr(load_frac), _ptr(balance), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)), "moe_balance_stats")
+
+
+def bias_update(cfg, counts, gamma, score_bias, stream=None):
+    _check(lib().moe_bias_update(ctypes.byref(cfg), _ptr(counts), float(gamma), _ptr(score_bias),
+                                 _stream(stream)), "moe_bias_update")
 
 
 def dispatch(cfg, topk_idx, x, counts, offsets, row_of_slot, token_of_row, x_perm, ws, stream=None):
@@ -195,7 +211,7 @@ def route_out_struct(r) -> Optional[MoeRouteOut]:
         return None
     g = lambda n: _ptr(r.get(n))  # noqa: E731
     return MoeRouteOut(g("topk_idx"), g("topk_w"), g("counts"), g("offsets"), g("row_of_slot"),
-                       g("token_of_row"))
+                       g("token_of_row"), g("scores"))
 
 
 def forward(cfg, weights, x, y, ws, route_out=None, stream=None, events=None):

@@ -146,7 +146,8 @@ moe_status moe_layer_params(const moe_config* c, int64_t* total, int64_t* active
 }
 
 moe_status moe_route_sel(const moe_config* c, const void* x, const void* w_router, const float* router_bias,
-                         const float* score_bias, int32_t* topk_idx, float* topk_w, void* stream) {
+                         const float* score_bias, int32_t* topk_idx, float* topk_w, float* scores,
+                         void* stream) {
   MOE_TRY(moe_validate(c));
   MOE_TRY(need(x));
   MOE_TRY(need(w_router));
@@ -154,13 +155,39 @@ moe_status moe_route_sel(const moe_config* c, const void* x, const void* w_route
   MOE_TRY(need(topk_w));
   MOE_TRY(opt(router_bias));
   MOE_TRY(opt(score_bias));
-  HIP_TRY(launch_route(*c, x, w_router, router_bias, score_bias, topk_idx, topk_w, S(stream)));
+  MOE_TRY(opt(scores));
+  HIP_TRY(launch_route(*c, x, w_router, router_bias, route_sel_of(*c, score_bias, scores), topk_idx, topk_w,
+                       S(stream)));
   return MOE_OK;
 }
 
 moe_status moe_route(const moe_config* c, const void* x, const void* w_router, const float* router_bias,
                      int32_t* topk_idx, float* topk_w, void* stream) {
-  return moe_route_sel(c, x, w_router, router_bias, nullptr, topk_idx, topk_w, stream);
+  return moe_route_sel(c, x, w_router, router_bias, nullptr, topk_idx, topk_w, nullptr, stream);
+}
+
+moe_status moe_balance_stats(const moe_config* c, const int32_t* counts, const float* scores, float* score_mean,
+                             float* load_frac, float* balance, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(moe_validate(c));
+  MOE_TRY(need(counts));
+  MOE_TRY(need(scores));
+  MOE_TRY(opt(score_mean));
+  MOE_TRY(opt(load_frac));
+  MOE_TRY(opt(balance));
+  if (ws == nullptr || ws_bytes < stats_scratch_bytes(*c)) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  HIP_TRY(launch_balance_stats(*c, counts, scores, score_mean, load_frac, balance, ws, S(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_bias_update(const moe_config* c, const int32_t* counts, float gamma, float* score_bias,
+                           void* stream) {
+  MOE_TRY(moe_validate(c));
+  MOE_TRY(need(counts));
+  MOE_TRY(need(score_bias));
+  if (!isfinite(gamma)) return MOE_ERR_SHAPE;
+  HIP_TRY(launch_bias_update(*c, counts, gamma, score_bias, S(stream)));
+  return MOE_OK;
 }
 
 moe_status moe_dispatch(const moe_config* c, const int32_t* topk_idx, const void* x, int32_t* counts,
@@ -270,6 +297,7 @@ moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const vo
   MOE_TRY(need(r.offsets));
   MOE_TRY(need(r.row_of_slot));
   MOE_TRY(need(r.token_of_row));
+  MOE_TRY(opt(r.scores));
 
   hipStream_t s = S(stream);
   auto mark = [&](int i) -> hipError_t {
@@ -283,8 +311,8 @@ moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const vo
   int32_t* nch = reinterpret_cast<int32_t*>(at(ws, L.n_chunks));
 
   HIP_TRY(mark(0));
-  HIP_TRY(launch_route_split(*c, x, w->w_router, w->router_bias, w->score_bias, r.topk_idx, r.topk_w,
-                             at(ws, L.rscratch), s));
+  HIP_TRY(launch_route_split(*c, x, w->w_router, w->router_bias, route_sel_of(*c, w->score_bias, r.scores),
+                             r.topk_idx, r.topk_w, at(ws, L.rscratch), s));
   HIP_TRY(mark(1));
   HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), r.topk_idx, r.counts, r.offsets, r.row_of_slot,
                           r.token_of_row, at(ws, L.dscratch), chunks, nch, bm, sh, Tk, s));

@@ -54,16 +54,35 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // ---- launches (each returns hipGetLastError() of its launch) ----
 
-// Router GEMM + gate + top-k.  x, w: bf16 or fp32 per dtype.  sbias: the
-// selection-only bias (or NULL); grouping from c.n_group / c.topk_group.
-hipError_t launch_route(const moe_config& c, const void* x, const void* w, const float* bias,
-                        const float* sbias, int32_t* topk_idx, float* topk_w, hipStream_t s);
+// Selection options of the router kernels and their optional dense output.
+struct RouteSel {
+  const float* sbias;  // [E] selection-only expert bias, or NULL
+  int n_group;         // expert groups of the group limit (0: none)
+  int topk_group;      // groups kept per token
+  float* scores;       // [T, E] gate score of every expert, or NULL
+};
+inline RouteSel route_sel_of(const moe_config& c, const float* sbias, float* scores) {
+  return RouteSel{sbias, c.n_group, c.topk_group, scores};
+}
+
+// Router GEMM + gate + top-k.  x, w: bf16 or fp32 per dtype.
+hipError_t launch_route(const moe_config& c, const void* x, const void* w, const float* bias, const RouteSel& rs,
+                        int32_t* topk_idx, float* topk_w, hipStream_t s);
 
 // Split-K router (bf16): partial logits in `scratch` (route_scratch_bytes), then
 // a per-token reduce + gate + top-k.  fp32 configs fall back to launch_route.
 size_t route_scratch_bytes(const moe_config& c);
 hipError_t launch_route_split(const moe_config& c, const void* x, const void* w, const float* bias,
-                              const float* sbias, int32_t* topk_idx, float* topk_w, void* scratch, hipStream_t s);
+                              const RouteSel& rs, int32_t* topk_idx, float* topk_w, void* scratch, hipStream_t s);
+
+// Routing statistics: P_i (mean score), f_i (routed fraction) and E * sum f_i P_i
+// from counts [E] and scores [T, E]; `part` holds stats_scratch_bytes(c).
+size_t stats_scratch_bytes(const moe_config& c);
+hipError_t launch_balance_stats(const moe_config& c, const int32_t* counts, const float* scores, float* mean,
+                                float* frac, float* balance, void* part, hipStream_t s);
+// score_bias[e] += gamma * sign(mean load - counts[e]).
+hipError_t launch_bias_update(const moe_config& c, const int32_t* counts, float gamma, float* score_bias,
+                              hipStream_t s);
 
 // Dispatch scratch sizes (bytes) for T*k assignments and E experts.
 size_t dispatch_scratch_bytes(int64_t Tk, int64_t E);

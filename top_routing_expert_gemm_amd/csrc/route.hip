@@ -52,6 +52,29 @@ struct SelOpts {
   float* wbuf;         // this wave's LDS scratch of E floats (used when n_group > 0)
 };
 
+// Gate score of every expert of one token (one wave), the same arithmetic as
+// the selection below: softmax over the E logits, or a sigmoid per logit.
+template <int VPL>
+__device__ void write_scores(const float (&z)[VPL], int E, int gate, float* out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float m = -INFINITY, den = 0.f;
+  if (gate == MOE_GATE_SOFTMAX) {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (lane + kWave * v < E) m = fmaxf(m, z[v]);
+    m = wave_max(m);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (lane + kWave * v < E) den += expf(z[v] - m);
+    den = wave_sum(den);
+  }
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = lane + kWave * v;
+    if (e < E) out[e] = gate == MOE_GATE_SOFTMAX ? expf(z[v] - m) / den : 1.f / (1.f + expf(-z[v]));
+  }
+}
+
 // Gate + top-k of one token, run by one whole wave.  z[v] holds the logit of
 // expert lane + 64 v (-inf past E).
 //  * Plain selection: both gates are increasing functions of z, so the k best
@@ -64,8 +87,9 @@ struct SelOpts {
 // Ties go to the lower expert (or group) index.  Lanes j < k write pick j.
 template <int VPL>
 __device__ void topk_token(float (&z)[VPL], int E, int k, int gate, int renorm, float scale, const SelOpts& o,
-                           int32_t* out_idx, float* out_w) {
+                           float* out_scores, int32_t* out_idx, float* out_w) {
   const int lane = threadIdx.x & (kWave - 1);
+  if (out_scores != nullptr) write_scores<VPL>(z, E, gate, out_scores);
   const bool plain = o.sbias == nullptr && o.n_group == 0;
   bool taken[VPL];
 #pragma unroll
@@ -307,8 +331,8 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x, cons
 template <int NBW>
 __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, const float* __restrict__ bias,
-    int T, int H, int E, int k, int gate, int renorm, float scale, const float* __restrict__ sbias, int n_group,
-    int topk_group, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    int T, int H, int E, int k, int gate, int renorm, float scale, RouteSel rs, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
   constexpr int VPL = 2 * NBW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);                 // [2][32][64] bf16
@@ -340,7 +364,7 @@ __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(
   }
   __syncthreads();
 
-  const SelOpts o{sbias, n_group, topk_group, wscr + wave * nblk * 32};
+  const SelOpts o{rs.sbias, rs.n_group, rs.topk_group, wscr + wave * nblk * 32};
   for (int row = wave; row < kRBM; row += 4) {
     const int t = t0 + row;
     if (t >= T) break;
@@ -350,7 +374,7 @@ __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(
       const int e = lane + kWave * v;
       z[v] = e < E ? lg[row * lde + e] : -INFINITY;
     }
-    topk_token<VPL>(z, E, k, gate, renorm, scale, o, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
+    topk_token<VPL>(z, E, k, gate, renorm, scale, o, rs.scores ? rs.scores + (int64_t)t * E : nullptr, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
   }
 }
 
@@ -394,8 +418,7 @@ template <int VPL>
 __global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __restrict__ part, int nsplit, int T,
                                                                int E, const float* __restrict__ bias, int k,
                                                                int gate, int renorm, float scale,
-                                                               const float* __restrict__ sbias, int n_group,
-                                                               int topk_group, int32_t* __restrict__ topk_idx,
+                                                               RouteSel rs, int32_t* __restrict__ topk_idx,
                                                                float* __restrict__ topk_w) {
   __shared__ float wscr[kRThreads / kWave][kMaxE];
   const int lane = threadIdx.x & 63;
@@ -425,8 +448,8 @@ __global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __re
       z[v] = -INFINITY;
     }
   }
-  const SelOpts o{sbias, n_group, topk_group, wscr[threadIdx.x >> 6]};
-  topk_token<VPL>(z, E, k, gate, renorm, scale, o, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
+  const SelOpts o{rs.sbias, rs.n_group, rs.topk_group, wscr[threadIdx.x >> 6]};
+  topk_token<VPL>(z, E, k, gate, renorm, scale, o, rs.scores ? rs.scores + (int64_t)t * E : nullptr, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
 }
 
 // fp32 path: one wave per token computes its E logits with lane-strided dot
@@ -434,8 +457,8 @@ __global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __re
 template <int VPL>
 __global__ __launch_bounds__(kRThreads) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias, int T,
-    int H, int E, int k, int gate, int renorm, float scale, const float* __restrict__ sbias, int n_group,
-    int topk_group, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    int H, int E, int k, int gate, int renorm, float scale, RouteSel rs, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
   __shared__ float wscr[kRThreads / kWave][kMaxE];
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kRThreads / kWave) + (threadIdx.x >> 6);
@@ -462,13 +485,13 @@ __global__ __launch_bounds__(kRThreads) void route_f32_kernel(
       if (lane == el) z[v] = s;
     }
   }
-  const SelOpts o{sbias, n_group, topk_group, wscr[threadIdx.x >> 6]};
-  topk_token<VPL>(z, E, k, gate, renorm, scale, o, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
+  const SelOpts o{rs.sbias, rs.n_group, rs.topk_group, wscr[threadIdx.x >> 6]};
+  topk_token<VPL>(z, E, k, gate, renorm, scale, o, rs.scores ? rs.scores + (int64_t)t * E : nullptr, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
 }
 
 template <int NBW>
 hipError_t launch_route_bf16(const moe_config& c, const void* x, const void* w, const float* bias,
-                             const float* sbias, int32_t* idx, float* tw, hipStream_t s) {
+                             const RouteSel& rs, int32_t* idx, float* tw, hipStream_t s) {
   const int nblk = (int)((c.E + 31) / 32);
   const size_t lds = 2 * kRBM * kRBK * 2 + (size_t)kRBM * (nblk * 32 + 4) * 4 + (size_t)4 * nblk * 32 * 4;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_bf16_kernel<NBW>),
@@ -477,20 +500,18 @@ hipError_t launch_route_bf16(const moe_config& c, const void* x, const void* w, 
   const int grid = (int)((c.T + kRBM - 1) / kRBM);
   hipLaunchKernelGGL(route_bf16_kernel<NBW>, dim3(grid), dim3(kRThreads), lds, s,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), bias, (int)c.T,
-                     (int)c.H, (int)c.E, (int)c.k, c.gate, c.renormalize, c.routed_scaling_factor, sbias, c.n_group,
-                     c.topk_group, idx, tw);
+                     (int)c.H, (int)c.E, (int)c.k, c.gate, c.renormalize, c.routed_scaling_factor, rs, idx, tw);
   return hipGetLastError();
 }
 
 template <int VPL>
 hipError_t launch_route_f32(const moe_config& c, const void* x, const void* w, const float* bias,
-                            const float* sbias, int32_t* idx, float* tw, hipStream_t s) {
+                            const RouteSel& rs, int32_t* idx, float* tw, hipStream_t s) {
   const int per = kRThreads / kWave;
   const int grid = (int)((c.T + per - 1) / per);
   hipLaunchKernelGGL(route_f32_kernel<VPL>, dim3(grid), dim3(kRThreads), 0, s,
                      static_cast<const float*>(x), static_cast<const float*>(w), bias, (int)c.T,
-                     (int)c.H, (int)c.E, (int)c.k, c.gate, c.renormalize, c.routed_scaling_factor, sbias, c.n_group,
-                     c.topk_group, idx, tw);
+                     (int)c.H, (int)c.E, (int)c.k, c.gate, c.renormalize, c.routed_scaling_factor, rs, idx, tw);
   return hipGetLastError();
 }
 
@@ -510,7 +531,7 @@ inline int route_nsplit(int64_t T, int64_t H, int64_t E) {
 
 template <int NBW, int RBT>
 hipError_t launch_route_split_t(const moe_config& c, const void* x, const void* w, const float* bias,
-                                const float* sbias, int32_t* idx, float* tw, float* part, hipStream_t s) {
+                                const RouteSel& rs, int32_t* idx, float* tw, float* part, hipStream_t s) {
   const int nsplit = route_nsplit(c.T, c.H, c.E);
   const int nk = (int)(c.H / kRBK);
   const int per = (nk + nsplit - 1) / nsplit;
@@ -524,16 +545,16 @@ hipError_t launch_route_split_t(const moe_config& c, const void* x, const void* 
   const int tpb = kRThreads / kWave;
   hipLaunchKernelGGL(route_topk_kernel<2 * NBW>, dim3((unsigned)((c.T + tpb - 1) / tpb)), dim3(kRThreads), 0, s,
                      part, nsplit_eff, (int)c.T, (int)c.E, bias, (int)c.k, c.gate, c.renormalize,
-                     c.routed_scaling_factor, sbias, c.n_group, c.topk_group, idx, tw);
+                     c.routed_scaling_factor, rs, idx, tw);
   return hipGetLastError();
 }
 
 template <int NBW>
 hipError_t launch_route_split_n(const moe_config& c, const void* x, const void* w, const float* bias,
-                                const float* sbias, int32_t* idx, float* tw, float* part, hipStream_t s) {
+                                const RouteSel& rs, int32_t* idx, float* tw, float* part, hipStream_t s) {
   if constexpr (NBW <= 4)
-    if (route_rbt(c.T, c.E) == 2) return launch_route_split_t<NBW, 2>(c, x, w, bias, sbias, idx, tw, part, s);
-  return launch_route_split_t<NBW, 1>(c, x, w, bias, sbias, idx, tw, part, s);
+    if (route_rbt(c.T, c.E) == 2) return launch_route_split_t<NBW, 2>(c, x, w, bias, rs, idx, tw, part, s);
+  return launch_route_split_t<NBW, 1>(c, x, w, bias, rs, idx, tw, part, s);
 }
 
 }  // namespace
@@ -545,26 +566,27 @@ size_t route_scratch_bytes(const moe_config& c) {
 }
 
 hipError_t launch_route_split(const moe_config& c, const void* x, const void* w, const float* bias,
-                              const float* sbias, int32_t* topk_idx, float* topk_w, void* scratch, hipStream_t s) {
-  if (c.dtype != MOE_BF16) return launch_route(c, x, w, bias, sbias, topk_idx, topk_w, s);
+                              const RouteSel& rs, int32_t* topk_idx, float* topk_w, void* scratch,
+                              hipStream_t s) {
+  if (c.dtype != MOE_BF16) return launch_route(c, x, w, bias, rs, topk_idx, topk_w, s);
   float* part = static_cast<float*>(scratch);
-  if (c.E <= 128) return launch_route_split_n<1>(c, x, w, bias, sbias, topk_idx, topk_w, part, s);
-  if (c.E <= 256) return launch_route_split_n<2>(c, x, w, bias, sbias, topk_idx, topk_w, part, s);
-  if (c.E <= 512) return launch_route_split_n<4>(c, x, w, bias, sbias, topk_idx, topk_w, part, s);
-  return launch_route_split_n<8>(c, x, w, bias, sbias, topk_idx, topk_w, part, s);
+  if (c.E <= 128) return launch_route_split_n<1>(c, x, w, bias, rs, topk_idx, topk_w, part, s);
+  if (c.E <= 256) return launch_route_split_n<2>(c, x, w, bias, rs, topk_idx, topk_w, part, s);
+  if (c.E <= 512) return launch_route_split_n<4>(c, x, w, bias, rs, topk_idx, topk_w, part, s);
+  return launch_route_split_n<8>(c, x, w, bias, rs, topk_idx, topk_w, part, s);
 }
 
-hipError_t launch_route(const moe_config& c, const void* x, const void* w, const float* bias, const float* sbias,
+hipError_t launch_route(const moe_config& c, const void* x, const void* w, const float* bias, const RouteSel& rs,
                         int32_t* topk_idx, float* topk_w, hipStream_t s) {
   if (c.dtype == MOE_BF16) {
-    if (c.E <= 128) return launch_route_bf16<1>(c, x, w, bias, sbias, topk_idx, topk_w, s);
-    if (c.E <= 256) return launch_route_bf16<2>(c, x, w, bias, sbias, topk_idx, topk_w, s);
-    if (c.E <= 512) return launch_route_bf16<4>(c, x, w, bias, sbias, topk_idx, topk_w, s);
-    return launch_route_bf16<8>(c, x, w, bias, sbias, topk_idx, topk_w, s);
+    if (c.E <= 128) return launch_route_bf16<1>(c, x, w, bias, rs, topk_idx, topk_w, s);
+    if (c.E <= 256) return launch_route_bf16<2>(c, x, w, bias, rs, topk_idx, topk_w, s);
+    if (c.E <= 512) return launch_route_bf16<4>(c, x, w, bias, rs, topk_idx, topk_w, s);
+    return launch_route_bf16<8>(c, x, w, bias, rs, topk_idx, topk_w, s);
   }
-  if (c.E <= 64) return launch_route_f32<1>(c, x, w, bias, sbias, topk_idx, topk_w, s);
-  if (c.E <= 256) return launch_route_f32<4>(c, x, w, bias, sbias, topk_idx, topk_w, s);
-  return launch_route_f32<16>(c, x, w, bias, sbias, topk_idx, topk_w, s);
+  if (c.E <= 64) return launch_route_f32<1>(c, x, w, bias, rs, topk_idx, topk_w, s);
+  if (c.E <= 256) return launch_route_f32<4>(c, x, w, bias, rs, topk_idx, topk_w, s);
+  return launch_route_f32<16>(c, x, w, bias, rs, topk_idx, topk_w, s);
 }
 
 }  // namespace moe
