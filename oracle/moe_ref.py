@@ -51,7 +51,8 @@ __all__ = [
     "select_topk", "topk_weights", "route", "expert_capacity", "dispatch",
     "gather_rows", "silu", "swiglu_ffn", "grouped_expert_ffn", "combine",
     "moe_forward", "moe_layer_params", "expected_touched_experts", "select_topk_grouped",
-    "route_grouped", "aux_loss_terms", "bias_update",
+    "route_grouped", "aux_loss_terms", "bias_update", "expert_choice_capacity",
+    "select_expert_choice", "moe_forward_ec",
 ]
 
 GATE_SOFTMAX = 0
@@ -376,6 +377,76 @@ def moe_forward(x, w_router, router_bias, w_gate, w_up, w_down, *, k: int, gate:
     if shared is not None:
         y += swiglu_ffn(xw[tok], *shared)
     return y, r
+
+
+# ------------------------------------------------------ expert-choice routing ---
+
+def expert_choice_capacity(T: int, k: int, E: int, capacity_factor: float) -> int:
+    """Tokens each expert takes under expert-choice routing.
+
+    [Hardest] (the two routing schools) fixes only that every expert takes a
+    fixed number of tokens.  Reading: the token-choice capacity with the same
+    T*k budget, C = ceil(cf * T * k / E) with cf = 1 when no factor is given,
+    and at most T (an expert cannot take a token twice).
+    """
+    cf = float(capacity_factor) if capacity_factor is not None and capacity_factor > 0 else 1.0
+    return int(min(T, math.ceil(cf * T * k / E)))
+
+
+def select_expert_choice(scores: np.ndarray, C: int):
+    """Expert-choice selection ([Hardest], the two routing schools): every expert
+    takes the C tokens with the highest score for it (equal scores -> lower token
+    index), so every expert gets exactly C tokens and a token may get none.
+
+    Returns (chosen [E, C] token ids in ascending token order per expert,
+    gap [E] = C-th minus (C+1)-th best score of the expert, inf when C = T).
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    T, E = scores.shape
+    if not 1 <= C <= T:
+        raise ValueError("need 1 <= C <= T")
+    order = np.argsort(-scores, axis=0, kind="stable")   # per expert column: best token first
+    chosen = np.sort(order[:C], axis=0).T
+    ranked = np.take_along_axis(scores, order, axis=0)
+    gap = ranked[C - 1] - ranked[C] if C < T else np.full(E, np.inf)
+    return chosen, gap
+
+
+def moe_forward_ec(x, w_router, router_bias, w_gate, w_up, w_down, *, gate: int,
+                   routed_scaling_factor: float = 1.0, C: int, shared=None,
+                   tokens: Optional[np.ndarray] = None):
+    """The layer under expert-choice routing.
+
+    Router and gate as in token choice; expert e runs on the C tokens it chose
+    and token t's output is the sum over the experts that chose it of
+    score[t, e] * routed_scaling_factor * expert_e(x_t), plus the shared expert.
+    Readings: the combine weight of a chosen pair is its gate score (no
+    renormalisation: a token may have any number of experts, or none); a token
+    no expert chose passes through with the shared output only (0 without one).
+    ``w_gate`` etc. as in moe_forward.  Returns (y [len(tokens), H], routing dict
+    with scores, chosen [E, C], gap [E], token_of_row [E*C]).
+    """
+    T, H = np.asarray(x).shape
+    E = np.asarray(w_router).shape[0]
+    z = router_logits(x, w_router, router_bias)
+    s = gate_scores(z, gate)
+    chosen, gap = select_expert_choice(s, C)
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    pos = {int(t): i for i, t in enumerate(tok)}
+    y = np.zeros((len(tok), H))
+    xw = np.asarray(x)
+    for e in range(E):
+        sel = np.array([t for t in chosen[e] if int(t) in pos], dtype=np.int64)
+        if len(sel) == 0:
+            continue
+        wg, wu, wd = _expert(w_gate, w_up, w_down, e)
+        o = swiglu_ffn(xw[sel], wg, wu, wd)
+        for n, t in enumerate(sel):
+            y[pos[int(t)]] += s[t, e] * float(routed_scaling_factor) * o[n]
+    if shared is not None:
+        y += swiglu_ffn(xw[tok], *shared)
+    return y, {"logits": z, "scores": s, "chosen": chosen, "gap": gap,
+               "token_of_row": chosen.reshape(-1)}
 
 
 # -------------------------------------------------------- routing statistics ---
