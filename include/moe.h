@@ -228,6 +228,44 @@ moe_status moe_forward_timed(const moe_config *cfg, const moe_weights *w, const 
                              void *y, moe_route_out *route_out, void *ws, size_t ws_bytes,
                              void *stream, void *const *events);
 
+/* ---- expert-choice routing ([Hardest], the two routing schools: each expert
+ * takes a fixed number of the tokens it wants most; the load is balanced by
+ * construction and a token may get no expert) ---- */
+
+/* Optional outputs of moe_forward_ec (each may be NULL: kept in the workspace). */
+typedef struct {
+  float *scores;         /* [T, E] gate score of every expert for every token */
+  int32_t *token_of_row; /* [E * C] chosen tokens, expert-contiguous, ascending token id */
+  int32_t *row_of_pair;  /* [T, E] row e*C + j of the pair (t, e), or -1 when e did not take t */
+} moe_ec_out;
+
+/* Host only: tokens per expert C = min(T, ceil(cf * T * k / E)) in double, with
+ * cf = capacity_factor, read as 1.0 when <= 0 (the token-choice budget of T*k
+ * assignments spread evenly); -1 when cfg is invalid. */
+int64_t moe_ec_capacity(const moe_config *cfg);
+
+/* Host only: bytes of device workspace that moe_forward_ec needs. */
+moe_status moe_ec_workspace_size(const moe_config *cfg, size_t *bytes);
+
+/* Per-expert top-C selection from scores [T, E] (float32): expert e takes the
+ * C = moe_ec_capacity(cfg) tokens with the highest scores[t, e], equal scores
+ * going to the lower token id (selection exact on the float32 values).  Writes
+ * token_of_row [E*C] (expert e's tokens at e*C.., ascending token id) and
+ * row_of_pair [T, E] (the row of each chosen pair, -1 elsewhere). */
+moe_status moe_route_ec(const moe_config *cfg, const float *scores, int32_t *token_of_row,
+                        int32_t *row_of_pair, void *stream);
+
+/* The layer under expert choice: router and gate (cfg->gate; score_bias and
+ * expert groups do not apply), per-expert top-C, grouped SwiGLU experts over
+ * the E*C chosen rows (the shared expert as one more group over all T tokens),
+ * then y[t] = sum over the experts e that took t, in expert order, of
+ * scores[t,e] * routed_scaling_factor * expert_e(x_t), accumulated in float32,
+ * plus the shared output.  No renormalisation: a token's weights are its raw
+ * scores; a token no expert took gets the shared output only (0 without one).
+ * ws: at least moe_ec_workspace_size() bytes; eo may be NULL. */
+moe_status moe_forward_ec(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
+                          moe_ec_out *eo, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

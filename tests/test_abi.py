@@ -123,3 +123,22 @@ def test_launch_entry_points_reject_before_launch():
     assert L.moe_dispatch(p(good), 16, 16, 16, 16, 16, 16, None, None, 0, None) == 4   # no workspace
     assert L.moe_expert_ffn(p(good), 16, 16, 16, 16, 16, 16, 16, 8, None) == 4       # workspace too small
     assert L.moe_forward(p(good), None, 16, 16, None, 16, 1 << 30, None) == 1       # no weights
+
+
+def test_expert_choice_host_calls():
+    """Expert-choice capacity and workspace on the host; invalid calls launch nothing."""
+    ds = moe.make_config(8192, 7168, 2048, 256, 8, moe.GATE_SIGMOID, True, 2.5, 0.0, 1, 2048)
+    assert moe.ec_capacity(ds) == 256
+    assert moe.ec_capacity(moe.make_config(8192, 7168, 2048, 256, 8, capacity_factor=1.25)) == 320
+    assert moe.ec_capacity(moe.make_config(10, 64, 64, 4, 1)) == 3
+    assert moe.ec_capacity(moe.make_config(4, 64, 64, 1, 1, capacity_factor=4.0)) == 4     # at most T
+    assert moe.ec_capacity(moe.make_config(8, 64, 64, 4, 5)) == -1
+    ws = moe.ec_workspace_size(ds)
+    rows = 256 * 256 + 8192
+    assert rows * (2048 + 7168) * 2 <= ws < rows * (2048 + 7168) * 2 * 1.1
+    L = moe.lib()
+    p = ctypes.byref
+    good = moe.make_config(8, 64, 64, 4, 2)
+    assert L.moe_route_ec(p(good), None, 16, 16, None) == 1
+    assert L.moe_route_ec(p(good), 16, 16, 8, None) == 6
+    assert L.moe_forward_ec(p(good), None, 16, 16, None, 16, 1 << 30, None) == 1

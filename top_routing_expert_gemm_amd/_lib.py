@@ -23,7 +23,8 @@ STAGE_EVENTS = 6
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_capacity", "moe_layer_params",
            "moe_route", "moe_route_sel", "moe_balance_stats", "moe_bias_update", "moe_dispatch",
-           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_timed")
+           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_timed", "moe_ec_capacity",
+           "moe_ec_workspace_size", "moe_route_ec", "moe_forward_ec")
 
 
 class MoeConfig(ctypes.Structure):
@@ -42,6 +43,10 @@ class MoeWeights(ctypes.Structure):
 class MoeRouteOut(ctypes.Structure):
     _fields_ = [("topk_idx", c_void_p), ("topk_w", c_void_p), ("counts", c_void_p), ("offsets", c_void_p),
                 ("row_of_slot", c_void_p), ("token_of_row", c_void_p), ("scores", c_void_p)]
+
+
+class MoeEcOut(ctypes.Structure):
+    _fields_ = [("scores", c_void_p), ("token_of_row", c_void_p), ("row_of_pair", c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -96,6 +101,15 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_timed.restype = c_int32
         L.moe_forward_timed.argtypes = [P, POINTER(MoeWeights), c_void_p, c_void_p, POINTER(MoeRouteOut),
                                         c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]
+        L.moe_ec_capacity.restype = c_int64
+        L.moe_ec_capacity.argtypes = [P]
+        L.moe_ec_workspace_size.restype = c_int32
+        L.moe_ec_workspace_size.argtypes = [P, POINTER(c_size_t)]
+        L.moe_route_ec.restype = c_int32
+        L.moe_route_ec.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.moe_forward_ec.restype = c_int32
+        L.moe_forward_ec.argtypes = [P, POINTER(MoeWeights), c_void_p, c_void_p, POINTER(MoeEcOut), c_void_p,
+                                     c_size_t, c_void_p]
         _lib = L
     return _lib
 
@@ -229,3 +243,31 @@ def forward(cfg, weights, x, y, ws, route_out=None, stream=None, events=None):
     st = lib().moe_forward_timed(ctypes.byref(cfg), ctypes.byref(W), _ptr(x), _ptr(y), rp, _ptr(ws), nbytes,
                                  _stream(stream), arr)
     _check(st, "moe_forward_timed")
+
+
+# ---- expert choice ----
+
+def ec_capacity(cfg: MoeConfig) -> int:
+    return lib().moe_ec_capacity(ctypes.byref(cfg))
+
+
+def ec_workspace_size(cfg: MoeConfig) -> int:
+    n = c_size_t(0)
+    _check(lib().moe_ec_workspace_size(ctypes.byref(cfg), ctypes.byref(n)), "moe_ec_workspace_size")
+    return n.value
+
+
+def route_ec(cfg, scores, token_of_row, row_of_pair, stream=None):
+    _check(lib().moe_route_ec(ctypes.byref(cfg), _ptr(scores), _ptr(token_of_row), _ptr(row_of_pair),
+                              _stream(stream)), "moe_route_ec")
+
+
+def forward_ec(cfg, weights, x, y, ws, ec_out=None, stream=None):
+    """moe_forward_ec; ``ec_out`` is None or a dict with scores / token_of_row / row_of_pair tensors."""
+    W = weights if isinstance(weights, MoeWeights) else weights_struct(weights)
+    O = None
+    if ec_out is not None:
+        O = MoeEcOut(_ptr(ec_out.get("scores")), _ptr(ec_out.get("token_of_row")), _ptr(ec_out.get("row_of_pair")))
+    _check(lib().moe_forward_ec(ctypes.byref(cfg), ctypes.byref(W), _ptr(x), _ptr(y),
+                                ctypes.byref(O) if O is not None else None, _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)), "moe_forward_ec")

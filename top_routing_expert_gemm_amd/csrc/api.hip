@@ -49,6 +49,46 @@ Layout layout(const moe_config* c) {
   return L;
 }
 
+// Expert choice: C tokens per expert (capacity_factor <= 0 reads as 1), at most T.
+int64_t ec_cap_of(const moe_config* c) {
+  const double cf = c->capacity_factor > 0.f ? (double)c->capacity_factor : 1.0;
+  const double v = ceil(cf * (double)c->T * (double)c->k / (double)c->E);
+  return std::min<int64_t>(c->T, (int64_t)v);
+}
+
+// Device workspace of moe_forward_ec.
+struct LayoutEC {
+  size_t topk_idx, topk_w, scores, rscratch, token_of_row, row_of_pair, chunks, n_chunks, h, y_perm, total;
+  int64_t C, rows, max_chunks;
+};
+
+LayoutEC layout_ec(const moe_config* c) {
+  LayoutEC L;
+  L.C = ec_cap_of(c);
+  const int64_t R = c->E * L.C;
+  const int64_t sh = c->n_shared ? c->T : 0;
+  L.rows = R + sh;
+  L.max_chunks = max_chunks(R, c->E, sh, gemm_bm(*c));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L.topk_idx = take((size_t)c->T * c->k * 4);   // the router's own top-k, unused here
+  L.topk_w = take((size_t)c->T * c->k * 4);
+  L.scores = take((size_t)c->T * c->E * 4);
+  L.rscratch = take(route_scratch_bytes(*c));
+  L.token_of_row = take((size_t)R * 4);
+  L.row_of_pair = take((size_t)c->T * c->E * 4);
+  L.chunks = take((size_t)L.max_chunks * sizeof(Chunk));
+  L.n_chunks = take(4);
+  L.h = take((size_t)L.rows * c->I * esize(c));
+  L.y_perm = take((size_t)L.rows * c->H * esize(c));
+  L.total = off;
+  return L;
+}
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 template <typename P>
@@ -355,6 +395,111 @@ moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const vo
 moe_status moe_forward(const moe_config* c, const moe_weights* w, const void* x, void* y, moe_route_out* ro,
                        void* ws, size_t ws_bytes, void* stream) {
   return moe_forward_timed(c, w, x, y, ro, ws, ws_bytes, stream, nullptr);
+}
+
+// ---- expert choice ----
+
+static moe_status validate_ec(const moe_config* c) {
+  MOE_TRY(moe_validate(c));
+  const int64_t C = ec_cap_of(c);
+  if (c->E * C + c->T >= (int64_t(1) << 31) || c->T * c->E >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int64_t moe_ec_capacity(const moe_config* c) {
+  if (validate_ec(c) != MOE_OK) return -1;
+  return ec_cap_of(c);
+}
+
+moe_status moe_ec_workspace_size(const moe_config* c, size_t* bytes) {
+  MOE_TRY(validate_ec(c));
+  if (bytes == nullptr) return MOE_ERR_NULL;
+  *bytes = layout_ec(c).total;
+  return MOE_OK;
+}
+
+moe_status moe_route_ec(const moe_config* c, const float* scores, int32_t* token_of_row, int32_t* row_of_pair,
+                        void* stream) {
+  MOE_TRY(validate_ec(c));
+  MOE_TRY(need(scores));
+  MOE_TRY(need(token_of_row));
+  MOE_TRY(need(row_of_pair));
+  HIP_TRY(launch_ec_select(scores, c->T, c->E, ec_cap_of(c), token_of_row, row_of_pair, S(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void* x, void* y, moe_ec_out* eo,
+                          void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate_ec(c));
+  if (w == nullptr) return MOE_ERR_NULL;
+  MOE_TRY(need(x));
+  MOE_TRY(need(y));
+  MOE_TRY(need(w->w_router));
+  MOE_TRY(opt(w->router_bias));
+  MOE_TRY(need(w->w_gate));
+  MOE_TRY(need(w->w_up));
+  MOE_TRY(need(w->w_down));
+  if (c->n_shared) {
+    MOE_TRY(need(w->ws_gate));
+    MOE_TRY(need(w->ws_up));
+    MOE_TRY(need(w->ws_down));
+  }
+  const LayoutEC L = layout_ec(c);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  moe_ec_out o{};
+  if (eo != nullptr) o = *eo;
+  if (o.scores == nullptr) o.scores = reinterpret_cast<float*>(at(ws, L.scores));
+  if (o.token_of_row == nullptr) o.token_of_row = reinterpret_cast<int32_t*>(at(ws, L.token_of_row));
+  if (o.row_of_pair == nullptr) o.row_of_pair = reinterpret_cast<int32_t*>(at(ws, L.row_of_pair));
+  MOE_TRY(need(o.scores));
+  MOE_TRY(need(o.token_of_row));
+  MOE_TRY(need(o.row_of_pair));
+
+  hipStream_t s = S(stream);
+  const int bm = gemm_bm(*c);
+  const int64_t R = c->E * L.C;
+  const int64_t sh = c->n_shared ? c->T : 0;
+  Chunk* chunks = reinterpret_cast<Chunk*>(at(ws, L.chunks));
+  int32_t* nch = reinterpret_cast<int32_t*>(at(ws, L.n_chunks));
+  // router + gate (its top-k output is not used), then the per-expert top-C
+  HIP_TRY(launch_route_split(*c, x, w->w_router, w->router_bias, RouteSel{nullptr, 0, 0, o.scores},
+                             reinterpret_cast<int32_t*>(at(ws, L.topk_idx)), reinterpret_cast<float*>(at(ws, L.topk_w)),
+                             at(ws, L.rscratch), s));
+  HIP_TRY(launch_ec_select(o.scores, c->T, c->E, L.C, o.token_of_row, o.row_of_pair, s));
+  HIP_TRY(launch_chunks_uniform(c->E, L.C, sh, R, chunks, nch, bm, s));
+  GemmArgs g{};
+  g.A = x;
+  g.gather = o.token_of_row;
+  g.shared_row0 = R;
+  g.chunks = chunks;
+  g.n_chunks = nch;
+  g.max_chunks = L.max_chunks;
+  g.bm = bm;
+  g.w0 = w->w_gate;
+  g.w1 = w->w_up;
+  g.ws0 = w->ws_gate;
+  g.ws1 = w->ws_up;
+  g.E = c->E;
+  g.K = c->H;
+  g.N = c->I;
+  g.out = at(ws, L.h);
+  HIP_TRY(launch_gateup(g, c->dtype, s));
+  g.A = at(ws, L.h);
+  g.gather = nullptr;
+  g.w0 = w->w_down;
+  g.w1 = nullptr;
+  g.ws0 = w->ws_down;
+  g.ws1 = nullptr;
+  g.K = c->I;
+  g.N = c->H;
+  g.out = at(ws, L.y_perm);
+  HIP_TRY(launch_down(g, c->dtype, s));
+  const void* ysh = c->n_shared ? static_cast<const void*>(at(ws, L.y_perm + (size_t)R * c->H * esize(c))) : nullptr;
+  // weight of a chosen pair: its gate score times routed_scaling_factor
+  HIP_TRY(launch_combine(at(ws, L.y_perm), o.row_of_pair, o.scores, ysh, y, c->T, c->H, c->E, c->dtype, s,
+                         c->routed_scaling_factor));
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -6,10 +6,10 @@
 // "细粒度专家与共享专家" (the shared expert's output is added directly) and
 // section "负载不均：路由坍缩与丢 token" (a dropped token skips the expert).
 //
-// One workgroup per token (grid-stride): the k (row, weight) pairs of the token
-// are read once, then every thread accumulates 16-byte column vectors of the
-// selected y_perm rows in float32 in slot order j = 0..k-1, adds the shared row,
-// and stores.  A gather, not a scatter: no atomics, so the result is bitwise
+// One workgroup per token (grid-stride): the kept (row, weight) pairs of the
+// token are read once and compacted in slot order, then every thread
+// accumulates 16-byte column vectors of those y_perm rows in float32 in slot
+// order j = 0..k-1, adds the shared row, and stores.  A gather, not a scatter: no atomics, so the result is bitwise
 // reproducible.  HBM bound: reads (kept slots + shared) rows, writes one row.
 #include "common.h"
 
@@ -25,29 +25,60 @@ __device__ __forceinline__ void acc_bf16x8(float (&acc)[8], const uint4& v, floa
   }
 }
 
+// The token's kept (row, weight) pairs, in slot order, into LDS: slots are read
+// 256 at a time and compacted with wave ballots, so a token with k slots of
+// which few are kept (expert choice: k = E) costs only its kept rows later.
+// Returns the number of kept pairs; weights are multiplied by `scale`.
+__device__ __forceinline__ int load_pairs(const int32_t* __restrict__ ros, const float* __restrict__ tw, int64_t t,
+                                          int k, float scale, int* s_row, float* s_w, int* s_cnt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int n = 0;
+  for (int j0 = 0; j0 < k; j0 += 256) {
+    const int j = j0 + threadIdx.x;
+    int row = -1;
+    float w = 0.f;
+    if (j < k) {
+      row = ros[t * k + j];
+      if (row >= 0) w = tw[t * k + j];
+    }
+    const uint64_t b = __ballot(row >= 0);
+    if (lane == 0) s_cnt[wave] = __popcll(b);
+    __syncthreads();
+    int off = n, tot = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < wave) off += s_cnt[q];
+      tot += s_cnt[q];
+    }
+    if (row >= 0) {
+      const int at = off + __popcll(b & ((1ull << lane) - 1ull));
+      s_row[at] = row;
+      s_w[at] = w * scale;
+    }
+    n += tot;
+    __syncthreads();
+  }
+  return n;
+}
+
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __restrict__ yp,
                                                            const int32_t* __restrict__ ros,
                                                            const float* __restrict__ tw,
                                                            const uint16_t* __restrict__ ysh,
-                                                           uint16_t* __restrict__ y, int64_t T, int64_t H, int k) {
-  __shared__ int s_row[kMaxK];
-  __shared__ float s_w[kMaxK];
+                                                           uint16_t* __restrict__ y, int64_t T, int64_t H, int k,
+                                                           float scale) {
+  __shared__ int s_row[kMaxE];
+  __shared__ float s_w[kMaxE];
+  __shared__ int s_cnt[4];
   const int64_t hv = H / 8;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
-    if (threadIdx.x < k) {
-      s_row[threadIdx.x] = ros[t * k + threadIdx.x];
-      s_w[threadIdx.x] = tw[t * k + threadIdx.x];
-    }
-    __syncthreads();
+    const int n = load_pairs(ros, tw, t, k, scale, s_row, s_w, s_cnt);
     for (int64_t c = threadIdx.x; c < hv; c += blockDim.x) {
       float acc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int row = s_row[j];
-        if (row < 0) continue;  // dropped slot: contributes exactly 0
-        acc_bf16x8(acc, reinterpret_cast<const uint4*>(yp + (int64_t)row * H)[c], s_w[j]);
-      }
+      for (int j = 0; j < n; ++j)
+        acc_bf16x8(acc, reinterpret_cast<const uint4*>(yp + (int64_t)s_row[j] * H)[c], s_w[j]);
       if (ysh != nullptr) acc_bf16x8(acc, reinterpret_cast<const uint4*>(ysh + t * H)[c], 1.f);
       uint4 o;
       o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
@@ -64,22 +95,17 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
                                                           const int32_t* __restrict__ ros,
                                                           const float* __restrict__ tw,
                                                           const float* __restrict__ ysh, float* __restrict__ y,
-                                                          int64_t T, int64_t H, int k) {
-  __shared__ int s_row[kMaxK];
-  __shared__ float s_w[kMaxK];
+                                                          int64_t T, int64_t H, int k, float scale) {
+  __shared__ int s_row[kMaxE];
+  __shared__ float s_w[kMaxE];
+  __shared__ int s_cnt[4];
   const int64_t hv = H / 4;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
-    if (threadIdx.x < k) {
-      s_row[threadIdx.x] = ros[t * k + threadIdx.x];
-      s_w[threadIdx.x] = tw[t * k + threadIdx.x];
-    }
-    __syncthreads();
+    const int n = load_pairs(ros, tw, t, k, scale, s_row, s_w, s_cnt);
     for (int64_t c = threadIdx.x; c < hv; c += blockDim.x) {
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int j = 0; j < k; ++j) {
-        const int row = s_row[j];
-        if (row < 0) continue;
-        const float4 v = reinterpret_cast<const float4*>(yp + (int64_t)row * H)[c];
+      for (int j = 0; j < n; ++j) {
+        const float4 v = reinterpret_cast<const float4*>(yp + (int64_t)s_row[j] * H)[c];
         const float w = s_w[j];
         acc.x = fmaf(w, v.x, acc.x);
         acc.y = fmaf(w, v.y, acc.y);
@@ -103,16 +129,16 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
 
 hipError_t launch_combine(const void* y_perm, const int32_t* row_of_slot, const float* topk_w,
                           const void* y_shared, void* y, int64_t T, int64_t H, int64_t k, int dtype,
-                          hipStream_t s) {
+                          hipStream_t s, float scale) {
   const unsigned grid = (unsigned)std::min<int64_t>(T, 8192);
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_bf16_kernel, dim3(grid), dim3(256), 0, s, static_cast<const uint16_t*>(y_perm),
                        row_of_slot, topk_w, static_cast<const uint16_t*>(y_shared), static_cast<uint16_t*>(y), T,
-                       H, (int)k);
+                       H, (int)k, scale);
   else
     hipLaunchKernelGGL(combine_f32_kernel, dim3(grid), dim3(256), 0, s, static_cast<const float*>(y_perm),
                        row_of_slot, topk_w, static_cast<const float*>(y_shared), static_cast<float*>(y), T, H,
-                       (int)k);
+                       (int)k, scale);
   return hipGetLastError();
 }
 

@@ -127,8 +127,17 @@ struct GemmArgs {
 hipError_t launch_gateup(const GemmArgs& a, int dtype, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, int dtype, hipStream_t s);
 
+// y[t] = sum over slots j < k with row_of_slot[t*k+j] >= 0 of scale * topk_w[t*k+j]
+// * y_perm[row] (+ y_shared[t]); k up to kMaxE.
 hipError_t launch_combine(const void* y_perm, const int32_t* row_of_slot, const float* topk_w,
                           const void* y_shared, void* y, int64_t T, int64_t H, int64_t k,
-                          int dtype, hipStream_t s);
+                          int dtype, hipStream_t s, float scale = 1.f);
+
+// Expert choice: chunk list of E groups of C rows each (+ shared rows), and the
+// per-expert top-C selection from scores [T, E].
+hipError_t launch_chunks_uniform(int64_t E, int64_t C, int64_t shared_rows, int64_t shared_row0, Chunk* chunks,
+                                 int32_t* n_chunks, int bm, hipStream_t s);
+hipError_t launch_ec_select(const float* scores, int64_t T, int64_t E, int64_t C, int32_t* token_of_row,
+                            int32_t* row_of_pair, hipStream_t s);
 
 }  // namespace moe

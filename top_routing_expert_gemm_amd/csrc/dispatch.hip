@@ -172,6 +172,14 @@ __global__ __launch_bounds__(256) void finalize_kernel(const int32_t* __restrict
   }
 }
 
+// Every one of the E groups holds C rows (row0 = e*C), then the shared rows.
+__global__ __launch_bounds__(kScanThreads) void chunks_uniform_kernel(int E, int C, int64_t shared_rows,
+                                                                      int64_t shared_row0, Chunk* __restrict__ chunks,
+                                                                      int32_t* __restrict__ n_chunks, int bm) {
+  __shared__ int tmp[kScanThreads];
+  const int e = threadIdx.x;
+  emit_chunks(e < E, C, e * C, E, bm, shared_rows, shared_row0, chunks, n_chunks, tmp);
+}
 __global__ __launch_bounds__(kScanThreads) void chunks_from_offsets_kernel(
     const int32_t* __restrict__ offsets, int E, Chunk* __restrict__ chunks, int32_t* __restrict__ n_chunks,
     int bm) {
@@ -223,6 +231,13 @@ hipError_t launch_dispatch(int64_t T, int64_t k, int64_t E, int64_t cap, const i
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)nb), dim3(256), 0, s, topk_idx, Tk, (int)k, (int)E, ch,
                      cap, blk, rank_tmp, offsets, row_of_slot, token_of_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunks_uniform(int64_t E, int64_t C, int64_t shared_rows, int64_t shared_row0, Chunk* chunks,
+                                 int32_t* n_chunks, int bm, hipStream_t s) {
+  hipLaunchKernelGGL(chunks_uniform_kernel, dim3(1), dim3(kScanThreads), 0, s, (int)E, (int)C, shared_rows,
+                     shared_row0, chunks, n_chunks, bm);
   return hipGetLastError();
 }
 
