@@ -52,7 +52,8 @@ __all__ = [
     "gather_rows", "silu", "swiglu_ffn", "grouped_expert_ffn", "combine",
     "moe_forward", "moe_layer_params", "expected_touched_experts", "select_topk_grouped",
     "route_grouped", "aux_loss_terms", "bias_update", "expert_choice_capacity",
-    "select_expert_choice", "moe_forward_ec",
+    "select_expert_choice", "moe_forward_ec", "E4M3_VALUES", "quantize_fp8_blockwise",
+    "dequantize_fp8_blockwise",
 ]
 
 GATE_SOFTMAX = 0
@@ -447,6 +448,65 @@ def moe_forward_ec(x, w_router, router_bias, w_gate, w_up, w_down, *, gate: int,
         y += swiglu_ffn(xw[tok], *shared)
     return y, {"logits": z, "scores": s, "chosen": chosen, "gap": gap,
                "token_of_row": chosen.reshape(-1)}
+
+
+# ------------------------------------------------------- FP8 expert weights ---
+# [MoE-10] "推理时：显存按总参数，计算按激活参数": the released DeepSeek-V3 weights are
+# FP8, about one byte per parameter.  The pages give no format or scaling, so the
+# readings are: OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+# bits; subnormals; largest finite 448; 0x7F / 0xFF are NaN) and one float32
+# scale per 128 x 128 block of each [out, in] weight matrix, dequantised as
+# code value x scale.  The scale is the block's largest |w| / 448 (1 for an
+# all-zero block) computed in float32; each weight becomes the E4M3 value
+# nearest to the float32 quotient w / scale, ties to the even code.
+
+def _e4m3_value(code: int) -> float:
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    if e == 0:
+        return sign * m / 8.0 * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3_VALUES = np.array([_e4m3_value(c) for c in range(256)])   # value of every code
+_E4M3_POS = E4M3_VALUES[:0x7F]                                  # codes 0x00..0x7E: 0 .. 448, increasing
+
+
+def _nearest_e4m3(q32: np.ndarray) -> np.ndarray:
+    """Code of the E4M3 value nearest to each float32 q (ties to the even code),
+    |q| beyond 448 saturating to +-448."""
+    a = np.abs(q32.astype(np.float64))
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 1, 0x7E)   # first value >= a
+    lo = hi - 1
+    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(a >= _E4M3_POS[0x7E], 0x7E, code)
+    code = np.where(a == 0, 0, code)
+    return (code | np.where(np.signbit(q32), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_fp8_blockwise(w_bits: np.ndarray, block: int = 128):
+    """bf16 (uint16 bits) or float32 weights [G, N, K] -> (codes uint8 [G, N, K],
+    scales float32 [G, N/block, K/block]).  N and K must be multiples of block."""
+    w = widen(w_bits).astype(np.float32)          # exact: bf16 / fp32 values are float32 values
+    G, N, K = w.shape
+    if N % block or K % block:
+        raise ValueError("N and K must be multiples of the block")
+    blk = w.reshape(G, N // block, block, K // block, block)
+    amax = np.abs(blk).max(axis=(2, 4))
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = (blk / scale[:, :, None, :, None]).astype(np.float32)       # float32 quotient
+    codes = _nearest_e4m3(q).reshape(G, N, K)
+    return codes, scale
+
+
+def dequantize_fp8_blockwise(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> np.ndarray:
+    """Float64 weights code value x block scale, [G, N, K]."""
+    G, N, K = codes.shape
+    v = E4M3_VALUES[codes].reshape(G, N // block, block, K // block, block)
+    return (v * scales.astype(np.float64)[:, :, None, :, None]).reshape(G, N, K)
 
 
 # -------------------------------------------------------- routing statistics ---
