@@ -10,8 +10,11 @@ A step is one moe_forward: route, dispatch, gate/up + SwiGLU, down, combine.
 Prints one JSON line.  The dominant kernel (the gate/up grouped GEMM) is timed
 with HIP events recorded on the layer's stream around it in every timed step.
 The decode layer (T=16 through the same weights) is timed too and reported
-under "decode".  The CPU baseline is the float64 oracle on a bounded sample of
-the same workload, on the host cores.
+under "decode", with bf16 and with FP8 (E4M3, 128x128 block scales) expert
+weights.  "variants" times the other routing paths on the prefill workload:
+DeepSeek-V3 group-limited selection with a selection bias, the routing
+statistics and bias step, and expert-choice routing.  The CPU baseline is the
+float64 oracle on a bounded sample of the same workload, on the host cores.
 """
 from __future__ import annotations
 
@@ -39,6 +42,7 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=16)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-variants", action="store_true")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (reference for HBM counters)")
     return p.parse_args()
@@ -77,6 +81,59 @@ def timed_forward(moe, torch, cfg, dev, x, y, ws, route, steps, warmup):
     names = ["route", "dispatch", "gateup", "down", "combine"]
     stages = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)] for j, n in enumerate(names)}
     return t1 - t0, stages
+
+
+def event_ms(torch, fn, steps, warmup):
+    """Mean milliseconds of fn() over `steps` calls, timed with events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def variants(moe, torch, np, s, dev, x, y, ws, steps, warmup):
+    """The other routing paths on the prefill workload (same x and weights)."""
+    from synth import NOAUX, make_inputs
+    from synth.device import bits, to_torch
+    res = {}
+    # group-limited top-k with a selection-only bias (DeepSeek-V3 noaux_tc)
+    sn = NOAUX["prefill"]
+    devn = dict(dev)
+    devn["score_bias"] = to_torch(make_inputs(sn, with_experts=False).score_bias, "cuda")
+    cfgn = moe.config_from_shape(sn)
+    route = {"scores": torch.empty((s.T, s.E), dtype=torch.float32, device="cuda"),
+             "counts": torch.empty((s.E,), dtype=torch.int32, device="cuda")}
+    secs, st = timed_forward(moe, torch, cfgn, devn, x, y, ws, route, steps, warmup)
+    res["noaux_tc"] = {"workload": sn.name, "ms_per_step": secs / steps * 1e3, "tokens_per_s": s.T * steps / secs,
+                       "route_ms": float(np.mean(st["route"])), "n_group": sn.n_group, "topk_group": sn.topk_group,
+                       "note": "step includes writing the [T, E] float32 scores"}
+    # routing statistics and the bias step on that batch's counts and scores
+    mean = torch.empty(s.E, device="cuda")
+    frac = torch.empty(s.E, device="cuda")
+    bal = torch.empty(1, device="cuda")
+    b = devn["score_bias"].clone()
+    ms_stats = event_ms(torch, lambda: moe.balance_stats(cfgn, route["counts"], route["scores"], mean, frac, bal, ws),
+                        steps, warmup)
+    ms_bias = event_ms(torch, lambda: moe.bias_update(cfgn, route["counts"], 0.001, b), steps, warmup)
+    sbytes = s.T * s.E * 4 + s.E * 4
+    res["balance_stats"] = {"ms": ms_stats, "bytes": sbytes, "achieved_GBps": sbytes / (ms_stats * 1e-3) / 1e9,
+                            "balance_term": float(bits(bal)[0])}
+    res["bias_update"] = {"ms": ms_bias}
+    # expert-choice routing: C = T k / E tokens per expert
+    cfg = moe.config_from_shape(s)
+    wse = torch.empty(moe.ec_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    ms_ec = event_ms(torch, lambda: moe.forward_ec(cfg, dev, x, y, wse), steps, warmup)
+    C = moe.ec_capacity(cfg)
+    res["expert_choice"] = {"ms_per_step": ms_ec, "tokens_per_s": s.T / (ms_ec * 1e-3), "C": C,
+                            "grouped_gemm_flops": 2.0 * (s.E * C + s.T) * 3 * s.H * s.I}
+    del wse
+    return res
 
 
 def cpu_baseline(inp, s, n_tok):
@@ -198,6 +255,31 @@ def main():
                          "touched_experts": touched, "weight_bytes": wbytes, "achieved_GBps": gbps,
                          "frac_hbm_peak": gbps / PEAK_HBM_GBPS,
                          "stages_ms": {n: float(np.mean(v)) for n, v in st5.items()}}
+        # the same decode layer with FP8 experts (quantised on the GPU from these bf16 weights)
+        q = {}
+        for name, src in (("gate", "w_gate"), ("up", "w_up"), ("down", "w_down")):
+            w = dev[src]
+            q["w_" + name] = torch.empty(w.shape, dtype=torch.uint8, device="cuda")
+            q["s_" + name] = torch.empty((w.shape[0], w.shape[1] // 128, w.shape[2] // 128), device="cuda")
+            moe.quantize_fp8(w, q["w_" + name], q["s_" + name])
+            w = dev["ws_" + name]
+            q["ws_" + name] = torch.empty((1,) + tuple(w.shape), dtype=torch.uint8, device="cuda")
+            q["ss_" + name] = torch.empty((1, w.shape[0] // 128, w.shape[1] // 128), device="cuda")
+            moe.quantize_fp8(w.unsqueeze(0), q["ws_" + name], q["ss_" + name])
+        ms8 = event_ms(torch, lambda: moe.forward_fp8(cfg5, dev5, q, dev5["x"], y5, ws5, route_out=r5), steps5,
+                       a.warmup)
+        wbytes8 = (touched + s5.n_shared) * (3 * s5.H * s5.I + 3 * (s5.H // 128) * (s5.I // 128) * 4) \
+            + s5.E * s5.H * 2
+        gbps8 = wbytes8 / (ms8 * 1e-3) / 1e9
+        out["decode"]["fp8_weights"] = {"ms_per_step": ms8, "tokens_per_s": s5.T / (ms8 * 1e-3),
+                                        "weight_bytes": wbytes8, "achieved_GBps": gbps8,
+                                        "frac_hbm_peak": gbps8 / PEAK_HBM_GBPS,
+                                        "format": "E4M3 codes, one fp32 scale per 128x128 block"}
+        del q
+
+    if not a.no_variants:
+        out["variants"] = variants(moe, torch, np, s, dev, x, y, ws, a.steps, a.warmup)
+        print("[bench] routing variants timed", file=sys.stderr, flush=True)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, s, a.cpu_sample_tokens)

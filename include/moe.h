@@ -228,6 +228,39 @@ moe_status moe_forward_timed(const moe_config *cfg, const moe_weights *w, const 
                              void *y, moe_route_out *route_out, void *ws, size_t ws_bytes,
                              void *stream, void *const *events);
 
+/* ---- FP8 expert weights for decode ([MoE-10] "推理时：显存按总参数，计算按激活参数":
+ * the released DeepSeek-V3 weights are FP8, about one byte per parameter; a
+ * small decode batch streams only the touched experts' weights, so one byte per
+ * weight halves the streamed bytes).  The page gives no format; the library
+ * uses OCP E4M3 codes (bias 7, subnormals, largest finite 448, 0x7F/0xFF NaN)
+ * and one float32 scale per 128 x 128 block of each [out, in] weight matrix,
+ * weight = E4M3 value x block scale.  Activations stay bf16; products are
+ * accumulated in float32 per block and scaled per block. ---- */
+
+typedef struct {
+  const uint8_t *w_gate, *w_up, *w_down;    /* codes [E, I, H], [E, I, H], [E, H, I] */
+  const float *s_gate, *s_up, *s_down;      /* scales [E, I/128, H/128], [E, I/128, H/128], [E, H/128, I/128] */
+  const uint8_t *ws_gate, *ws_up, *ws_down; /* shared expert codes [I, H], [I, H], [H, I]; NULL if n_shared = 0 */
+  const float *ss_gate, *ss_up, *ss_down;   /* its scales [I/128, H/128], [I/128, H/128], [H/128, I/128] */
+} moe_fp8_experts;
+
+/* Quantise G matrices w [G, N, K] (dtype MOE_BF16 or MOE_F32, device) to E4M3
+ * codes [G, N, K] and scales [G, N/128, K/128]: a block's scale is its largest
+ * |w| / 448 in float32 (1.0 for an all-zero block) and each weight becomes the
+ * E4M3 code nearest to the float32 quotient w / scale, ties to the even code.
+ * N and K multiples of 128, G <= 65535. */
+moe_status moe_quantize_fp8(const void *w, int32_t dtype, int64_t G, int64_t N, int64_t K,
+                            uint8_t *codes, float *scales, void *stream);
+
+/* moe_forward with FP8 routed and shared experts (q) for decode batches: the
+ * router (w->w_router, w->router_bias, w->score_bias) and x / y stay bf16;
+ * w's expert pointers are not read.  Requires cfg->dtype == MOE_BF16 and
+ * T <= 16 (else MOE_ERR_UNSUPPORTED), H and I multiples of 128.  Same
+ * workspace as moe_forward. */
+moe_status moe_forward_fp8(const moe_config *cfg, const moe_weights *w, const moe_fp8_experts *q,
+                           const void *x, void *y, moe_route_out *route_out, void *ws,
+                           size_t ws_bytes, void *stream);
+
 /* ---- expert-choice routing ([Hardest], the two routing schools: each expert
  * takes a fixed number of the tokens it wants most; the load is balanced by
  * construction and a token may get no expert) ---- */

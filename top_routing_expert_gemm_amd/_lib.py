@@ -24,7 +24,7 @@ STAGE_EVENTS = 6
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_capacity", "moe_layer_params",
            "moe_route", "moe_route_sel", "moe_balance_stats", "moe_bias_update", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_timed", "moe_ec_capacity",
-           "moe_ec_workspace_size", "moe_route_ec", "moe_forward_ec")
+           "moe_ec_workspace_size", "moe_route_ec", "moe_forward_ec", "moe_quantize_fp8", "moe_forward_fp8")
 
 
 class MoeConfig(ctypes.Structure):
@@ -43,6 +43,11 @@ class MoeWeights(ctypes.Structure):
 class MoeRouteOut(ctypes.Structure):
     _fields_ = [("topk_idx", c_void_p), ("topk_w", c_void_p), ("counts", c_void_p), ("offsets", c_void_p),
                 ("row_of_slot", c_void_p), ("token_of_row", c_void_p), ("scores", c_void_p)]
+
+
+class MoeFp8Experts(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "ws_gate", "ws_up",
+                                        "ws_down", "ss_gate", "ss_up", "ss_down")]
 
 
 class MoeEcOut(ctypes.Structure):
@@ -110,6 +115,11 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_ec.restype = c_int32
         L.moe_forward_ec.argtypes = [P, POINTER(MoeWeights), c_void_p, c_void_p, POINTER(MoeEcOut), c_void_p,
                                      c_size_t, c_void_p]
+        L.moe_quantize_fp8.restype = c_int32
+        L.moe_quantize_fp8.argtypes = [c_void_p, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p]
+        L.moe_forward_fp8.restype = c_int32
+        L.moe_forward_fp8.argtypes = [P, POINTER(MoeWeights), POINTER(MoeFp8Experts), c_void_p, c_void_p,
+                                      POINTER(MoeRouteOut), c_void_p, c_size_t, c_void_p]
         _lib = L
     return _lib
 
@@ -271,3 +281,28 @@ def forward_ec(cfg, weights, x, y, ws, ec_out=None, stream=None):
     _check(lib().moe_forward_ec(ctypes.byref(cfg), ctypes.byref(W), _ptr(x), _ptr(y),
                                 ctypes.byref(O) if O is not None else None, _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(stream)), "moe_forward_ec")
+
+
+# ---- FP8 experts ----
+
+def quantize_fp8(w, codes, scales, stream=None):
+    """moe_quantize_fp8 of a [G, N, K] bf16 / fp32 tensor into codes (uint8) and scales (fp32)."""
+    import torch
+    G, N, K = w.shape
+    dt = BF16 if w.dtype == torch.bfloat16 else F32
+    _check(lib().moe_quantize_fp8(_ptr(w), dt, G, N, K, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_quantize_fp8")
+
+
+def fp8_struct(q) -> MoeFp8Experts:
+    """MoeFp8Experts from a dict of tensors (missing keys -> NULL)."""
+    return MoeFp8Experts(*[_ptr(q.get(n)) for n, _ in MoeFp8Experts._fields_])
+
+
+def forward_fp8(cfg, weights, fp8, x, y, ws, route_out=None, stream=None):
+    W = weights if isinstance(weights, MoeWeights) else weights_struct(weights)
+    Q = fp8 if isinstance(fp8, MoeFp8Experts) else fp8_struct(fp8)
+    R = route_out if isinstance(route_out, MoeRouteOut) or route_out is None else route_out_struct(route_out)
+    _check(lib().moe_forward_fp8(ctypes.byref(cfg), ctypes.byref(W), ctypes.byref(Q), _ptr(x), _ptr(y),
+                                 ctypes.byref(R) if R is not None else None, _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)), "moe_forward_fp8")

@@ -304,8 +304,11 @@ moe_status moe_combine(const moe_config* c, const void* y_perm, const int32_t* r
   return MOE_OK;
 }
 
-moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const void* x, void* y,
-                             moe_route_out* ro, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+// The layer's stage sequence; expert weights from `w` (cfg->dtype) or, when q is
+// not NULL, from the FP8 experts of q (decode batches only, checked by the caller).
+static moe_status forward_impl(const moe_config* c, const moe_weights* w, const moe_fp8_experts* q, const void* x,
+                               void* y, moe_route_out* ro, void* ws, size_t ws_bytes, void* stream,
+                               void* const* events) {
   MOE_TRY(moe_validate(c));
   if (w == nullptr) return MOE_ERR_NULL;
   MOE_TRY(need(x));
@@ -313,13 +316,30 @@ moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const vo
   MOE_TRY(need(w->w_router));
   MOE_TRY(opt(w->router_bias));
   MOE_TRY(opt(w->score_bias));
-  MOE_TRY(need(w->w_gate));
-  MOE_TRY(need(w->w_up));
-  MOE_TRY(need(w->w_down));
-  if (c->n_shared) {
-    MOE_TRY(need(w->ws_gate));
-    MOE_TRY(need(w->ws_up));
-    MOE_TRY(need(w->ws_down));
+  if (q == nullptr) {
+    MOE_TRY(need(w->w_gate));
+    MOE_TRY(need(w->w_up));
+    MOE_TRY(need(w->w_down));
+    if (c->n_shared) {
+      MOE_TRY(need(w->ws_gate));
+      MOE_TRY(need(w->ws_up));
+      MOE_TRY(need(w->ws_down));
+    }
+  } else {
+    MOE_TRY(need(q->w_gate));
+    MOE_TRY(need(q->w_up));
+    MOE_TRY(need(q->w_down));
+    MOE_TRY(need(q->s_gate));
+    MOE_TRY(need(q->s_up));
+    MOE_TRY(need(q->s_down));
+    if (c->n_shared) {
+      MOE_TRY(need(q->ws_gate));
+      MOE_TRY(need(q->ws_up));
+      MOE_TRY(need(q->ws_down));
+      MOE_TRY(need(q->ss_gate));
+      MOE_TRY(need(q->ss_up));
+      MOE_TRY(need(q->ss_down));
+    }
   }
   MOE_TRY(check_ws(c, ws, ws_bytes));
   const Layout L = layout(c);
@@ -365,26 +385,45 @@ moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const vo
   g.n_chunks = nch;
   g.max_chunks = L.max_chunks;
   g.bm = bm;
-  g.w0 = w->w_gate;
-  g.w1 = w->w_up;
-  g.ws0 = w->ws_gate;
-  g.ws1 = w->ws_up;
+  if (q == nullptr) {
+    g.w0 = w->w_gate;
+    g.w1 = w->w_up;
+    g.ws0 = w->ws_gate;
+    g.ws1 = w->ws_up;
+  } else {
+    g.w0 = q->w_gate;
+    g.w1 = q->w_up;
+    g.ws0 = q->ws_gate;
+    g.ws1 = q->ws_up;
+    g.sc0 = q->s_gate;
+    g.sc1 = q->s_up;
+    g.ssc0 = q->ss_gate;
+    g.ssc1 = q->ss_up;
+  }
   g.E = c->E;
   g.K = c->H;
   g.N = c->I;
   g.out = at(ws, L.h);
-  HIP_TRY(launch_gateup(g, c->dtype, s));
+  HIP_TRY(q == nullptr ? launch_gateup(g, c->dtype, s) : launch_gateup_fp8(g, s));
   HIP_TRY(mark(3));
   g.A = at(ws, L.h);
   g.gather = nullptr;
-  g.w0 = w->w_down;
+  if (q == nullptr) {
+    g.w0 = w->w_down;
+    g.ws0 = w->ws_down;
+  } else {
+    g.w0 = q->w_down;
+    g.ws0 = q->ws_down;
+    g.sc0 = q->s_down;
+    g.ssc0 = q->ss_down;
+    g.sc1 = g.ssc1 = nullptr;
+  }
   g.w1 = nullptr;
-  g.ws0 = w->ws_down;
   g.ws1 = nullptr;
   g.K = c->I;
   g.N = c->H;
   g.out = at(ws, L.y_perm);
-  HIP_TRY(launch_down(g, c->dtype, s));
+  HIP_TRY(q == nullptr ? launch_down(g, c->dtype, s) : launch_down_fp8(g, s));
   HIP_TRY(mark(4));
   const void* ysh = c->n_shared ? static_cast<const void*>(at(ws, L.y_perm + (size_t)Tk * c->H * esize(c))) : nullptr;
   HIP_TRY(launch_combine(at(ws, L.y_perm), r.row_of_slot, r.topk_w, ysh, y, c->T, c->H, c->k, c->dtype, s));
@@ -392,9 +431,37 @@ moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const vo
   return MOE_OK;
 }
 
+moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const void* x, void* y,
+                             moe_route_out* ro, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  return forward_impl(c, w, nullptr, x, y, ro, ws, ws_bytes, stream, events);
+}
+
 moe_status moe_forward(const moe_config* c, const moe_weights* w, const void* x, void* y, moe_route_out* ro,
                        void* ws, size_t ws_bytes, void* stream) {
-  return moe_forward_timed(c, w, x, y, ro, ws, ws_bytes, stream, nullptr);
+  return forward_impl(c, w, nullptr, x, y, ro, ws, ws_bytes, stream, nullptr);
+}
+
+// ---- FP8 expert weights ----
+
+moe_status moe_quantize_fp8(const void* w, int32_t dtype, int64_t G, int64_t N, int64_t K, uint8_t* codes,
+                            float* scales, void* stream) {
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (G < 1 || N < kFp8Block || K < kFp8Block || N % kFp8Block != 0 || K % kFp8Block != 0) return MOE_ERR_SHAPE;
+  if (G > 65535 || (N / kFp8Block) * (K / kFp8Block) > (int64_t(1) << 31) - 1) return MOE_ERR_SHAPE;
+  MOE_TRY(need(w));
+  MOE_TRY(need(codes));
+  MOE_TRY(need(scales));
+  HIP_TRY(launch_quantize_fp8(w, dtype, G, N, K, codes, scales, S(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_forward_fp8(const moe_config* c, const moe_weights* w, const moe_fp8_experts* q, const void* x,
+                           void* y, moe_route_out* ro, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(moe_validate(c));
+  if (q == nullptr) return MOE_ERR_NULL;
+  if (c->dtype != MOE_BF16 || c->T > kGemvMaxT) return MOE_ERR_UNSUPPORTED;
+  if (c->H % kFp8Block != 0 || c->I % kFp8Block != 0) return MOE_ERR_SHAPE;
+  return forward_impl(c, w, q, x, y, ro, ws, ws_bytes, stream, nullptr);
 }
 
 // ---- expert choice ----

@@ -122,10 +122,24 @@ struct GemmArgs {
   int64_t N;                // output columns (I or H)
   void* out;                // [rows, N]
   int bm;                   // chunk height the list was cut to (selects the kernel)
+  // FP8 weights (w0/w1/ws0/ws1 then hold E4M3 codes): float32 scales per
+  // kFp8Block x kFp8Block block, [E, N/128, K/128] and [N/128, K/128] (shared)
+  const float* sc0 = nullptr;
+  const float* sc1 = nullptr;
+  const float* ssc0 = nullptr;
+  const float* ssc1 = nullptr;
 };
 
 hipError_t launch_gateup(const GemmArgs& a, int dtype, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, int dtype, hipStream_t s);
+
+// FP8 (E4M3) weights, bf16 activations, batches of <= kGemvMaxT tokens.
+constexpr int kFp8Block = 128;
+hipError_t launch_gateup_fp8(const GemmArgs& a, hipStream_t s);
+hipError_t launch_down_fp8(const GemmArgs& a, hipStream_t s);
+// Block-scaled E4M3 quantisation of G matrices [N, K] (bf16 or fp32 per dtype).
+hipError_t launch_quantize_fp8(const void* w, int dtype, int64_t G, int64_t N, int64_t K, uint8_t* codes,
+                               float* scales, hipStream_t s);
 
 // y[t] = sum over slots j < k with row_of_slot[t*k+j] >= 0 of scale * topk_w[t*k+j]
 // * y_perm[row] (+ y_shared[t]); k up to kMaxE.
