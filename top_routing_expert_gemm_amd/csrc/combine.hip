@@ -6,9 +6,10 @@
 // "细粒度专家与共享专家" (the shared expert's output is added directly) and
 // section "负载不均：路由坍缩与丢 token" (a dropped token skips the expert).
 //
-// One workgroup per token (grid-stride): the kept (row, weight) pairs of the
-// token are read once and compacted in slot order, then every thread
-// accumulates 16-byte column vectors of those y_perm rows in float32 in slot
+// Work item = (token, chunk of 256 16-byte column vectors), grid-stride, so a
+// small batch still spreads over many workgroups.  The kept (row, weight) pairs
+// of the token are read and compacted in slot order, then each thread
+// accumulates one 16-byte column vector of those y_perm rows in float32 in slot
 // order j = 0..k-1, adds the shared row, and stores.  A gather, not a scatter: no atomics, so the result is bitwise
 // reproducible.  HBM bound: reads (kept slots + shared) rows, writes one row.
 #include "common.h"
@@ -71,9 +72,12 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __res
   __shared__ float s_w[kMaxE];
   __shared__ int s_cnt[4];
   const int64_t hv = H / 8;
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+  const int64_t nch = (hv + blockDim.x - 1) / blockDim.x;  // column chunks of a row
+  for (int64_t wi = blockIdx.x; wi < T * nch; wi += gridDim.x) {
+    const int64_t t = wi / nch;
     const int n = load_pairs(ros, tw, t, k, scale, s_row, s_w, s_cnt);
-    for (int64_t c = threadIdx.x; c < hv; c += blockDim.x) {
+    const int64_t c = (wi % nch) * blockDim.x + threadIdx.x;
+    if (c < hv) {
       float acc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -100,9 +104,12 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
   __shared__ float s_w[kMaxE];
   __shared__ int s_cnt[4];
   const int64_t hv = H / 4;
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+  const int64_t nch = (hv + blockDim.x - 1) / blockDim.x;  // column chunks of a row
+  for (int64_t wi = blockIdx.x; wi < T * nch; wi += gridDim.x) {
+    const int64_t t = wi / nch;
     const int n = load_pairs(ros, tw, t, k, scale, s_row, s_w, s_cnt);
-    for (int64_t c = threadIdx.x; c < hv; c += blockDim.x) {
+    const int64_t c = (wi % nch) * blockDim.x + threadIdx.x;
+    if (c < hv) {
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int j = 0; j < n; ++j) {
         const float4 v = reinterpret_cast<const float4*>(yp + (int64_t)s_row[j] * H)[c];
@@ -130,7 +137,8 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
 hipError_t launch_combine(const void* y_perm, const int32_t* row_of_slot, const float* topk_w,
                           const void* y_shared, void* y, int64_t T, int64_t H, int64_t k, int dtype,
                           hipStream_t s, float scale) {
-  const unsigned grid = (unsigned)std::min<int64_t>(T, 8192);
+  const int64_t hv = dtype == MOE_BF16 ? H / 8 : H / 4;
+  const unsigned grid = (unsigned)std::min<int64_t>(T * ((hv + 255) / 256), 16384);
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_bf16_kernel, dim3(grid), dim3(256), 0, s, static_cast<const uint16_t*>(y_perm),
                        row_of_slot, topk_w, static_cast<const uint16_t*>(y_shared), static_cast<uint16_t*>(y), T,

@@ -172,6 +172,75 @@ __global__ __launch_bounds__(256) void finalize_kernel(const int32_t* __restrict
   }
 }
 
+// Small batches (T*k <= kScanThreads): the three steps above in one workgroup.
+// Wave 0 ranks the assignments exactly as hist_rank does (one block); all
+// threads then scan, cut the chunk list and write the row maps, with the ranks
+// and offsets kept in LDS.  Same outputs, one launch instead of three.
+__global__ __launch_bounds__(kScanThreads) void dispatch_small_kernel(
+    const int32_t* __restrict__ idx, int Tk, int k, int E, int64_t cap, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_of_slot, int32_t* __restrict__ token_of_row,
+    Chunk* __restrict__ chunks, int32_t* __restrict__ n_chunks, int bm, int64_t shared_rows,
+    int64_t shared_row0) {
+  __shared__ int32_t cnt[kMaxE];
+  __shared__ int32_t offs[kMaxE];
+  __shared__ int32_t rank_s[kScanThreads];
+  __shared__ int tmp[kScanThreads];
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int e = tid; e < E; e += kScanThreads) cnt[e] = 0;
+  __syncthreads();
+  if (tid < 64) {
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = 0; base < Tk; base += 64) {
+      const int i = base + lane;
+      int e = i < Tk ? idx[i] : 0;
+      const bool valid = i < Tk && e >= 0 && e < E;  // out-of-range ids (a violated precondition) are skipped
+      if (!valid) e = 0;
+      uint64_t peers = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool on = (e >> bit) & 1;
+        const uint64_t bal = __ballot(valid && on);
+        peers &= on ? bal : ~bal;
+      }
+      const int before = __popcll(peers & lt);
+      const int old = valid ? cnt[e] : 0;
+      __builtin_amdgcn_wave_barrier();  // every lane has read its counter before the leaders update
+      if (valid && before == 0) cnt[e] = old + __popcll(peers);
+      if (i < Tk) rank_s[i] = valid ? old + before : -1;
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+  const int e = tid;
+  int load = 0;
+  if (e < E) {
+    const int run = cnt[e];
+    counts[e] = run;
+    load = cap < 0 ? run : (int)min((int64_t)run, cap);
+  }
+  const int incl = block_inclusive_scan(load, tmp);
+  const int excl = incl - load;
+  if (e < E) {
+    offsets[e] = excl;
+    offs[e] = excl;
+  }
+  if (e == E - 1) offsets[E] = incl;
+  emit_chunks(e < E, load, excl, E, bm, shared_rows, shared_row0, chunks, n_chunks, tmp);
+  __syncthreads();
+  if (tid < Tk) {
+    const int r = rank_s[tid];
+    const int ee = r < 0 ? -1 : idx[tid];
+    if (r >= 0 && (cap < 0 || r < cap)) {
+      const int row = offs[ee] + r;
+      row_of_slot[tid] = row;
+      token_of_row[row] = tid / k;
+    } else {
+      row_of_slot[tid] = -1;
+    }
+  }
+}
+
 // Every one of the E groups holds C rows (row0 = e*C), then the shared rows.
 __global__ __launch_bounds__(kScanThreads) void chunks_uniform_kernel(int E, int C, int64_t shared_rows,
                                                                       int64_t shared_row0, Chunk* __restrict__ chunks,
@@ -217,6 +286,12 @@ hipError_t launch_dispatch(int64_t T, int64_t k, int64_t E, int64_t cap, const i
                            int32_t* token_of_row, void* scratch, Chunk* chunks, int32_t* n_chunks,
                            int bm, int64_t shared_rows, int64_t shared_row0, hipStream_t s) {
   const int64_t Tk = T * k;
+  if (Tk <= kScanThreads) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kScanThreads), 0, s, topk_idx, (int)Tk, (int)k, (int)E,
+                       cap, counts, offsets, row_of_slot, token_of_row, chunks, n_chunks, bm, shared_rows,
+                       shared_row0);
+    return hipGetLastError();
+  }
   const int64_t ch = hist_chunk(Tk);
   const int64_t nb = hist_blocks(Tk);
   int32_t* blk = static_cast<int32_t*>(scratch);

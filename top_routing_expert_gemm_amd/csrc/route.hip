@@ -420,36 +420,50 @@ __global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __re
                                                                int gate, int renorm, float scale,
                                                                RouteSel rs, int32_t* __restrict__ topk_idx,
                                                                float* __restrict__ topk_w) {
-  __shared__ float wscr[kRThreads / kWave][kMaxE];
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (kRThreads / kWave) + (threadIdx.x >> 6);
-  if (t >= T) return;
+  constexpr int TPB = kRThreads / kWave;  // tokens per workgroup, one wave each for the top-k
+  __shared__ float wscr[TPB][kMaxE];
+  __shared__ float zs[TPB][kMaxE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * TPB;
   const int Epad = (E + 31) / 32 * 32;
+  const int64_t stride = (int64_t)T * Epad;
+  // The whole workgroup sums the slice partials of its TPB tokens: thread -> expert,
+  // all tokens at once, eight slices per round, added strictly in slice order.
+  for (int e = threadIdx.x; e < E; e += kRThreads) {
+    float s[TPB];
+#pragma unroll
+    for (int j = 0; j < TPB; ++j) s[j] = 0.f;
+    const float* pp = part + (int64_t)t0 * Epad + e;
+    int ks = 0;
+    for (; ks + 8 <= nsplit; ks += 8) {
+      float q[8][TPB];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < TPB; ++j) q[u][j] = t0 + j < T ? pp[(ks + u) * stride + (int64_t)j * Epad] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < TPB; ++j) s[j] += q[u][j];
+    }
+    for (; ks < nsplit; ++ks)
+#pragma unroll
+      for (int j = 0; j < TPB; ++j) s[j] += t0 + j < T ? pp[ks * stride + (int64_t)j * Epad] : 0.f;
+#pragma unroll
+    for (int j = 0; j < TPB; ++j) zs[j][e] = s[j];
+  }
+  __syncthreads();
+  const int t = t0 + wave;
+  if (t >= T) return;
   float z[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int e = lane + kWave * v;
-    if (e < E) {
-      // loads issued eight at a time, added strictly in slice order
-      const float* pp = part + (int64_t)t * Epad + e;
-      const int64_t stride = (int64_t)T * Epad;
-      float s = 0.f;
-      int ks = 0;
-      for (; ks + 8 <= nsplit; ks += 8) {
-        float q[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) q[u] = pp[(ks + u) * stride];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) s += q[u];
-      }
-      for (; ks < nsplit; ++ks) s += pp[ks * stride];
-      z[v] = bias != nullptr ? s + bias[e] : s;
-    } else {
-      z[v] = -INFINITY;
-    }
+    z[v] = e < E ? (bias != nullptr ? zs[wave][e] + bias[e] : zs[wave][e]) : -INFINITY;
   }
-  const SelOpts o{rs.sbias, rs.n_group, rs.topk_group, wscr[threadIdx.x >> 6]};
-  topk_token<VPL>(z, E, k, gate, renorm, scale, o, rs.scores ? rs.scores + (int64_t)t * E : nullptr, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
+  const SelOpts o{rs.sbias, rs.n_group, rs.topk_group, wscr[wave]};
+  topk_token<VPL>(z, E, k, gate, renorm, scale, o, rs.scores ? rs.scores + (int64_t)t * E : nullptr,
+                  topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
 }
 
 // fp32 path: one wave per token computes its E logits with lane-strided dot
@@ -516,7 +530,10 @@ hipError_t launch_route_f32(const moe_config& c, const void* x, const void* w, c
 }
 
 // Split factor of the K dimension: enough workgroups to cover the chip twice,
-// each slice at least 4 K steps long.
+// each slice at least MOE_ROUTE_MIN_KSTEPS K steps long.
+#ifndef MOE_ROUTE_MIN_KSTEPS
+#define MOE_ROUTE_MIN_KSTEPS 4
+#endif
 // Token blocks per workgroup: 64 tokens for large batches (halves the router
 // weight traffic), 32 otherwise and for E > 512 (register budget).
 inline int route_rbt(int64_t T, int64_t E) { return T >= 4096 && E <= 512 ? 2 : 1; }
@@ -525,7 +542,7 @@ inline int route_nsplit(int64_t T, int64_t H, int64_t E) {
   const int64_t mt = (T + rows - 1) / rows;
   const int64_t nk = H / kRBK;
   int64_t ns = (512 + mt - 1) / mt;
-  ns = std::min<int64_t>(ns, std::max<int64_t>(1, nk / 4));
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, nk / MOE_ROUTE_MIN_KSTEPS));
   return (int)std::max<int64_t>(1, ns);
 }
 
