@@ -160,7 +160,7 @@ def cpu_baseline(inp, s, n_tok):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU only; run with --gpus 1"}))
         print("bench.py: only --gpus 1 is supported (single-GPU layer; no collectives)", file=sys.stderr)
         sys.exit(2)
 
@@ -168,12 +168,12 @@ def main():
     import torch
 
     import top_routing_expert_gemm_amd as moe
-    from synth import CONFIGS, make_inputs
+    from synth import DS_DECODE, DS_PREFILL, WORKLOADS, make_inputs
     from synth.device import bits, to_torch, upload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.lib()
-    s = CONFIGS[4]
+    s = WORKLOADS[DS_PREFILL]
     t_gen = time.perf_counter()
     inp = make_inputs(s)
     dev = upload(inp)
@@ -234,7 +234,7 @@ def main():
     }
 
     if not a.no_decode:
-        s5 = CONFIGS[5]
+        s5 = WORKLOADS[DS_DECODE]
         from synth import make_inputs as mk
         inp5 = mk(s5, with_experts=False)
         dev5 = dict(dev)

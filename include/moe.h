@@ -51,7 +51,7 @@ typedef enum {
   MOE_OK = 0,
   MOE_ERR_NULL = 1,        /* a required pointer is NULL */
   MOE_ERR_SHAPE = 2,       /* sizes outside the supported range */
-  MOE_ERR_UNSUPPORTED = 3, /* a valid option this build does not implement */
+  MOE_ERR_UNSUPPORTED = 3, /* a valid option the library does not implement */
   MOE_ERR_WORKSPACE = 4,   /* workspace missing or smaller than moe_workspace_size() */
   MOE_ERR_HIP = 5,         /* a HIP launch or runtime call failed */
   MOE_ERR_ALIGN = 6        /* a device pointer is not 16-byte aligned */

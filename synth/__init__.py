@@ -67,31 +67,33 @@ class MoEShape:
         return replace(self, **kw)
 
 
-# The five layer workloads.  Ids 1..5 are also the seed namespaces.
-CONFIGS = {
-    1: MoEShape("tiny_fp32", T=64, H=128, I=256, E=4, k=2, gate=GATE_SOFTMAX,
+# The five layer workloads, by name; cfg_id is each one's seed namespace.
+WORKLOADS = {s.name: s for s in (
+    MoEShape("tiny_fp32", T=64, H=128, I=256, E=4, k=2, gate=GATE_SOFTMAX,
                 renormalize=True, dtype=F32, cfg_id=1),
-    2: MoEShape("switch_capacity_bf16", T=8192, H=1024, I=4096, E=64, k=1,
+    MoEShape("switch_capacity_bf16", T=8192, H=1024, I=4096, E=64, k=1,
                 gate=GATE_SOFTMAX, renormalize=False, capacity_factor=1.25,
                 dtype=BF16, logit_skew=True, cfg_id=2),
-    3: MoEShape("mixtral_8x7b_bf16", T=4096, H=4096, I=14336, E=8, k=2,
+    MoEShape("mixtral_8x7b_bf16", T=4096, H=4096, I=14336, E=8, k=2,
                 gate=GATE_SOFTMAX, renormalize=True, dtype=BF16, cfg_id=3),
-    4: MoEShape("deepseek_v3_prefill_bf16", T=8192, H=7168, I=2048, E=256, k=8,
+    MoEShape("deepseek_v3_prefill_bf16", T=8192, H=7168, I=2048, E=256, k=8,
                 gate=GATE_SIGMOID, renormalize=True, routed_scaling_factor=2.5,
                 n_shared=1, I_shared=2048, dtype=BF16, cfg_id=4),
     # decode through the same layer (same weights) as the prefill workload
-    5: MoEShape("deepseek_v3_decode_bf16", T=16, H=7168, I=2048, E=256, k=8,
+    MoEShape("deepseek_v3_decode_bf16", T=16, H=7168, I=2048, E=256, k=8,
                 gate=GATE_SIGMOID, renormalize=True, routed_scaling_factor=2.5,
                 n_shared=1, I_shared=2048, dtype=BF16, cfg_id=5, weight_cfg_id=4),
-}
+)}
+TINY, SWITCH, MIXTRAL, DS_PREFILL, DS_DECODE = (
+    "tiny_fp32", "switch_capacity_bf16", "mixtral_8x7b_bf16", "deepseek_v3_prefill_bf16", "deepseek_v3_decode_bf16")
 
 # DeepSeek-V3's own selection on the same layer: 8 groups of 32 experts, 4 kept,
 # and a selection-only per-expert bias drawn N(0, 0.05^2) (the drift of fifty
 # bias steps of 0.001, comparable to the spread of the sigmoid scores).
 NOAUX = {
-    "prefill": CONFIGS[4].with_(name="deepseek_v3_noaux_prefill_bf16", n_group=8, topk_group=4,
+    "prefill": WORKLOADS[DS_PREFILL].with_(name="deepseek_v3_noaux_prefill_bf16", n_group=8, topk_group=4,
                                 score_bias_std=0.05),
-    "decode": CONFIGS[5].with_(name="deepseek_v3_noaux_decode_bf16", n_group=8, topk_group=4,
+    "decode": WORKLOADS[DS_DECODE].with_(name="deepseek_v3_noaux_decode_bf16", n_group=8, topk_group=4,
                                score_bias_std=0.05),
 }
 

@@ -12,7 +12,7 @@ import oracle.moe_ref as ref
 import top_routing_expert_gemm_amd as moe
 from moe_gpu import (TOL, alloc_route, bits, check_rows, compare_dispatch, compare_routing, full_parity,
                      gpu_forward, oracle_kwargs, require_gpu, widen_out, workspace)
-from synth import BF16, CONFIGS, F32, GATE_SIGMOID, GATE_SOFTMAX, MoEShape, make_inputs
+from synth import BF16, DS_DECODE, DS_PREFILL, F32, MIXTRAL, SWITCH, TINY, WORKLOADS, GATE_SIGMOID, GATE_SOFTMAX, MoEShape, make_inputs
 from synth.device import to_torch, upload
 
 pytestmark = pytest.mark.gpu
@@ -26,7 +26,7 @@ SMALL = {
                                    capacity_factor=1.25, logit_skew=True, cfg_id=103),
     "bf16_capacity_k3": MoEShape("bf16_capacity_k3", T=513, H=192, I=256, E=12, k=3, gate=GATE_SIGMOID,
                                  capacity_factor=0.8, cfg_id=104),
-    "fp32_tiny": CONFIGS[1],
+    "fp32_tiny": WORKLOADS[TINY],
     "fp32_sigmoid_shared_capacity": MoEShape("fp32_sigmoid_shared_capacity", T=200, H=192, I=128, E=8, k=3,
                                              gate=GATE_SIGMOID, capacity_factor=1.0, n_shared=1, I_shared=128,
                                              dtype=F32, cfg_id=105),
@@ -252,9 +252,9 @@ def test_errors_launch_nothing():
 _cache = {}
 
 
-def _inputs(cid):
+def _inputs(name):
     """Inputs of one workload; keeps at most one weight namespace resident."""
-    s = CONFIGS[cid]
+    s = WORKLOADS[name]
     if _cache.get("wid") != s.wid:
         _cache.clear()
         torch.cuda.empty_cache()
@@ -270,15 +270,16 @@ def _inputs(cid):
     return s, inp, dev
 
 
-@pytest.mark.parametrize("cid,n_sample", [(1, None), (2, 96), (3, 32), (4, 16), (5, None)])
-def test_forward_workload(cid, n_sample):
-    s, inp, dev = _inputs(cid)
+@pytest.mark.parametrize("name,n_sample", [(TINY, None), (SWITCH, 96), (MIXTRAL, 32), (DS_PREFILL, 16),
+                                            (DS_DECODE, None)])
+def test_forward_workload(name, n_sample):
+    s, inp, dev = _inputs(name)
     res = full_parity(s, inp, dev=dev, n_sample=n_sample)
     print(f"{s.name}: ties={res['ties']} worst_row_rel_err={res['worst']:.3e}")
-    if cid == 2:
+    if name == SWITCH:
         ros = bits(res["route"]["row_of_slot"])
         assert (ros < 0).sum() > 0, "the skewed capacity workload should drop tokens"
-    if cid == 5:
+    if name == DS_DECODE:
         touched = int((bits(res["route"]["counts"]) > 0).sum())
         print(f"decode: {touched} distinct experts touched (uniform model: "
               f"{ref.expected_touched_experts(256, 8, 16):.1f})")

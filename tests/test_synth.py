@@ -1,7 +1,7 @@
 """The seeded input generator: determinism and bfloat16 rounding."""
 import numpy as np
 
-from synth import (BF16, CONFIGS, F32, MoEShape, bf16_bits_to_f32, draw, f32_to_bf16_bits,
+from synth import (BF16, F32, TINY, WORKLOADS, MoEShape, bf16_bits_to_f32, draw, f32_to_bf16_bits,
                    make_inputs, router_skew_bias)
 
 
@@ -30,7 +30,7 @@ def test_threads_do_not_change_bits():
 
 
 def test_fan_in_scaling_and_skew():
-    s = CONFIGS[1]
+    s = WORKLOADS[TINY]
     inp = make_inputs(s, threads=2)
     assert inp.x.dtype == np.float32 and inp.w_gate.shape == (4, 256, 128)
     assert abs(inp.w_gate.std() * np.sqrt(128) - 1) < 0.02
