@@ -255,6 +255,19 @@ def main():
                          "touched_experts": touched, "weight_bytes": wbytes, "achieved_GBps": gbps,
                          "frac_hbm_peak": gbps / PEAK_HBM_GBPS,
                          "stages_ms": {n: float(np.mean(v)) for n, v in st5.items()}}
+        # the same step captured once in a HIP graph and replayed (no host launches per step)
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gs):
+            moe.forward(cfg5, dev5, dev5["x"], y5, ws5, route_out=r5)
+        torch.cuda.current_stream().wait_stream(gs)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            moe.forward(cfg5, dev5, dev5["x"], y5, ws5, route_out=r5)
+        msg = event_ms(torch, graph.replay, steps5, a.warmup)
+        out["decode"]["graph_replay"] = {"ms_per_step": msg, "frac_hbm_peak": wbytes / (msg * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        del graph
         # the same decode layer with FP8 experts (quantised on the GPU from these bf16 weights)
         q = {}
         for name, src in (("gate", "w_gate"), ("up", "w_up"), ("down", "w_down")):
