@@ -26,8 +26,10 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 
+// Assignments per histogram block: 256 (four 64-wide steps of one wave), doubled
+// until there are at most 4096 blocks.
 inline int64_t hist_chunk(int64_t Tk) {
-  int64_t ch = 1024;
+  int64_t ch = 256;
   while ((Tk + ch - 1) / ch > 4096) ch *= 2;
   return ch;
 }
@@ -130,10 +132,22 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   const int e = tid;
   int load = 0;
   if (e < E) {
+    // exclusive block bases, sixteen independent loads per round, summed in block order
     int run = 0;
-    for (int64_t b = 0; b < nb; ++b) {
+    int64_t b = 0;
+    for (; b + 16 <= nb; b += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c[u] = blk_counts[(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        blk_counts[(b + u) * E + e] = run;
+        run += c[u];
+      }
+    }
+    for (; b < nb; ++b) {
       const int c = blk_counts[b * E + e];
-      blk_counts[b * E + e] = run;  // exclusive block base
+      blk_counts[b * E + e] = run;
       run += c;
     }
     counts[e] = run;

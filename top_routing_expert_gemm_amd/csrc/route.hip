@@ -529,20 +529,24 @@ hipError_t launch_route_f32(const moe_config& c, const void* x, const void* w, c
   return hipGetLastError();
 }
 
-// Split factor of the K dimension: enough workgroups to cover the chip twice,
-// each slice at least MOE_ROUTE_MIN_KSTEPS K steps long.
-#ifndef MOE_ROUTE_MIN_KSTEPS
-#define MOE_ROUTE_MIN_KSTEPS 4
-#endif
-// Token blocks per workgroup: 64 tokens for large batches (halves the router
-// weight traffic), 32 otherwise and for E > 512 (register budget).
-inline int route_rbt(int64_t T, int64_t E) { return T >= 4096 && E <= 512 ? 2 : 1; }
+// Token blocks per workgroup: 128 tokens for the largest batches with E <= 256
+// and 64 for large ones (fewer passes over the router weights per token), 32
+// otherwise and for E > 512 (register budget).
+// Split factor of the K dimension: enough workgroups to cover the chip twice
+// (once with 128-token blocks, whose partials are twice as many per token),
+// each slice at least four K steps long.
+inline int route_rbt(int64_t T, int64_t E) {
+  if (T >= 8192 && E <= 256) return 4;
+  return T >= 4096 && E <= 512 ? 2 : 1;
+}
 inline int route_nsplit(int64_t T, int64_t H, int64_t E) {
-  const int64_t rows = route_rbt(T, E) * kRBM;
+  const int rbt = route_rbt(T, E);
+  const int64_t rows = rbt * kRBM;
   const int64_t mt = (T + rows - 1) / rows;
   const int64_t nk = H / kRBK;
-  int64_t ns = (512 + mt - 1) / mt;
-  ns = std::min<int64_t>(ns, std::max<int64_t>(1, nk / MOE_ROUTE_MIN_KSTEPS));
+  const int64_t target = rbt == 4 ? 256 : 512;
+  int64_t ns = (target + mt - 1) / mt;
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, nk / 4));
   return (int)std::max<int64_t>(1, ns);
 }
 
@@ -569,6 +573,8 @@ hipError_t launch_route_split_t(const moe_config& c, const void* x, const void* 
 template <int NBW>
 hipError_t launch_route_split_n(const moe_config& c, const void* x, const void* w, const float* bias,
                                 const RouteSel& rs, int32_t* idx, float* tw, float* part, hipStream_t s) {
+  if constexpr (NBW <= 2)
+    if (route_rbt(c.T, c.E) == 4) return launch_route_split_t<NBW, 4>(c, x, w, bias, rs, idx, tw, part, s);
   if constexpr (NBW <= 4)
     if (route_rbt(c.T, c.E) == 2) return launch_route_split_t<NBW, 2>(c, x, w, bias, rs, idx, tw, part, s);
   return launch_route_split_t<NBW, 1>(c, x, w, bias, rs, idx, tw, part, s);
