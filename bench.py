@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-variants", action="store_true")
+    p.add_argument("--no-achievable", action="store_true")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (reference for HBM counters)")
     return p.parse_args()
@@ -65,7 +66,8 @@ def traffic_entry(kernel_ms):
 
 
 def timed_forward(moe, torch, cfg, dev, x, y, ws, route, steps, warmup):
-    """Warmup, then `steps` timed moe_forward calls with stage events; returns (seconds, stage ms lists)."""
+    """Warmup, then `steps` timed moe_forward calls with stage events; returns (seconds, stage ms lists,
+    whole-step ms list from the first to the last event of each step)."""
     for _ in range(warmup):
         moe.forward(cfg, dev, x, y, ws, route_out=route)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.STAGE_EVENTS)] for _ in range(steps)]
@@ -80,7 +82,8 @@ def timed_forward(moe, torch, cfg, dev, x, y, ws, route, steps, warmup):
     t1 = time.perf_counter()
     names = ["route", "dispatch", "gateup", "down", "combine"]
     stages = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)] for j, n in enumerate(names)}
-    return t1 - t0, stages
+    per_step = [evs[i][0].elapsed_time(evs[i][len(names)]) for i in range(steps)]
+    return t1 - t0, stages, per_step
 
 
 def event_ms(torch, fn, steps, warmup):
@@ -97,6 +100,27 @@ def event_ms(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def achievable(torch):
+    """Peaks this box reaches on plain work, next to the published ones: a 2 GiB
+    device copy (torch copy_: read + write bytes) and a dense bf16 GEMM of the
+    gate/up shape with every token on one expert (torch.matmul -> hipBLASLt)."""
+    n = 2 ** 31
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms_copy = event_ms(torch, lambda: dst.copy_(src), 10, 3)
+    del src, dst
+    m, kk, nn = 8192 * 9, 7168, 4096
+    a = torch.randn(m, kk, device="cuda").to(torch.bfloat16)
+    b = torch.randn(kk, nn, device="cuda").to(torch.bfloat16)
+    ms_mm = event_ms(torch, lambda: torch.matmul(a, b), 10, 3)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": 2.0 * n / (ms_copy * 1e-3) / 1e9,
+            "dense_bf16_gemm_TFLOPs": 2.0 * m * kk * nn / (ms_mm * 1e-3) / 1e12,
+            "dense_gemm_shape": [m, kk, nn],
+            "note": "copy counts bytes read + written; GEMM is torch.matmul (hipBLASLt), contiguous operands"}
+
+
 def variants(moe, torch, np, s, dev, x, y, ws, steps, warmup):
     """The other routing paths on the prefill workload (same x and weights)."""
     from synth import NOAUX, make_inputs
@@ -109,7 +133,7 @@ def variants(moe, torch, np, s, dev, x, y, ws, steps, warmup):
     cfgn = moe.config_from_shape(sn)
     route = {"scores": torch.empty((s.T, s.E), dtype=torch.float32, device="cuda"),
              "counts": torch.empty((s.E,), dtype=torch.int32, device="cuda")}
-    secs, st = timed_forward(moe, torch, cfgn, devn, x, y, ws, route, steps, warmup)
+    secs, st, _ = timed_forward(moe, torch, cfgn, devn, x, y, ws, route, steps, warmup)
     res["noaux_tc"] = {"workload": sn.name, "ms_per_step": secs / steps * 1e3, "tokens_per_s": s.T * steps / secs,
                        "route_ms": float(np.mean(st["route"])), "n_group": sn.n_group, "topk_group": sn.topk_group,
                        "note": "step includes writing the [T, E] float32 scores"}
@@ -200,7 +224,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    secs, st = timed_forward(moe, torch, cfg, dev, x, y, ws, route, a.steps, a.warmup)
+    secs, st, per_step = timed_forward(moe, torch, cfg, dev, x, y, ws, route, a.steps, a.warmup)
     ms_step = secs / a.steps * 1e3
     tokens_per_s = s.T * a.steps / secs
     print(f"[bench] {a.steps} steps in {secs:.3f} s", file=sys.stderr, flush=True)
@@ -230,6 +254,8 @@ def main():
         "grouped_gemm": {"tflops": gemm_tflops, "frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS,
                          "flops": fl_gateup + fl_down, "ms": avg["gateup"] + avg["down"]},
         "stages_ms": avg,
+        "step_ms_events": {"median": float(np.median(per_step)), "min": float(np.min(per_step)),
+                           "max": float(np.max(per_step))},
         "routing": {"kept_rows": R, "max_rows_per_expert": int(counts.max()), "min_rows_per_expert": int(counts.min())},
     }
 
@@ -244,7 +270,7 @@ def main():
         ws5 = torch.empty(moe.workspace_size(cfg5), dtype=torch.uint8, device="cuda")
         r5 = {"counts": torch.empty((s5.E,), dtype=torch.int32, device="cuda")}
         steps5 = max(a.steps, 20)
-        secs5, st5 = timed_forward(moe, torch, cfg5, dev5, dev5["x"], y5, ws5, r5, steps5, a.warmup)
+        secs5, st5, _ = timed_forward(moe, torch, cfg5, dev5, dev5["x"], y5, ws5, r5, steps5, a.warmup)
         c5 = bits(r5["counts"])
         touched = int((c5 > 0).sum())
         per_expert = 3 * s5.H * s5.I * 2
@@ -293,6 +319,11 @@ def main():
     if not a.no_variants:
         out["variants"] = variants(moe, torch, np, s, dev, x, y, ws, a.steps, a.warmup)
         print("[bench] routing variants timed", file=sys.stderr, flush=True)
+    if not a.no_achievable:
+        out["achievable"] = achievable(torch)
+        g = out["achievable"]
+        out["roofline"]["frac_of_achievable"] = gateup_tflops / g["dense_bf16_gemm_TFLOPs"]
+        print("[bench] achievable peaks measured", file=sys.stderr, flush=True)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, s, a.cpu_sample_tokens)
