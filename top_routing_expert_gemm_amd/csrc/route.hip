@@ -194,7 +194,7 @@ __device__ void topk_token(float (&z)[VPL], int E, int k, int gate, int renorm, 
       float bv = cand ? gs : -INFINITY;
       int bi = cand ? lane : 0x7fffffff;
       wave_argmax(bv, bi);
-      kept |= 1ull << bi;
+      if (bi < 64) kept |= 1ull << bi;  // always a group id when topk_group <= n_group
     }
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
