@@ -75,6 +75,9 @@ CASES = {
                                   capacity_factor=3.0, n_shared=1, I_shared=64, dtype=F32, cfg_id=403),
     "bf16_decode_T12": MoEShape("bf16_decode_T12", T=12, H=256, I=128, E=32, k=8, gate=GATE_SIGMOID,
                                 routed_scaling_factor=2.5, n_shared=1, I_shared=128, cfg_id=404),
+    # C = 512: two 256-row chunks per expert; 3 K steps in the down pass (I = 192)
+    "bf16_C512": MoEShape("bf16_C512", T=1024, H=256, I=192, E=4, k=2, gate=GATE_SIGMOID, n_shared=1,
+                          I_shared=192, cfg_id=406),
     "deepseek_v3_ec_narrow_experts": MoEShape("deepseek_v3_ec_narrow_experts", T=8192, H=7168, I=64, E=256, k=8,
                                               gate=GATE_SIGMOID, routed_scaling_factor=2.5, n_shared=1,
                                               I_shared=64, cfg_id=405),

@@ -21,12 +21,24 @@ struct Layout {
   int64_t max_chunks;  // chunk-list capacity
 };
 
+int64_t cap_of(const moe_config* c);
+
+// Chunk height of the moe_forward family: its row space holds at most T*k
+// routed + T shared rows; the busiest expert is expected to hold its capacity
+// when one is set, else about 1.2x the mean T*k/E (the spread of the synthetic
+// routing of the benchmark shapes stays within it).
+int fwd_bm(const moe_config* c) {
+  const int64_t cap = cap_of(c);
+  const int64_t busiest = cap > 0 ? cap : (c->T * c->k * 6 + 5 * c->E - 1) / (5 * c->E);
+  return gemm_bm(*c, c->T * c->k + c->T, busiest);
+}
+
 Layout layout(const moe_config* c) {
   Layout L;
   const int64_t Tk = c->T * c->k;
   const int64_t sh = c->n_shared ? c->T : 0;
   L.rows = Tk + sh;
-  L.max_chunks = max_chunks(Tk, c->E, sh, gemm_bm(*c));
+  L.max_chunks = max_chunks(Tk, c->E, sh, fwd_bm(c));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -68,7 +80,7 @@ LayoutEC layout_ec(const moe_config* c) {
   const int64_t R = c->E * L.C;
   const int64_t sh = c->n_shared ? c->T : 0;
   L.rows = R + sh;
-  L.max_chunks = max_chunks(R, c->E, sh, gemm_bm(*c));
+  L.max_chunks = max_chunks(R, c->E, sh, gemm_bm(*c, R + c->T, L.C));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -245,7 +257,7 @@ moe_status moe_dispatch(const moe_config* c, const int32_t* topk_idx, const void
   const Layout L = layout(c);
   HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), topk_idx, counts, offsets, row_of_slot, token_of_row,
                           at(ws, L.dscratch), reinterpret_cast<Chunk*>(at(ws, L.chunks)),
-                          reinterpret_cast<int32_t*>(at(ws, L.n_chunks)), gemm_bm(*c), 0, 0, S(stream)));
+                          reinterpret_cast<int32_t*>(at(ws, L.n_chunks)), fwd_bm(c), 0, 0, S(stream)));
   if (x_perm != nullptr)
     HIP_TRY(launch_gather(x, token_of_row, offsets, c->E, c->T * c->k, c->H, c->dtype, x_perm, S(stream)));
   return MOE_OK;
@@ -263,7 +275,7 @@ moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t
   MOE_TRY(need(y_perm));
   MOE_TRY(check_ws(c, ws, ws_bytes));
   const Layout L = layout(c);
-  const int bm = gemm_bm(*c);
+  const int bm = fwd_bm(c);
   Chunk* chunks = reinterpret_cast<Chunk*>(at(ws, L.chunks));
   int32_t* nch = reinterpret_cast<int32_t*>(at(ws, L.n_chunks));
   HIP_TRY(launch_chunks_from_offsets(offsets, c->E, chunks, nch, bm, S(stream)));
@@ -280,6 +292,7 @@ moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t
   g.E = c->E;
   g.K = c->H;
   g.N = c->I;
+  g.a_rows = c->T * c->k;
   g.out = at(ws, L.h);
   HIP_TRY(launch_gateup(g, c->dtype, S(stream)));
   g.A = at(ws, L.h);
@@ -364,7 +377,7 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
     if (events == nullptr || events[i] == nullptr) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
   };
-  const int bm = gemm_bm(*c);
+  const int bm = fwd_bm(c);
   const int64_t Tk = c->T * c->k;
   const int64_t sh = c->n_shared ? c->T : 0;
   Chunk* chunks = reinterpret_cast<Chunk*>(at(ws, L.chunks));
@@ -403,6 +416,7 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
   g.E = c->E;
   g.K = c->H;
   g.N = c->I;
+  g.a_rows = c->T;
   g.out = at(ws, L.h);
   HIP_TRY(q == nullptr ? launch_gateup(g, c->dtype, s) : launch_gateup_fp8(g, s));
   HIP_TRY(mark(3));
@@ -422,6 +436,7 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
   g.ws1 = nullptr;
   g.K = c->I;
   g.N = c->H;
+  g.a_rows = L.rows;
   g.out = at(ws, L.y_perm);
   HIP_TRY(q == nullptr ? launch_down(g, c->dtype, s) : launch_down_fp8(g, s));
   HIP_TRY(mark(4));
@@ -524,7 +539,7 @@ moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void*
   MOE_TRY(need(o.row_of_pair));
 
   hipStream_t s = S(stream);
-  const int bm = gemm_bm(*c);
+  const int bm = gemm_bm(*c, c->E * L.C + c->T, L.C);
   const int64_t R = c->E * L.C;
   const int64_t sh = c->n_shared ? c->T : 0;
   Chunk* chunks = reinterpret_cast<Chunk*>(at(ws, L.chunks));
@@ -550,6 +565,7 @@ moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void*
   g.E = c->E;
   g.K = c->H;
   g.N = c->I;
+  g.a_rows = c->T;
   g.out = at(ws, L.h);
   HIP_TRY(launch_gateup(g, c->dtype, s));
   g.A = at(ws, L.h);
@@ -560,6 +576,7 @@ moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void*
   g.ws1 = nullptr;
   g.K = c->I;
   g.N = c->H;
+  g.a_rows = L.rows;
   g.out = at(ws, L.y_perm);
   HIP_TRY(launch_down(g, c->dtype, s));
   const void* ysh = c->n_shared ? static_cast<const void*>(at(ws, L.y_perm + (size_t)R * c->H * esize(c))) : nullptr;

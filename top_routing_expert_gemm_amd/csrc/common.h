@@ -29,19 +29,39 @@ struct Chunk {
   int32_t pad[3];
 };
 
-// M-tile height of the bf16 grouped GEMM; chunk lists are cut to it.
-constexpr int kGemmBM = 320;
+// M-tile heights of the two bf16 grouped GEMM kernels: register-staged (256)
+// and direct-to-LDS (320).  Chunk lists are cut to the one gemm_bm picks.
+#ifndef MOE_GEMM_RS
+#define MOE_GEMM_RS 1
+#endif
+constexpr int kGemmBMrs = 256;
+constexpr int kGemmBMdl = 320;
 // M-tile height of the fp32 grouped GEMM.
 constexpr int kGemmBMf32 = 64;
 // Row chunks of the bf16 weight-streaming path used for small batches (decode).
 constexpr int kGemvBM = 16;
 constexpr int64_t kGemvMaxT = 16;
 
-// Chunk height for a layer: the streaming path when every expert group fits one
-// 16-row chunk (T <= 16), the 320-row MFMA tile otherwise; fp32 uses 64.
-inline int gemm_bm(const moe_config& c) {
+// Chunk height for a layer whose permuted row space has at most `rows` rows and
+// whose busiest expert group is expected to hold `group_rows` rows: the
+// streaming path when every group fits one 16-row chunk (T <= 16); fp32 uses
+// 64.  For bf16 both MFMA kernels are eligible when the register-staged one's
+// limits hold (both contractions >= 128 long, 32-bit buffer offsets covering
+// x [T, H], the row space and h [rows, I]); a register-staged 256-row chunk
+// costs about 0.85 of a direct-to-LDS 320-row chunk (measured on the DeepSeek-V3,
+// Mixtral and Switch shapes), so the 256-row tile is taken unless it needs
+// more chunks per group than that saves (a group of 257..320 rows: two
+// chunks instead of one).
+inline int gemm_bm(const moe_config& c, int64_t rows, int64_t group_rows) {
   if (c.dtype != MOE_BF16) return kGemmBMf32;
-  return c.T <= kGemvMaxT ? kGemvBM : kGemmBM;
+  if (c.T <= kGemvMaxT) return kGemvBM;
+  const int64_t lim = int64_t(1) << 32;
+  const bool fits = MOE_GEMM_RS && c.H >= 128 && c.I >= 128 && std::max<int64_t>(c.T, rows) * c.H * 2 < lim &&
+                    rows * c.I * 2 < lim && c.H * c.I * 2 < lim;
+  if (!fits) return kGemmBMdl;
+  const int64_t g = std::max<int64_t>(group_rows, 1);
+  const int64_t n_rs = (g + kGemmBMrs - 1) / kGemmBMrs, n_dl = (g + kGemmBMdl - 1) / kGemmBMdl;
+  return 17 * n_rs <= 20 * n_dl ? kGemmBMrs : kGemmBMdl;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -122,6 +142,7 @@ struct GemmArgs {
   int64_t N;                // output columns (I or H)
   void* out;                // [rows, N]
   int bm;                   // chunk height the list was cut to (selects the kernel)
+  int64_t a_rows = 0;       // rows of A addressable through `gather` / the row space
   // FP8 weights (w0/w1/ws0/ws1 then hold E4M3 codes): float32 scales per
   // kFp8Block x kFp8Block block, [E, N/128, K/128] and [N/128, K/128] (shared)
   const float* sc0 = nullptr;

@@ -89,7 +89,10 @@ __device__ int block_inclusive_scan(int v, int* tmp) {
 }
 
 // Chunk list of E groups with given loads and first rows, then (optionally) the
-// shared group over rows shared_row0 .. shared_row0 + shared_rows - 1.
+// shared group over rows shared_row0 .. shared_row0 + shared_rows - 1.  A group
+// of `load` rows takes ceil(load / bm) chunks of balanced height (chunk c holds
+// rows [c load / n, (c + 1) load / n)), so the workgroups that stream the same
+// weight tile for one group do equal work and stay in step.
 __device__ void emit_chunks(int e_valid, int load, int row0, int E, int bm, int64_t shared_rows,
                             int64_t shared_row0, Chunk* chunks, int32_t* n_chunks, int* tmp) {
   const int tid = threadIdx.x;
@@ -97,10 +100,11 @@ __device__ void emit_chunks(int e_valid, int load, int row0, int E, int bm, int6
   const int incl = block_inclusive_scan(nch, tmp);
   const int base = incl - nch;
   for (int c = 0; c < nch; ++c) {
+    const int r0 = (int)((int64_t)c * load / nch), r1 = (int)((int64_t)(c + 1) * load / nch);
     Chunk ck;
     ck.group = tid;
-    ck.row0 = row0 + c * bm;
-    ck.nrows = min(bm, load - c * bm);
+    ck.row0 = row0 + r0;
+    ck.nrows = r1 - r0;
     ck.gfirst = base;
     ck.gcount = nch;
     ck.pad[0] = ck.pad[1] = ck.pad[2] = 0;
@@ -111,10 +115,11 @@ __device__ void emit_chunks(int e_valid, int load, int row0, int E, int bm, int6
   __syncthreads();
   const int nsh = (int)((shared_rows + bm - 1) / bm);
   for (int c = tid; c < nsh; c += kScanThreads) {
+    const int64_t r0 = c * shared_rows / nsh, r1 = (c + 1) * shared_rows / nsh;
     Chunk ck;
     ck.group = E;
-    ck.row0 = (int)(shared_row0 + (int64_t)c * bm);
-    ck.nrows = (int)min((int64_t)bm, shared_rows - (int64_t)c * bm);
+    ck.row0 = (int)(shared_row0 + r0);
+    ck.nrows = (int)(r1 - r0);
     ck.gfirst = total;
     ck.gcount = nsh;
     ck.pad[0] = ck.pad[1] = ck.pad[2] = 0;

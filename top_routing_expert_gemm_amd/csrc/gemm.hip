@@ -37,7 +37,7 @@
 namespace moe {
 namespace {
 
-constexpr int BM = kGemmBM;  // 320 rows: one chunk holds a whole routed expert of the large workloads
+constexpr int BM = kGemmBMdl;  // 320 rows: one chunk holds a whole routed expert of the large workloads
 constexpr int BMW = BM / 2;  // rows per wave-row
 constexpr int RB = BMW / 32; // 32-row MFMA blocks per wave (5)
 constexpr int BN = 256;
@@ -48,6 +48,9 @@ constexpr int SUPER = 4;     // chunks of one group interleaved per n-tile
 #define MOE_GEMM_BK 32
 #endif
 constexpr int BK = MOE_GEMM_BK;
+#ifndef MOE_DL_B_AUX
+#define MOE_DL_B_AUX 0
+#endif
 constexpr int STAGES = BK == 64 ? 2 : 4;     // LDS: 2 x (320 + 256) x 128 B or 4 x (384 + 256) x 64 B
 constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row
 constexpr int RPB = 64 / CPR;               // tile rows per 1 KB direct-to-LDS block
@@ -151,7 +154,7 @@ __device__ __forceinline__ void issue_stage(const Frag& f, int kt, int wave) {
 #pragma unroll
   for (int i = 0; i < B_BLK; ++i)
     __builtin_amdgcn_global_load_lds((glb_void*)(f.gb[i] + ko), (lds_void*)(stB<S>() + (wave * B_BLK + i) * 512),
-                                     16, 0, 0);
+                                     16, 0, MOE_DL_B_AUX);
 }
 
 // NRB 32-row blocks x two 32-column blocks of this wave, one K step.
@@ -375,6 +378,406 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
   }
 }
 
+// ------------------------------------------------ bf16 register-staged path
+// A 256 x 256 tile with K steps of 64, four waves (one per SIMD: each wave has
+// the SIMD's whole register file, 256 accumulators in AGPRs plus operands and
+// staging).  Wave (wm, wn) computes 32-row blocks wm, wm + 2, ... (interleaved,
+// so a short chunk spreads its MFMA work over all four SIMDs) against 128 tile
+// columns, with v_mfma_f32_32x32x16_bf16.
+//
+// Data path: every lane fetches whole 128-byte row pieces (eight lanes per row,
+// 16 bytes each) of the K tile after next into registers while the current
+// tile is computed from LDS, then writes the next tile's registers into the
+// other LDS buffer.  Two K tiles are thus in flight per workgroup, held in the
+// register file rather than in LDS (two LDS buffers of 64 KB).  One barrier per
+// K step.  The 16-byte chunks of each 128-byte LDS row are XOR-swizzled by row
+// so the ds_write_b128 stores and the MFMA operand reads are free of bank
+// conflicts.
+//
+// Gate/up pass: the wave's four 32-column blocks are two gate blocks and the
+// matching two up blocks (same I columns), so SwiGLU is applied in registers.
+// A chunk's row count selects how many 32-row A blocks are fetched (NA) and how
+// many row blocks each wave multiplies (NRB): both are template arguments, so
+// the loop holds no conditional memory traffic and the compiler's wait counts
+// are exact.
+constexpr int RWMB = 4;            // 32-row blocks per wave
+constexpr int RWNB = 4;            // 32-column blocks per wave
+constexpr int RBM = 64 * RWMB;     // 256 tile rows
+constexpr int RBN = 64 * RWNB;     // 256 tile columns (gate/up: 128 gate + 128 up)
+constexpr int RBK = 64;            // K per step: 128-byte row pieces
+constexpr int RNT = 256;           // threads
+constexpr int RNAL = RBM / 32;     // A loads per lane per K step (at most)
+constexpr int RNBL = RBN / 32;     // B loads per lane per K step
+constexpr int RROWS = RBM + RBN;   // 128-byte LDS rows per buffer
+static_assert(kGemmBMrs == RBM, "chunk lists are cut to the tile height");
+static_assert(2 * RROWS * 128 <= 160 * 1024, "LDS");
+
+__device__ __forceinline__ int rswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct RsRegs {
+  u32x4 a[RNAL];
+  u32x4 b[RNBL];
+};
+
+// Buffer-resource loads: wave-uniform bases in scalar registers, one 32-bit
+// per-lane offset per A row and one shared by all B rows, the K position and
+// the B row group in the scalar offset.
+struct RsSrc {
+  __amdgpu_buffer_rsrc_t ra;   // A rows (x gathered, or the row space)
+  __amdgpu_buffer_rsrc_t rg;   // gate (gate/up) or down weights of the tile's group
+  __amdgpu_buffer_rsrc_t ru;   // up weights (gate/up)
+  uint32_t aoff[RNAL];         // per-lane byte offset of A row piece i at k = 0
+  uint32_t boff;               // per-lane byte offset of the row piece within a 32-row B group
+  uint32_t bgrp[RNBL];         // byte offset of B group j within its matrix
+};
+constexpr int kBufFlags = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
+#ifndef MOE_RS_B_AUX
+#define MOE_RS_B_AUX 2  // B loads: non-temporal (each weight is read once)
+#endif
+
+// Operand registers of one 16-wide substep.
+struct RsOps {
+  bf16x8 a[RWMB];
+  bf16x8 b[RWNB];
+};
+
+// LDS barrier: this wave's LDS operations done, then workgroup barrier; global
+// loads stay in flight.
+__device__ __forceinline__ void rs_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt(63) expcnt(7) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Global load q of one K step (q < NA: A block q, else B block q - NA).
+template <int MODE, int NA>
+__device__ __forceinline__ void rs_load1(RsRegs& r, const RsSrc& s, int kt, int q) {
+  const int ko = kt * (RBK * 2);
+  if (q < NA) {
+    r.a[q] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, s.aoff[q], ko, 0);
+  } else {
+    const int j = q - NA;
+    const bool up = MODE == MODE_GATEUP && (j & 3) >= 2;
+    r.b[j] = __builtin_amdgcn_raw_buffer_load_b128(up ? s.ru : s.rg, s.boff, (int)s.bgrp[j] + ko, MOE_RS_B_AUX);
+  }
+}
+
+// LDS store q of one K step into buffer L; wr = this lane's uint4 slot within a
+// 32-row group.
+template <int NA>
+__device__ __forceinline__ void rs_store1(const RsRegs& r, u32x4* L, int wr, int q) {
+  if (q < NA) L[q * 256 + wr] = r.a[q];
+  else L[(RNAL + q - NA) * 256 + wr] = r.b[q - NA];
+}
+
+// Operand read q of substep s from buffer L, in the order the MFMAs use them:
+// A block 0, the RWNB B blocks, then A blocks 1 .. NRB-1.  ra[s] / rb[s]: this
+// lane's uint4 slot of its first A / B operand row for substep s; A block a
+// adds 2 x 32 rows, B block n adds 32 rows.
+__device__ __forceinline__ void rs_read1(RsOps& o, const u32x4* L, const int (&ra)[4], const int (&rb)[4], int s,
+                                         int q) {
+  if (q == 0) o.a[0] = __builtin_bit_cast(bf16x8, L[ra[s]]);
+  else if (q <= RWNB) o.b[q - 1] = __builtin_bit_cast(bf16x8, L[rb[s] + (q - 1) * 256]);
+  else o.a[q - RWNB] = __builtin_bit_cast(bf16x8, L[ra[s] + (q - RWNB) * 512]);
+}
+
+// One 16-wide substep SS of K step t (in buffer S), with the memory traffic of
+// the pipeline interleaved between its MFMAs in a fixed order:
+//   SS 0: the global loads of step t + 2 (register set S), operand reads of SS 1;
+//   SS 1: operand reads of SS 2;
+//   SS 2: operand reads of SS 3, then the LDS stores of step t + 1 (register set
+//         1 - S into buffer 1 - S, whose last reads were before the previous
+//         barrier);
+//   SS 3: half the MFMAs, the barrier (step t + 1 is in LDS, step t's reads are
+//         done), then the operand reads of SS 0 of step t + 1.
+// Each group (side operations + one MFMA) is fenced with a scheduling barrier so
+// the compiler keeps this order and only two operand sets are live.
+#ifndef MOE_RS_ST_SS
+#define MOE_RS_ST_SS 2
+#endif
+#ifndef MOE_RS_LD_SPLIT
+#define MOE_RS_LD_SPLIT 1  // global loads over substeps 0 and 1
+#endif
+template <int MODE, int SS, int S, int NA, int NRB, bool LOAD, bool STORE, bool NEXT>
+__device__ __forceinline__ void rs_substep(f32x16 (&acc)[RWMB][RWNB], RsRegs (&R)[2], RsOps (&op)[2],
+                                           const RsSrc& src, u32x4* L0, u32x4* L1, int t, int wr,
+                                           const int (&ra)[4], const int (&rb)[4]) {
+  constexpr int M = NRB * RWNB;                  // MFMAs
+  constexpr int NOP = NRB > 0 ? NRB + RWNB : 0;  // operand reads per substep
+  constexpr int NLD = NA + RNBL;                 // global loads (and LDS stores) per K step
+  constexpr int ld0 = !LOAD ? 0 : (MOE_RS_LD_SPLIT ? (SS == 0 ? 0 : NLD / 2) : 0);
+  constexpr int n_gl = !LOAD ? 0 : (MOE_RS_LD_SPLIT ? (SS == 0 ? NLD / 2 : SS == 1 ? NLD - NLD / 2 : 0)
+                                                    : (SS == 0 ? NLD : 0));
+  constexpr int n_rd = SS < 3 ? NOP : (NEXT ? NOP : 0);
+  constexpr int n_st = (SS == MOE_RS_ST_SS && STORE) ? NLD : 0;
+  constexpr bool BAR = SS == 3 && NEXT;
+  // before the barrier (substep 3 only): the LDS stores if they belong here
+  constexpr int P_pre = BAR ? n_st : 0;
+  constexpr int P = n_gl + n_rd + n_st - P_pre;  // side operations after the barrier (or all)
+  constexpr int M0 = BAR ? M / 2 : 0;            // MFMAs before the barrier
+  const u32x4* Lc = S == 0 ? L0 : L1;
+  u32x4* Ln = S == 0 ? L1 : L0;
+  const u32x4* Lr = SS < 3 ? Lc : Ln;            // buffer of the operands read here
+  constexpr int sr = (SS + 1) & 3;               // substep they belong to
+  RsOps& cur = op[SS & 1];
+  RsOps& nxt = op[(SS & 1) ^ 1];
+
+  // order: global loads, operand reads, LDS stores (stores of substep 3 before its barrier)
+  auto side = [&](int q) {
+    if (q < n_gl) rs_load1<MODE, NA>(R[S], src, t + 2, ld0 + q);
+    else if (q < n_gl + n_rd) rs_read1(nxt, Lr, ra, rb, sr, q - n_gl);
+    else rs_store1<NA>(R[1 - S], Ln, wr, q - n_gl - n_rd);
+  };
+  auto side_pre = [&](int q) { rs_store1<NA>(R[1 - S], Ln, wr, q); };
+  auto mfma = [&](int m) {
+    const int ai = m / RWNB, ni = m % RWNB;
+    acc[ai][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[ai], cur.b[ni], acc[ai][ni], 0, 0, 0);
+  };
+
+  if constexpr (BAR) {
+    if constexpr (M0 == 0) {
+#pragma unroll
+      for (int q = 0; q < P_pre; ++q) side_pre(q);
+    } else {
+      constexpr int PPM0 = (P_pre + M0 - 1) / M0;
+#pragma unroll
+      for (int m = 0; m < M0; ++m) {
+#pragma unroll
+        for (int j = 0; j < PPM0; ++j) {
+          const int q = m * P_pre / M0 + j;
+          if (q < (m + 1) * P_pre / M0) side_pre(q);
+        }
+        mfma(m);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    rs_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  constexpr int MR = M - M0;  // MFMAs that carry the side operations
+  if constexpr (MR == 0) {
+#pragma unroll
+    for (int q = 0; q < P; ++q) side(q);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    constexpr int PPM = (P + MR - 1) / MR;  // side operations per MFMA, at most
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+#pragma unroll
+      for (int j = 0; j < PPM; ++j) {  // constant trip count: fully unrolled, q is a constant
+        const int q = m * P / MR + j;
+        if (q < (m + 1) * P / MR) side(q);
+      }
+      mfma(M0 + m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <int MODE, int S, int NA, int NRB, bool LOAD, bool STORE, bool NEXT>
+__device__ __forceinline__ void rs_step(f32x16 (&acc)[RWMB][RWNB], RsRegs (&R)[2], RsOps (&op)[2], const RsSrc& src,
+                                        u32x4* L0, u32x4* L1, int t, int wr, const int (&ra)[4],
+                                        const int (&rb)[4]) {
+  rs_substep<MODE, 0, S, NA, NRB, LOAD, STORE, NEXT>(acc, R, op, src, L0, L1, t, wr, ra, rb);
+  rs_substep<MODE, 1, S, NA, NRB, LOAD, STORE, NEXT>(acc, R, op, src, L0, L1, t, wr, ra, rb);
+  rs_substep<MODE, 2, S, NA, NRB, LOAD, STORE, NEXT>(acc, R, op, src, L0, L1, t, wr, ra, rb);
+  rs_substep<MODE, 3, S, NA, NRB, LOAD, STORE, NEXT>(acc, R, op, src, L0, L1, t, wr, ra, rb);
+}
+
+// The K loop: nk >= 2 steps, nk odd iff ODD (the tail is then one straight
+// sequence, so no accumulator state merges across branches).
+template <int MODE, int NA, int NRB, bool ODD>
+__device__ __forceinline__ void rs_kloop(f32x16 (&acc)[RWMB][RWNB], const RsSrc& src, u32x4* L0, u32x4* L1, int nk,
+                                         int wr, const int (&ra)[4], const int (&rb)[4]) {
+  RsRegs R[2];
+  RsOps op[2];
+#pragma unroll
+  for (int q = 0; q < NA + RNBL; ++q) rs_load1<MODE, NA>(R[0], src, 0, q);
+#pragma unroll
+  for (int q = 0; q < NA + RNBL; ++q) rs_load1<MODE, NA>(R[1], src, 1, q);
+#pragma unroll
+  for (int q = 0; q < NA + RNBL; ++q) rs_store1<NA>(R[0], L0, wr, q);
+  rs_barrier();
+  if constexpr (NRB > 0) {
+#pragma unroll
+    for (int q = 0; q < NRB + RWNB; ++q) rs_read1(op[0], L0, ra, rb, 0, q);
+  }
+  constexpr int TAIL = ODD ? 3 : 2;  // steps after the loop, the first in buffer 0
+  int t = 0;
+  for (; t + TAIL < nk; t += 2) {
+    rs_step<MODE, 0, NA, NRB, true, true, true>(acc, R, op, src, L0, L1, t, wr, ra, rb);
+    rs_step<MODE, 1, NA, NRB, true, true, true>(acc, R, op, src, L0, L1, t + 1, wr, ra, rb);
+  }
+  if constexpr (ODD) {
+    rs_step<MODE, 0, NA, NRB, true, true, true>(acc, R, op, src, L0, L1, t, wr, ra, rb);
+    rs_step<MODE, 1, NA, NRB, false, true, true>(acc, R, op, src, L0, L1, t + 1, wr, ra, rb);
+    rs_step<MODE, 0, NA, NRB, false, false, false>(acc, R, op, src, L0, L1, t + 2, wr, ra, rb);
+  } else {
+    rs_step<MODE, 0, NA, NRB, false, true, true>(acc, R, op, src, L0, L1, t, wr, ra, rb);
+    rs_step<MODE, 1, NA, NRB, false, false, false>(acc, R, op, src, L0, L1, t + 1, wr, ra, rb);
+  }
+}
+
+// K loop and epilogue of one wave; NA A blocks are fetched for the workgroup,
+// this wave multiplies NRB row blocks (tile rows (2a + wm) * 32 .. + 32).
+template <int MODE, int NA, int NRB, bool ODD>
+__device__ __forceinline__ void rs_wave(const GemmArgs& a, const Chunk& ch, int nt, const RsSrc& src, u32x4* L0,
+                                        u32x4* L1, int wm, int wn, int lane, int wr) {
+  const int64_t N = a.N;
+  const int nk = (int)(a.K / RBK);
+  int ra[4], rb[4];
+  const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = (2 * s + h) ^ rswz(l32);
+    ra[s] = (wm * 32 + l32) * 8 + c;
+    rb[s] = (RBM + wn * 128 + l32) * 8 + c;
+  }
+  f32x16 acc[RWMB][RWNB];
+#pragma unroll
+  for (int i = 0; i < RWMB; ++i)
+#pragma unroll
+    for (int j = 0; j < RWNB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  rs_kloop<MODE, NA, NRB, ODD>(acc, src, L0, L1, nk, wr, ra, rb);
+
+  // ---- epilogue ----
+  // Lane holds column l32 and rows 8g + 4h + q (g, q < 4) of each 32 x 32 block.
+  // Each row block goes through a wave-private LDS region (32 KB per wave, free
+  // once every wave is past the K loop): lane pairs swap one value so each lane
+  // writes two adjacent columns as one dword, then rows leave as 16-byte stores.
+  rs_barrier();
+  if constexpr (NRB > 0) {
+    constexpr int NJ = MODE == MODE_GATEUP ? RWNB / 2 : RWNB;  // 32-column output blocks of this wave
+    constexpr int LDSR = NJ * 32 + 8;                           // padded LDS row (elements)
+    constexpr int CPRW = NJ * 4;                                // 16-byte chunks per output row
+    static_assert(32 * LDSR * 2 <= 32 * 1024, "epilogue region");
+    uint16_t* tile = reinterpret_cast<uint16_t*>(L0) + (wm + 2 * wn) * (32 * 1024 / 2);
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    const int64_t n0 = MODE == MODE_GATEUP ? (int64_t)nt * 128 + wn * 64 : (int64_t)nt * RBN + wn * 128;
+    const bool odd = l32 & 1;
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int p = 0; p < 4; p += 2) {
+            float va, vb;
+            if (MODE == MODE_GATEUP) {
+              va = silu_f(acc[i][jj][4 * g + p]) * acc[i][jj + 2][4 * g + p];
+              vb = silu_f(acc[i][jj][4 * g + p + 1]) * acc[i][jj + 2][4 * g + p + 1];
+            } else {
+              va = acc[i][jj][4 * g + p];
+              vb = acc[i][jj][4 * g + p + 1];
+            }
+            // even lane: (row ra, cols c, c+1); odd lane: (row ra+1, cols c-1, c)
+            const float x = __shfl_xor(odd ? va : vb, 1, kWave);
+            const int r = 8 * g + 4 * h + p;
+            const uint32_t w = odd ? ((uint32_t)f32_to_bf16(x) | ((uint32_t)f32_to_bf16(vb) << 16))
+                                   : ((uint32_t)f32_to_bf16(va) | ((uint32_t)f32_to_bf16(x) << 16));
+            const int lr = odd ? r + 1 : r;
+            *reinterpret_cast<uint32_t*>(tile + lr * LDSR + jj * 32 + (l32 & ~1)) = w;
+          }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+      const int rowb = (2 * i + wm) * 32;
+#pragma unroll
+      for (int q = 0; q < 32 * CPRW / kWave; ++q) {
+        const int idx = q * kWave + lane;
+        const int lr = idx / CPRW, c16 = idx % CPRW;
+        const int row = rowb + lr;
+        const int64_t n = n0 + c16 * 8;
+        if (row < ch.nrows && n < N)
+          *reinterpret_cast<uint4*>(out + ((int64_t)ch.row0 + row) * N + n) =
+              *reinterpret_cast<const uint4*>(tile + lr * LDSR + c16 * 8);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block overwrites the region
+    }
+  }
+}
+
+template <int MODE, int NA, bool ODD>
+__device__ __forceinline__ void rs_run(const GemmArgs& a, const Chunk& ch, int nt, u32x4* L0, u32x4* L1) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const bool shared = ch.group == a.E;
+  const int64_t K = a.K, N = a.N;
+
+  // loader: lane -> row (tid / 8) of each 32-row group, logical 16-byte chunk tid % 8
+  const int lrow = tid >> 3, lchunk = tid & 7;
+  const int wr = lrow * 8 + (lchunk ^ rswz(lrow));
+  RsSrc src;
+  src.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), (short)0, -1, kBufFlags);
+#pragma unroll
+  for (int i = 0; i < RNAL; ++i) {
+    const int rc = min(i * 32 + lrow, ch.nrows - 1);
+    const int64_t row = (int64_t)ch.row0 + rc;
+    int64_t sr = row;
+    if (a.gather != nullptr) sr = shared ? row - a.shared_row0 : (int64_t)a.gather[row];
+    src.aoff[i] = (uint32_t)((sr * K + lchunk * 8) * 2);  // A spans < 4 GiB (checked by the host)
+  }
+  const int64_t goff = shared ? 0 : (int64_t)ch.group * N * K;
+  const uint16_t* Wg = static_cast<const uint16_t*>(shared ? a.ws0 : a.w0) + goff;
+  const uint16_t* Wu = MODE == MODE_GATEUP ? static_cast<const uint16_t*>(shared ? a.ws1 : a.w1) + goff : Wg;
+  src.rg = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Wg), (short)0, -1, kBufFlags);
+  src.ru = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Wu), (short)0, -1, kBufFlags);
+#pragma unroll
+  for (int j = 0; j < RNBL; ++j) {
+    // B tile rows 32 j .. 32 j + 31; rows of wave column wn are [128 wn, 128 wn + 128)
+    int64_t n;
+    if (MODE == MODE_GATEUP)  // per wave column: 64 gate rows, then the same 64 up rows
+      n = (int64_t)nt * 128 + (j >> 2) * 64 + (j & 1) * 32;
+    else
+      n = (int64_t)nt * RBN + j * 32;
+    // a group past N is clamped to the last 32 rows (loaded, never stored); N is a multiple of 32
+    src.bgrp[j] = (uint32_t)(min(n, N - 32) * K * 2);
+  }
+  src.boff = (uint32_t)((lrow * K + lchunk * 8) * 2);
+
+  if (wm == 0) rs_wave<MODE, NA, (NA + 1) / 2, ODD>(a, ch, nt, src, L0, L1, wm, wn, lane, wr);
+  else rs_wave<MODE, NA, NA / 2, ODD>(a, ch, nt, src, L0, L1, wm, wn, lane, wr);
+}
+
+template <int MODE, bool ODD>
+__global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_rs(GemmArgs a, int n_tiles) {
+  __shared__ __attribute__((aligned(1024))) u32x4 lds[2 * RROWS * 8];
+  const int V = *a.n_chunks * n_tiles;
+  int L;
+  if (!xcd_map(blockIdx.x, V, L)) return;
+  int ci, nt;
+  tile_of(L, n_tiles, a.chunks, ci, nt);
+  const Chunk ch = a.chunks[ci];
+  u32x4* L0 = lds;
+  u32x4* L1 = lds + RROWS * 8;
+  switch ((ch.nrows + 31) / 32) {
+    case 1: rs_run<MODE, 1, ODD>(a, ch, nt, L0, L1); break;
+    case 2: rs_run<MODE, 2, ODD>(a, ch, nt, L0, L1); break;
+    case 3: rs_run<MODE, 3, ODD>(a, ch, nt, L0, L1); break;
+    case 4: rs_run<MODE, 4, ODD>(a, ch, nt, L0, L1); break;
+    case 5: rs_run<MODE, 5, ODD>(a, ch, nt, L0, L1); break;
+    case 6: rs_run<MODE, 6, ODD>(a, ch, nt, L0, L1); break;
+    case 7: rs_run<MODE, 7, ODD>(a, ch, nt, L0, L1); break;
+    default: rs_run<MODE, 8, ODD>(a, ch, nt, L0, L1); break;
+  }
+  static_assert(RNAL == 8, "row-block dispatch");
+}
+
+// The register-staged kernel takes a pass when it has at least two K steps and
+// its 32-bit buffer offsets cover A and one expert's weights (the chunk height
+// of the layer already says so; a pass it does not fit runs on the
+// direct-to-LDS kernel, which takes chunks of up to 320 rows).
+bool rs_fits(const GemmArgs& a) {
+  const int64_t lim = int64_t(1) << 32;
+  return a.K >= 2 * RBK && a.a_rows * a.K * 2 < lim && a.N * a.K * 2 < lim;
+}
+
 // ------------------------------------------------------ bf16 streaming path
 // Small batches (decode): every expert group has at most 16 rows, so the work is
 // streaming each touched expert's weights once.  One wave owns 16 output columns
@@ -587,6 +990,13 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
     const int n_wt = (int)(a.N / 16);
     const int64_t grid = (a.max_chunks * n_wt + SW - 1) / SW;
     hipLaunchKernelGGL(grouped_stream_bf16<MODE>, dim3((unsigned)grid), dim3(SW * 64), 0, s, a, n_wt);
+  } else if (dtype == MOE_BF16 && a.bm == RBM && rs_fits(a)) {
+    const int n_tiles = (int)(MODE == MODE_GATEUP ? (a.N + 127) / 128 : (a.N + RBN - 1) / RBN);
+    const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
+    if ((a.K / RBK) % 2)
+      hipLaunchKernelGGL((grouped_gemm_rs<MODE, true>), dim3((unsigned)grid), dim3(RNT), 0, s, a, n_tiles);
+    else
+      hipLaunchKernelGGL((grouped_gemm_rs<MODE, false>), dim3((unsigned)grid), dim3(RNT), 0, s, a, n_tiles);
   } else if (dtype == MOE_BF16) {
     const int n_tiles = (int)(MODE == MODE_GATEUP ? (a.N + 127) / 128 : (a.N + BN - 1) / BN);
     const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
