@@ -48,7 +48,7 @@ constexpr int64_t kGemvMaxT = 16;
 // 64.  For bf16 both MFMA kernels are eligible when the register-staged one's
 // limits hold (both contractions >= 128 long, 32-bit buffer offsets covering
 // x [T, H], the row space and h [rows, I]); a register-staged 256-row chunk
-// costs about 0.85 of a direct-to-LDS 320-row chunk (measured on the DeepSeek-V3,
+// costs about 0.88 of a direct-to-LDS 320-row chunk (measured on the DeepSeek-V3,
 // Mixtral and Switch shapes), so the 256-row tile is taken unless it needs
 // more chunks per group than that saves (a group of 257..320 rows: two
 // chunks instead of one).
@@ -61,7 +61,7 @@ inline int gemm_bm(const moe_config& c, int64_t rows, int64_t group_rows) {
   if (!fits) return kGemmBMdl;
   const int64_t g = std::max<int64_t>(group_rows, 1);
   const int64_t n_rs = (g + kGemmBMrs - 1) / kGemmBMrs, n_dl = (g + kGemmBMdl - 1) / kGemmBMdl;
-  return 17 * n_rs <= 20 * n_dl ? kGemmBMrs : kGemmBMdl;
+  return 22 * n_rs <= 25 * n_dl ? kGemmBMrs : kGemmBMdl;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -69,10 +69,19 @@ typedef __attribute__((address_space(1))) void glb_void;
 
 // One LDS array per pipeline stage: distinct objects let the compiler tell the
 // in-flight direct-to-LDS writes of one stage from the reads of another.
-__shared__ __attribute__((aligned(1024))) uint16_t sA0[BM_LD * BK];
-__shared__ __attribute__((aligned(1024))) uint16_t sA1[BM_LD * BK];
-__shared__ __attribute__((aligned(1024))) uint16_t sA2[STAGES > 2 ? BM_LD * BK : 8];
-__shared__ __attribute__((aligned(1024))) uint16_t sA3[STAGES > 3 ? BM_LD * BK : 8];
+#ifndef MOE_DL_A64
+#define MOE_DL_A64 1
+#endif
+// A64 mode: the A tile moves in 64-wide K steps (whole 128-byte lines) through
+// two stages of BM x 64, the B tile in 32-wide steps through four stages.
+constexpr int A64 = MOE_DL_A64 && BK == 32;
+constexpr int A64_BLK = BM / 8 / NWAVES;  // 1 KB blocks of 8 rows x 128 B per wave per A stage (5)
+static_assert(!A64 || A64_BLK * 8 * NWAVES == BM, "A64 staging");
+static_assert(!A64 || 2 * BM * 64 * 2 + 4 * BN * 32 * 2 <= 160 * 1024, "A64 LDS");
+__shared__ __attribute__((aligned(1024))) uint16_t sA0[A64 ? BM * 64 : BM_LD * BK];
+__shared__ __attribute__((aligned(1024))) uint16_t sA1[A64 ? BM * 64 : BM_LD * BK];
+__shared__ __attribute__((aligned(1024))) uint16_t sA2[!A64 && STAGES > 2 ? BM_LD * BK : 8];
+__shared__ __attribute__((aligned(1024))) uint16_t sA3[!A64 && STAGES > 3 ? BM_LD * BK : 8];
 __shared__ __attribute__((aligned(1024))) uint16_t sB0[BN * BK];
 __shared__ __attribute__((aligned(1024))) uint16_t sB1[BN * BK];
 __shared__ __attribute__((aligned(1024))) uint16_t sB2[STAGES > 2 ? BN * BK : 8];
@@ -140,7 +149,7 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 struct Frag {
-  const uint16_t* ga[A_BLK];  // per-lane global source of each direct-to-LDS block
+  const uint16_t* ga[A64 ? A64_BLK : A_BLK];  // per-lane global source of each direct-to-LDS block
   const uint16_t* gb[B_BLK];
 };
 
@@ -224,6 +233,93 @@ __device__ __forceinline__ void k_loop(const Frag& f, f32x16 (&acc)[RB][2], int 
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
 }
 
+// ---- A64 mode ----
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }  // 8 chunks per 128-byte row
+
+// A tile at = k / 64 into A stage SA: block i of this wave holds rows
+// (wave * A64_BLK + i) * 8 .. + 8, whole 128-byte row pieces.
+template <int SA>
+__device__ __forceinline__ void issue_a64(const Frag& f, int at, int wave) {
+#pragma unroll
+  for (int i = 0; i < A64_BLK; ++i)
+    __builtin_amdgcn_global_load_lds((glb_void*)(f.ga[i] + at * 64),
+                                     (lds_void*)(stA<SA>() + (wave * A64_BLK + i) * 512), 16, 0, 0);
+}
+template <int SB>
+__device__ __forceinline__ void issue_b32(const Frag& f, int kt, int wave) {
+#pragma unroll
+  for (int i = 0; i < B_BLK; ++i)
+    __builtin_amdgcn_global_load_lds((glb_void*)(f.gb[i] + kt * BK), (lds_void*)(stB<SB>() + (wave * B_BLK + i) * 512),
+                                     16, 0, MOE_DL_B_AUX);
+}
+
+// One 32-wide K step: A from half HALF of A stage SA (128-byte rows), B from B
+// stage SB (64-byte rows).
+template <int SA, int HALF, int SB, int NRB>
+__device__ __forceinline__ void compute_a64(f32x16 (&acc)[RB][2], int wrow0, const int (&brow)[2], int lane) {
+  const uint16_t* Ab = stA<SA>();
+  const uint16_t* Bb = stB<SB>();
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int cb = s * 2 + (lane >> 5);
+    const int ca = HALF * 4 + cb;
+    bf16x8 bv[2], av[NRB];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = brow[j];
+      bv[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bb + r * BK + ((cb ^ swz(r)) * 8)));
+    }
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      const int r = wrow0 + i * 32 + (lane & 31);
+      av[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ab + r * 64 + ((ca ^ swz8(r)) * 8)));
+    }
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// K step kt (S = kt % 4, in B stage S and A stage (S / 2) % 2, half S % 2).
+// Issue order per step: B step kt + 3 (B_BLK loads), then on even steps A tile
+// kt / 2 + 1 (A64_BLK loads), all clamped so every step issues the same.  At the
+// barrier of an even step only B step kt + 2 may be outstanding beyond what it
+// needs (B step kt and A tile kt / 2); at an odd step B step kt was issued
+// before one A tile, two B steps and another A tile.
+template <int S, int NRB>
+__device__ __forceinline__ void pipe_step_a64(const Frag& f, f32x16 (&acc)[RB][2], int kt, int nk, int wrow0,
+                                              const int (&brow)[2], int lane, int wave) {
+  stage_barrier<(S % 2 == 0) ? B_BLK : 2 * B_BLK + 2 * A64_BLK>();
+  issue_b32<(S + 3) % 4>(f, min(kt + 3, nk - 1), wave);
+  if constexpr (S % 2 == 0) issue_a64<((S / 2) + 1) % 2>(f, min(kt / 2 + 1, nk / 2 - 1), wave);
+  if constexpr (NRB > 0) compute_a64<(S / 2) % 2, S % 2, S, NRB>(acc, wrow0, brow, lane);
+}
+
+// nk (32-wide steps) is even: K is a multiple of 64.
+template <int NRB>
+__device__ __forceinline__ void k_loop_a64(const Frag& f, f32x16 (&acc)[RB][2], int nk, int wrow0,
+                                           const int (&brow)[2], int lane, int wave) {
+  // the issues of steps -3, -2, -1: B 0; B 1, A 0; B 2
+  issue_b32<0>(f, 0, wave);
+  issue_b32<1>(f, min(1, nk - 1), wave);
+  issue_a64<0>(f, 0, wave);
+  issue_b32<2>(f, min(2, nk - 1), wave);
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
+    pipe_step_a64<0, NRB>(f, acc, kt, nk, wrow0, brow, lane, wave);
+    pipe_step_a64<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
+    pipe_step_a64<2, NRB>(f, acc, kt + 2, nk, wrow0, brow, lane, wave);
+    pipe_step_a64<3, NRB>(f, acc, kt + 3, nk, wrow0, brow, lane, wave);
+  }
+  if (kt < nk) {  // two steps left
+    pipe_step_a64<0, NRB>(f, acc, kt, nk, wrow0, brow, lane, wave);
+    pipe_step_a64<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): the clamped refills land before the wave retires
+}
+
 template <int MODE>
 __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles) {
   const int V = *a.n_chunks * n_tiles;
@@ -244,15 +340,28 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
   // the chunk are clamped to its last row (loaded, never used).
   Frag f;
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
+  if constexpr (A64) {  // A blocks of 8 rows x 128 B: lane -> row lane / 8, physical chunk lane % 8
 #pragma unroll
-  for (int i = 0; i < A_BLK; ++i) {
-    const int r = (wave * A_BLK + i) * RPB + lane / CPR;
-    const int c = (lane % CPR) ^ swz(r);
-    const int rc = min(r, ch.nrows - 1);
-    const int64_t row = (int64_t)ch.row0 + rc;
-    int64_t src = row;
-    if (a.gather != nullptr) src = shared ? row - a.shared_row0 : (int64_t)a.gather[row];
-    f.ga[i] = A + src * K + c * 8;
+    for (int i = 0; i < A64_BLK; ++i) {
+      const int r = (wave * A64_BLK + i) * 8 + lane / 8;
+      const int c = (lane % 8) ^ swz8(r);
+      const int rc = min(r, ch.nrows - 1);
+      const int64_t row = (int64_t)ch.row0 + rc;
+      int64_t src = row;
+      if (a.gather != nullptr) src = shared ? row - a.shared_row0 : (int64_t)a.gather[row];
+      f.ga[i] = A + src * K + c * 8;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < A_BLK; ++i) {
+      const int r = (wave * A_BLK + i) * RPB + lane / CPR;
+      const int c = (lane % CPR) ^ swz(r);
+      const int rc = min(r, ch.nrows - 1);
+      const int64_t row = (int64_t)ch.row0 + rc;
+      int64_t src = row;
+      if (a.gather != nullptr) src = shared ? row - a.shared_row0 : (int64_t)a.gather[row];
+      f.ga[i] = A + src * K + c * 8;
+    }
   }
   const int64_t goff = shared ? 0 : (int64_t)ch.group * N * K;
 #pragma unroll
@@ -294,13 +403,24 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
   }
 
   const int nk = (int)(K / BK);
-  switch (nrb) {
-    case 0: k_loop<0>(f, acc, nk, wrow0, brow, lane, wave); break;
-    case 1: k_loop<1>(f, acc, nk, wrow0, brow, lane, wave); break;
-    case 2: k_loop<2>(f, acc, nk, wrow0, brow, lane, wave); break;
-    case 3: k_loop<3>(f, acc, nk, wrow0, brow, lane, wave); break;
-    case 4: k_loop<4>(f, acc, nk, wrow0, brow, lane, wave); break;
-    default: k_loop<5>(f, acc, nk, wrow0, brow, lane, wave); break;
+  if constexpr (A64) {
+    switch (nrb) {
+      case 0: k_loop_a64<0>(f, acc, nk, wrow0, brow, lane, wave); break;
+      case 1: k_loop_a64<1>(f, acc, nk, wrow0, brow, lane, wave); break;
+      case 2: k_loop_a64<2>(f, acc, nk, wrow0, brow, lane, wave); break;
+      case 3: k_loop_a64<3>(f, acc, nk, wrow0, brow, lane, wave); break;
+      case 4: k_loop_a64<4>(f, acc, nk, wrow0, brow, lane, wave); break;
+      default: k_loop_a64<5>(f, acc, nk, wrow0, brow, lane, wave); break;
+    }
+  } else {
+    switch (nrb) {
+      case 0: k_loop<0>(f, acc, nk, wrow0, brow, lane, wave); break;
+      case 1: k_loop<1>(f, acc, nk, wrow0, brow, lane, wave); break;
+      case 2: k_loop<2>(f, acc, nk, wrow0, brow, lane, wave); break;
+      case 3: k_loop<3>(f, acc, nk, wrow0, brow, lane, wave); break;
+      case 4: k_loop<4>(f, acc, nk, wrow0, brow, lane, wave); break;
+      default: k_loop<5>(f, acc, nk, wrow0, brow, lane, wave); break;
+    }
   }
   static_assert(RB == 5, "k_loop dispatch");
 
@@ -318,11 +438,11 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
     constexpr int PB = 3;                            // row blocks per pass
     static_assert(PB * 32 * LDSR * 2 <= BN * BK * 2, "epilogue pass fits a stage buffer");
     uint16_t* tile;
-    switch (wave) {
+    switch (wave) {  // A64 mode: the two A stages are split in halves for waves 0-3
       case 0: tile = sA0; break;
-      case 1: tile = sA1; break;
-      case 2: tile = sA2; break;
-      case 3: tile = sA3; break;
+      case 1: tile = A64 ? sA0 + BM * 32 : sA1; break;
+      case 2: tile = A64 ? sA1 : sA2; break;
+      case 3: tile = A64 ? sA1 + BM * 32 : sA3; break;
       case 4: tile = sB0; break;
       case 5: tile = sB1; break;
       case 6: tile = sB2; break;
