@@ -14,18 +14,20 @@
 // device-side tile count exit at once, so the grid is sized on the host for the
 // worst case and no host synchronisation is needed.
 //
-// bf16 tile: BM = 320 rows x BN = 256 weight rows x BK = 32, eight waves (two
-// per SIMD) in a 2 x 4 grid, each wave up to 160 x 64 of v_mfma_f32_32x32x16_bf16
+// 320-row bf16 tile: BM = 320 rows x BN = 256 weight rows, eight waves (two per
+// SIMD) in a 2 x 4 grid, each wave up to 160 x 64 of v_mfma_f32_32x32x16_bf16
 // (fp32 accumulators).  A 320-row chunk holds a whole routed expert of the large
-// workloads, so each expert's weights stream through one workgroup per n-tile.  Gate/up pass: the 256 weight rows are 128 gate rows and
-// the same 128 up rows; every wave owns 32 gate columns and the matching 32 up
-// columns, so each lane holds gate and up of the same (row, i) and applies
-// silu(g) * u in registers.  Down pass: 256 output columns.  The A tile is
-// gathered straight from x through token_of_row (the gather of the dispatch step
-// is fused into this loader).  Both tiles move global -> LDS with direct
-// (global_load_lds_dwordx4) loads through a four-stage pipeline, with 16-byte
-// chunks XOR-swizzled by row so the MFMA operand reads are free of bank
-// conflicts.
+// workloads, so each expert's weights stream through one workgroup per n-tile.
+// Gate/up pass: the 256 weight rows are 128 gate rows and the same 128 up rows;
+// every wave owns 32 gate columns and the matching 32 up columns, so each lane
+// holds gate and up of the same (row, i) and applies silu(g) * u in registers.
+// Down pass: 256 output columns.  The A tile is gathered straight from x
+// through token_of_row (the gather of the dispatch step is fused into this
+// loader).  Both tiles move global -> LDS with direct (global_load_lds_dwordx4)
+// loads: A (token rows, from L2) in 64-wide K steps, whole 128-byte lines,
+// through two stages, one step ahead; B (weights, from HBM) in 32-wide K steps
+// through four stages, three steps ahead.  The 16-byte chunks of each LDS row
+// are XOR-swizzled by row so the MFMA operand reads are free of bank conflicts.
 //
 // Tile order: within one expert the chunks of an n-tile are adjacent (groups of
 // up to four chunks), so a second row chunk of an expert reads the same weight
@@ -38,29 +40,17 @@ namespace moe {
 namespace {
 
 constexpr int BM = kGemmBMdl;  // 320 rows: one chunk holds a whole routed expert of the large workloads
-constexpr int BMW = BM / 2;  // rows per wave-row
-constexpr int RB = BMW / 32; // 32-row MFMA blocks per wave (5)
+constexpr int BMW = BM / 2;    // rows per wave-row
+constexpr int RB = BMW / 32;   // 32-row MFMA blocks per wave (5)
 constexpr int BN = 256;
 constexpr int NT = 512;
 constexpr int NWAVES = NT / 64;
-constexpr int SUPER = 4;     // chunks of one group interleaved per n-tile
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 32
-#endif
-constexpr int BK = MOE_GEMM_BK;
-#ifndef MOE_DL_B_AUX
-#define MOE_DL_B_AUX 0
-#endif
-constexpr int STAGES = BK == 64 ? 2 : 4;     // LDS: 2 x (320 + 256) x 128 B or 4 x (384 + 256) x 64 B
-constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row
-constexpr int RPB = 64 / CPR;               // tile rows per 1 KB direct-to-LDS block
-constexpr int A_BLK = (BM + NWAVES * RPB - 1) / (NWAVES * RPB);  // A blocks per wave per stage
-constexpr int BM_LD = NWAVES * A_BLK * RPB; // A rows staged per stage (rows >= BM are never read)
-constexpr int B_BLK = BN / RPB / NWAVES;
-constexpr int LOADS_PER_STAGE = A_BLK + B_BLK;
-static_assert(BK == 32 || BK == 64, "BK");
-static_assert(BM_LD >= BM && BM % 32 == 0, "A staging");
-static_assert(STAGES * (BM_LD + BN) * BK * 2 <= 160 * 1024, "LDS");
+constexpr int SUPER = 4;       // chunks of one group interleaved per n-tile
+constexpr int BK = 32;         // K per step (and per B stage)
+constexpr int B_BLK = BN / 16 / NWAVES;   // B blocks (16 rows x 64 B = 1 KB) per wave per stage (2)
+constexpr int A_BLK = BM / 8 / NWAVES;    // A blocks (8 rows x 128 B = 1 KB) per wave per 64-wide A stage (5)
+static_assert(A_BLK * 8 * NWAVES == BM && B_BLK * 16 * NWAVES == BN, "staging");
+static_assert(2 * BM * 64 * 2 + 4 * BN * BK * 2 <= 160 * 1024, "LDS");
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 
@@ -69,30 +59,17 @@ typedef __attribute__((address_space(1))) void glb_void;
 
 // One LDS array per pipeline stage: distinct objects let the compiler tell the
 // in-flight direct-to-LDS writes of one stage from the reads of another.
-#ifndef MOE_DL_A64
-#define MOE_DL_A64 1
-#endif
-// A64 mode: the A tile moves in 64-wide K steps (whole 128-byte lines) through
-// two stages of BM x 64, the B tile in 32-wide steps through four stages.
-constexpr int A64 = MOE_DL_A64 && BK == 32;
-constexpr int A64_BLK = BM / 8 / NWAVES;  // 1 KB blocks of 8 rows x 128 B per wave per A stage (5)
-static_assert(!A64 || A64_BLK * 8 * NWAVES == BM, "A64 staging");
-static_assert(!A64 || 2 * BM * 64 * 2 + 4 * BN * 32 * 2 <= 160 * 1024, "A64 LDS");
-__shared__ __attribute__((aligned(1024))) uint16_t sA0[A64 ? BM * 64 : BM_LD * BK];
-__shared__ __attribute__((aligned(1024))) uint16_t sA1[A64 ? BM * 64 : BM_LD * BK];
-__shared__ __attribute__((aligned(1024))) uint16_t sA2[!A64 && STAGES > 2 ? BM_LD * BK : 8];
-__shared__ __attribute__((aligned(1024))) uint16_t sA3[!A64 && STAGES > 3 ? BM_LD * BK : 8];
+__shared__ __attribute__((aligned(1024))) uint16_t sA0[BM * 64];
+__shared__ __attribute__((aligned(1024))) uint16_t sA1[BM * 64];
 __shared__ __attribute__((aligned(1024))) uint16_t sB0[BN * BK];
 __shared__ __attribute__((aligned(1024))) uint16_t sB1[BN * BK];
-__shared__ __attribute__((aligned(1024))) uint16_t sB2[STAGES > 2 ? BN * BK : 8];
-__shared__ __attribute__((aligned(1024))) uint16_t sB3[STAGES > 3 ? BN * BK : 8];
+__shared__ __attribute__((aligned(1024))) uint16_t sB2[BN * BK];
+__shared__ __attribute__((aligned(1024))) uint16_t sB3[BN * BK];
 
 template <int S>
 __device__ __forceinline__ uint16_t* stA() {
   if constexpr (S == 0) return sA0;
-  else if constexpr (S == 1) return sA1;
-  else if constexpr (S == 2) return sA2;
-  else return sA3;
+  else return sA1;
 }
 template <int S>
 __device__ __forceinline__ uint16_t* stB() {
@@ -102,13 +79,11 @@ __device__ __forceinline__ uint16_t* stB() {
   else return sB3;
 }
 
-// XOR swizzle of the 16-byte chunks of a tile row: the 16 lanes of one
+// XOR swizzles of the 16-byte chunks of a tile row: the 16 lanes of one
 // ds_read_b128 cycle (rows r..r+15, one logical chunk) hit distinct banks on a
 // 64-bank LDS, and the 8 lanes of a 32-bank cycle do too.
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);  // 8 chunks per 128-byte row
-  else return ((r >> 1) ^ (r >> 2)) & 3;                     // 4 chunks per 64-byte row
-}
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }  // 4 chunks per 64-byte row
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }   // 8 chunks per 128-byte row
 
 // Physical workgroup id -> logical tile id, XCD-contiguous; false past V.
 __device__ __forceinline__ bool xcd_map(int p, int V, int& L) {
@@ -149,125 +124,44 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 struct Frag {
-  const uint16_t* ga[A64 ? A64_BLK : A_BLK];  // per-lane global source of each direct-to-LDS block
+  const uint16_t* ga[A_BLK];  // per-lane global source of each direct-to-LDS block
   const uint16_t* gb[B_BLK];
 };
 
-template <int S>
-__device__ __forceinline__ void issue_stage(const Frag& f, int kt, int wave) {
-  const int ko = kt * BK;
+// A tile at (K offset 64 at) into A stage SA: block i of this wave holds rows
+// (wave * A_BLK + i) * 8 .. + 8, whole 128-byte row pieces.
+template <int SA>
+__device__ __forceinline__ void issue_a(const Frag& f, int at, int wave) {
 #pragma unroll
   for (int i = 0; i < A_BLK; ++i)
-    __builtin_amdgcn_global_load_lds((glb_void*)(f.ga[i] + ko), (lds_void*)(stA<S>() + (wave * A_BLK + i) * 512),
+    __builtin_amdgcn_global_load_lds((glb_void*)(f.ga[i] + at * 64), (lds_void*)(stA<SA>() + (wave * A_BLK + i) * 512),
                                      16, 0, 0);
-#pragma unroll
-  for (int i = 0; i < B_BLK; ++i)
-    __builtin_amdgcn_global_load_lds((glb_void*)(f.gb[i] + ko), (lds_void*)(stB<S>() + (wave * B_BLK + i) * 512),
-                                     16, 0, MOE_DL_B_AUX);
 }
-
-// NRB 32-row blocks x two 32-column blocks of this wave, one K step.
-template <int S, int NRB>
-__device__ __forceinline__ void compute_stage(f32x16 (&acc)[RB][2], int wrow0, const int (&brow)[2], int lane) {
-  const uint16_t* Ab = stA<S>();
-  const uint16_t* Bb = stB<S>();
-#pragma unroll
-  for (int s = 0; s < BK / 16; ++s) {
-    const int chunk = s * 2 + (lane >> 5);  // k = s*16 + (lane>>5)*8 .. +8
-    bf16x8 bv[2], av[NRB];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = brow[j];
-      bv[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bb + r * BK + ((chunk ^ swz(r)) * 8)));
-    }
-#pragma unroll
-    for (int i = 0; i < NRB; ++i) {
-      const int r = wrow0 + i * 32 + (lane & 31);
-      av[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ab + r * BK + ((chunk ^ swz(r)) * 8)));
-    }
-#pragma unroll
-    for (int i = 0; i < NRB; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-// One pipeline step for k-step kt held in stage S: wait for its data, refill the
-// stage consumed one step earlier with k-step kt + STAGES - 1 (clamped to the
-// last k-step: every step issues exactly one stage of loads, so the number of
-// loads issued after k-step kt is always (STAGES - 2) stages and the wait count
-// is a constant), then compute.  Loads complete in issue order.
-template <int S, int NRB>
-__device__ __forceinline__ void pipe_step(const Frag& f, f32x16 (&acc)[RB][2], int kt, int nk, int wrow0,
-                                          const int (&brow)[2], int lane, int wave) {
-  stage_barrier<(STAGES > 2 ? STAGES - 2 : 0) * LOADS_PER_STAGE>();
-  issue_stage<(S + STAGES - 1) % STAGES>(f, min(kt + STAGES - 1, nk - 1), wave);
-  if constexpr (NRB > 0) compute_stage<S, NRB>(acc, wrow0, brow, lane);
-}
-
-// The pipelined K loop of one wave computing NRB row blocks.  Every variant runs
-// the same barriers and loads, so waves with different NRB stay in step.
-template <int NRB>
-__device__ __forceinline__ void k_loop(const Frag& f, f32x16 (&acc)[RB][2], int nk, int wrow0,
-                                       const int (&brow)[2], int lane, int wave) {
-  issue_stage<0>(f, 0, wave);
-  if constexpr (STAGES > 2) issue_stage<1>(f, min(1, nk - 1), wave);
-  if constexpr (STAGES > 3) issue_stage<2>(f, min(2, nk - 1), wave);
-  int kt = 0;
-  // whole groups of STAGES steps: no conditional memory traffic inside the loop
-  for (; kt + STAGES <= nk; kt += STAGES) {
-    pipe_step<0, NRB>(f, acc, kt, nk, wrow0, brow, lane, wave);
-    pipe_step<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
-    if constexpr (STAGES > 2) pipe_step<2, NRB>(f, acc, kt + 2, nk, wrow0, brow, lane, wave);
-    if constexpr (STAGES > 3) pipe_step<3, NRB>(f, acc, kt + 3, nk, wrow0, brow, lane, wave);
-  }
-  // tail (nk not a multiple of STAGES)
-  if (kt < nk) pipe_step<0, NRB>(f, acc, kt, nk, wrow0, brow, lane, wave);
-  if constexpr (STAGES > 2)
-    if (kt + 1 < nk) pipe_step<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
-  if constexpr (STAGES > 3)
-    if (kt + 2 < nk) pipe_step<2, NRB>(f, acc, kt + 2, nk, wrow0, brow, lane, wave);
-  // the clamped refills of the last steps are still in flight: let them land
-  // before the wave can retire
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
-}
-
-// ---- A64 mode ----
-__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }  // 8 chunks per 128-byte row
-
-// A tile at = k / 64 into A stage SA: block i of this wave holds rows
-// (wave * A64_BLK + i) * 8 .. + 8, whole 128-byte row pieces.
-template <int SA>
-__device__ __forceinline__ void issue_a64(const Frag& f, int at, int wave) {
-#pragma unroll
-  for (int i = 0; i < A64_BLK; ++i)
-    __builtin_amdgcn_global_load_lds((glb_void*)(f.ga[i] + at * 64),
-                                     (lds_void*)(stA<SA>() + (wave * A64_BLK + i) * 512), 16, 0, 0);
-}
+// B step kt (K offset 32 kt) into B stage SB: block i of this wave holds rows
+// (wave * B_BLK + i) * 16 .. + 16, 64-byte row pieces.
 template <int SB>
-__device__ __forceinline__ void issue_b32(const Frag& f, int kt, int wave) {
+__device__ __forceinline__ void issue_b(const Frag& f, int kt, int wave) {
 #pragma unroll
   for (int i = 0; i < B_BLK; ++i)
     __builtin_amdgcn_global_load_lds((glb_void*)(f.gb[i] + kt * BK), (lds_void*)(stB<SB>() + (wave * B_BLK + i) * 512),
-                                     16, 0, MOE_DL_B_AUX);
+                                     16, 0, 0);
 }
 
-// One 32-wide K step: A from half HALF of A stage SA (128-byte rows), B from B
-// stage SB (64-byte rows).
+// One 32-wide K step of this wave's NRB row blocks x two column blocks: A from
+// half HALF of A stage SA (128-byte rows), B from B stage SB (64-byte rows).
 template <int SA, int HALF, int SB, int NRB>
-__device__ __forceinline__ void compute_a64(f32x16 (&acc)[RB][2], int wrow0, const int (&brow)[2], int lane) {
+__device__ __forceinline__ void compute_step(f32x16 (&acc)[RB][2], int wrow0, const int (&brow)[2], int lane) {
   const uint16_t* Ab = stA<SA>();
   const uint16_t* Bb = stB<SB>();
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int cb = s * 2 + (lane >> 5);
+    const int cb = s * 2 + (lane >> 5);  // k = 16 s + 8 (lane >> 5) .. + 8 of the step
     const int ca = HALF * 4 + cb;
     bf16x8 bv[2], av[NRB];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int r = brow[j];
-      bv[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bb + r * BK + ((cb ^ swz(r)) * 8)));
+      bv[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Bb + r * BK + ((cb ^ swz4(r)) * 8)));
     }
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
@@ -282,42 +176,47 @@ __device__ __forceinline__ void compute_a64(f32x16 (&acc)[RB][2], int wrow0, con
   }
 }
 
-// K step kt (S = kt % 4, in B stage S and A stage (S / 2) % 2, half S % 2).
-// Issue order per step: B step kt + 3 (B_BLK loads), then on even steps A tile
-// kt / 2 + 1 (A64_BLK loads), all clamped so every step issues the same.  At the
-// barrier of an even step only B step kt + 2 may be outstanding beyond what it
-// needs (B step kt and A tile kt / 2); at an odd step B step kt was issued
-// before one A tile, two B steps and another A tile.
+// K step kt (S = kt % 4: B stage S, A stage (S / 2) % 2, half S % 2).  Issue
+// order per step: B step kt + 3 (B_BLK loads), then on even steps A tile
+// kt / 2 + 1 (A_BLK loads), all clamped so every step issues the same.  Loads
+// complete in issue order: at the barrier of an even step only B step kt + 2
+// may be outstanding beyond what it needs (B step kt and A tile kt / 2); at an
+// odd step B step kt was issued before one A tile, two B steps and another A
+// tile.
 template <int S, int NRB>
-__device__ __forceinline__ void pipe_step_a64(const Frag& f, f32x16 (&acc)[RB][2], int kt, int nk, int wrow0,
-                                              const int (&brow)[2], int lane, int wave) {
-  stage_barrier<(S % 2 == 0) ? B_BLK : 2 * B_BLK + 2 * A64_BLK>();
-  issue_b32<(S + 3) % 4>(f, min(kt + 3, nk - 1), wave);
-  if constexpr (S % 2 == 0) issue_a64<((S / 2) + 1) % 2>(f, min(kt / 2 + 1, nk / 2 - 1), wave);
-  if constexpr (NRB > 0) compute_a64<(S / 2) % 2, S % 2, S, NRB>(acc, wrow0, brow, lane);
+__device__ __forceinline__ void pipe_step(const Frag& f, f32x16 (&acc)[RB][2], int kt, int nk, int wrow0,
+                                          const int (&brow)[2], int lane, int wave) {
+  stage_barrier<(S % 2 == 0) ? B_BLK : 2 * B_BLK + 2 * A_BLK>();
+  issue_b<(S + 3) % 4>(f, min(kt + 3, nk - 1), wave);
+  if constexpr (S % 2 == 0) issue_a<((S / 2) + 1) % 2>(f, min(kt / 2 + 1, nk / 2 - 1), wave);
+  if constexpr (NRB > 0) compute_step<(S / 2) % 2, S % 2, S, NRB>(acc, wrow0, brow, lane);
 }
 
-// nk (32-wide steps) is even: K is a multiple of 64.
+// The pipelined K loop of one wave computing NRB row blocks; nk (32-wide steps)
+// is even, as K is a multiple of 64.  Every variant runs the same barriers and
+// loads, so waves with different NRB stay in step.
 template <int NRB>
-__device__ __forceinline__ void k_loop_a64(const Frag& f, f32x16 (&acc)[RB][2], int nk, int wrow0,
-                                           const int (&brow)[2], int lane, int wave) {
+__device__ __forceinline__ void k_loop(const Frag& f, f32x16 (&acc)[RB][2], int nk, int wrow0,
+                                       const int (&brow)[2], int lane, int wave) {
   // the issues of steps -3, -2, -1: B 0; B 1, A 0; B 2
-  issue_b32<0>(f, 0, wave);
-  issue_b32<1>(f, min(1, nk - 1), wave);
-  issue_a64<0>(f, 0, wave);
-  issue_b32<2>(f, min(2, nk - 1), wave);
+  issue_b<0>(f, 0, wave);
+  issue_b<1>(f, min(1, nk - 1), wave);
+  issue_a<0>(f, 0, wave);
+  issue_b<2>(f, min(2, nk - 1), wave);
   int kt = 0;
-  for (; kt + 4 <= nk; kt += 4) {
-    pipe_step_a64<0, NRB>(f, acc, kt, nk, wrow0, brow, lane, wave);
-    pipe_step_a64<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
-    pipe_step_a64<2, NRB>(f, acc, kt + 2, nk, wrow0, brow, lane, wave);
-    pipe_step_a64<3, NRB>(f, acc, kt + 3, nk, wrow0, brow, lane, wave);
+  for (; kt + 4 <= nk; kt += 4) {  // no conditional memory traffic inside the loop
+    pipe_step<0, NRB>(f, acc, kt, nk, wrow0, brow, lane, wave);
+    pipe_step<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
+    pipe_step<2, NRB>(f, acc, kt + 2, nk, wrow0, brow, lane, wave);
+    pipe_step<3, NRB>(f, acc, kt + 3, nk, wrow0, brow, lane, wave);
   }
   if (kt < nk) {  // two steps left
-    pipe_step_a64<0, NRB>(f, acc, kt, nk, wrow0, brow, lane, wave);
-    pipe_step_a64<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
+    pipe_step<0, NRB>(f, acc, kt, nk, wrow0, brow, lane, wave);
+    pipe_step<1, NRB>(f, acc, kt + 1, nk, wrow0, brow, lane, wave);
   }
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): the clamped refills land before the wave retires
+  // the clamped refills of the last steps are still in flight: let them land
+  // before the wave can retire
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
 }
 
 template <int MODE>
@@ -335,39 +234,28 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
   const int wm = wave >> 2, wn = wave & 3;
 
   // ---- per-lane sources of the direct-to-LDS blocks ----
-  // block b holds tile rows b*RPB .. +RPB; lane -> row b*RPB + lane/CPR, physical
-  // chunk lane%CPR, which holds logical chunk (lane%CPR) ^ swz(row).  Rows past
-  // the chunk are clamped to its last row (loaded, never used).
+  // A block i of this wave holds tile rows (wave * A_BLK + i) * 8 .. + 8: lane ->
+  // row lane / 8, physical chunk lane % 8, which holds logical chunk
+  // (lane % 8) ^ swz8(row).  B block i: rows (wave * B_BLK + i) * 16 .. + 16, lane
+  // -> row lane / 4, physical chunk lane % 4.  Rows past the chunk are clamped to
+  // its last row (loaded, never used).
   Frag f;
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
-  if constexpr (A64) {  // A blocks of 8 rows x 128 B: lane -> row lane / 8, physical chunk lane % 8
 #pragma unroll
-    for (int i = 0; i < A64_BLK; ++i) {
-      const int r = (wave * A64_BLK + i) * 8 + lane / 8;
-      const int c = (lane % 8) ^ swz8(r);
-      const int rc = min(r, ch.nrows - 1);
-      const int64_t row = (int64_t)ch.row0 + rc;
-      int64_t src = row;
-      if (a.gather != nullptr) src = shared ? row - a.shared_row0 : (int64_t)a.gather[row];
-      f.ga[i] = A + src * K + c * 8;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < A_BLK; ++i) {
-      const int r = (wave * A_BLK + i) * RPB + lane / CPR;
-      const int c = (lane % CPR) ^ swz(r);
-      const int rc = min(r, ch.nrows - 1);
-      const int64_t row = (int64_t)ch.row0 + rc;
-      int64_t src = row;
-      if (a.gather != nullptr) src = shared ? row - a.shared_row0 : (int64_t)a.gather[row];
-      f.ga[i] = A + src * K + c * 8;
-    }
+  for (int i = 0; i < A_BLK; ++i) {
+    const int r = (wave * A_BLK + i) * 8 + lane / 8;
+    const int c = (lane % 8) ^ swz8(r);
+    const int rc = min(r, ch.nrows - 1);
+    const int64_t row = (int64_t)ch.row0 + rc;
+    int64_t src = row;
+    if (a.gather != nullptr) src = shared ? row - a.shared_row0 : (int64_t)a.gather[row];
+    f.ga[i] = A + src * K + c * 8;
   }
   const int64_t goff = shared ? 0 : (int64_t)ch.group * N * K;
 #pragma unroll
   for (int i = 0; i < B_BLK; ++i) {
-    const int r = (wave * B_BLK + i) * RPB + lane / CPR;
-    const int c = (lane % CPR) ^ swz(r);
+    const int r = (wave * B_BLK + i) * 16 + lane / 4;
+    const int c = (lane % 4) ^ swz4(r);
     const uint16_t* W;
     int64_t n;
     if (MODE == MODE_GATEUP) {  // rows < 128: gate, >= 128: up, same 128 columns of I
@@ -403,24 +291,13 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
   }
 
   const int nk = (int)(K / BK);
-  if constexpr (A64) {
-    switch (nrb) {
-      case 0: k_loop_a64<0>(f, acc, nk, wrow0, brow, lane, wave); break;
-      case 1: k_loop_a64<1>(f, acc, nk, wrow0, brow, lane, wave); break;
-      case 2: k_loop_a64<2>(f, acc, nk, wrow0, brow, lane, wave); break;
-      case 3: k_loop_a64<3>(f, acc, nk, wrow0, brow, lane, wave); break;
-      case 4: k_loop_a64<4>(f, acc, nk, wrow0, brow, lane, wave); break;
-      default: k_loop_a64<5>(f, acc, nk, wrow0, brow, lane, wave); break;
-    }
-  } else {
-    switch (nrb) {
-      case 0: k_loop<0>(f, acc, nk, wrow0, brow, lane, wave); break;
-      case 1: k_loop<1>(f, acc, nk, wrow0, brow, lane, wave); break;
-      case 2: k_loop<2>(f, acc, nk, wrow0, brow, lane, wave); break;
-      case 3: k_loop<3>(f, acc, nk, wrow0, brow, lane, wave); break;
-      case 4: k_loop<4>(f, acc, nk, wrow0, brow, lane, wave); break;
-      default: k_loop<5>(f, acc, nk, wrow0, brow, lane, wave); break;
-    }
+  switch (nrb) {
+    case 0: k_loop<0>(f, acc, nk, wrow0, brow, lane, wave); break;
+    case 1: k_loop<1>(f, acc, nk, wrow0, brow, lane, wave); break;
+    case 2: k_loop<2>(f, acc, nk, wrow0, brow, lane, wave); break;
+    case 3: k_loop<3>(f, acc, nk, wrow0, brow, lane, wave); break;
+    case 4: k_loop<4>(f, acc, nk, wrow0, brow, lane, wave); break;
+    default: k_loop<5>(f, acc, nk, wrow0, brow, lane, wave); break;
   }
   static_assert(RB == 5, "k_loop dispatch");
 
@@ -436,13 +313,13 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
     constexpr int NJ = MODE == MODE_GATEUP ? 1 : 2;  // 32-column output blocks of this wave
     constexpr int LDSR = NJ * 32 + 8;                // LDS row stride (elements), padded
     constexpr int PB = 3;                            // row blocks per pass
-    static_assert(PB * 32 * LDSR * 2 <= BN * BK * 2, "epilogue pass fits a stage buffer");
+    static_assert(PB * 32 * LDSR * 2 <= BN * BK * 2 && BN * BK <= BM * 32, "epilogue pass fits a region");
     uint16_t* tile;
-    switch (wave) {  // A64 mode: the two A stages are split in halves for waves 0-3
+    switch (wave) {  // the two 40 KB A stages in halves, the four B stages
       case 0: tile = sA0; break;
-      case 1: tile = A64 ? sA0 + BM * 32 : sA1; break;
-      case 2: tile = A64 ? sA1 : sA2; break;
-      case 3: tile = A64 ? sA1 + BM * 32 : sA3; break;
+      case 1: tile = sA0 + BM * 32; break;
+      case 2: tile = sA1; break;
+      case 3: tile = sA1 + BM * 32; break;
       case 4: tile = sB0; break;
       case 5: tile = sB1; break;
       case 6: tile = sB2; break;
@@ -509,10 +386,16 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
 // 16 bytes each) of the K tile after next into registers while the current
 // tile is computed from LDS, then writes the next tile's registers into the
 // other LDS buffer.  Two K tiles are thus in flight per workgroup, held in the
-// register file rather than in LDS (two LDS buffers of 64 KB).  One barrier per
-// K step.  The 16-byte chunks of each 128-byte LDS row are XOR-swizzled by row
-// so the ds_write_b128 stores and the MFMA operand reads are free of bank
-// conflicts.
+// register file rather than in LDS (two LDS buffers of 64 KB).  Loads are
+// buffer loads (scalar base, 32-bit per-lane offsets); the weights, read once,
+// with the non-temporal cache policy.  One barrier per K step.  The 16-byte
+// chunks of each 128-byte LDS row are XOR-swizzled by row so the ds_write_b128
+// stores and the MFMA operand reads are free of bank conflicts.
+//
+// Against the 320-row kernel: one wave per SIMD hides LDS waits and barriers
+// less well, but the deeper weight prefetch and whole-line loads make a chunk
+// cost about 0.88 of a 320-row chunk; gemm_bm takes this tile when that is
+// worth the smaller chunks.
 //
 // Gate/up pass: the wave's four 32-column blocks are two gate blocks and the
 // matching two up blocks (same I columns), so SwiGLU is applied in registers.
@@ -531,8 +414,6 @@ constexpr int RNBL = RBN / 32;     // B loads per lane per K step
 constexpr int RROWS = RBM + RBN;   // 128-byte LDS rows per buffer
 static_assert(kGemmBMrs == RBM, "chunk lists are cut to the tile height");
 static_assert(2 * RROWS * 128 <= 160 * 1024, "LDS");
-
-__device__ __forceinline__ int rswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -553,9 +434,7 @@ struct RsSrc {
   uint32_t bgrp[RNBL];         // byte offset of B group j within its matrix
 };
 constexpr int kBufFlags = 0x00020000;  // raw buffer resource word 3 (gfx9 family)
-#ifndef MOE_RS_B_AUX
-#define MOE_RS_B_AUX 2  // B loads: non-temporal (each weight is read once)
-#endif
+constexpr int kNonTemporal = 2;  // cache policy of the weight loads: each weight is read once
 
 // Operand registers of one 16-wide substep.
 struct RsOps {
@@ -581,7 +460,7 @@ __device__ __forceinline__ void rs_load1(RsRegs& r, const RsSrc& s, int kt, int 
   } else {
     const int j = q - NA;
     const bool up = MODE == MODE_GATEUP && (j & 3) >= 2;
-    r.b[j] = __builtin_amdgcn_raw_buffer_load_b128(up ? s.ru : s.rg, s.boff, (int)s.bgrp[j] + ko, MOE_RS_B_AUX);
+    r.b[j] = __builtin_amdgcn_raw_buffer_load_b128(up ? s.ru : s.rg, s.boff, (int)s.bgrp[j] + ko, kNonTemporal);
   }
 }
 
@@ -606,8 +485,10 @@ __device__ __forceinline__ void rs_read1(RsOps& o, const u32x4* L, const int (&r
 
 // One 16-wide substep SS of K step t (in buffer S), with the memory traffic of
 // the pipeline interleaved between its MFMAs in a fixed order:
-//   SS 0: the global loads of step t + 2 (register set S), operand reads of SS 1;
-//   SS 1: operand reads of SS 2;
+//   SS 0: the first half of the global loads of step t + 2 (register set S,
+//         whose previous contents were stored in the step before), operand
+//         reads of SS 1;
+//   SS 1: the second half of those loads, operand reads of SS 2;
 //   SS 2: operand reads of SS 3, then the LDS stores of step t + 1 (register set
 //         1 - S into buffer 1 - S, whose last reads were before the previous
 //         barrier);
@@ -615,12 +496,6 @@ __device__ __forceinline__ void rs_read1(RsOps& o, const u32x4* L, const int (&r
 //         done), then the operand reads of SS 0 of step t + 1.
 // Each group (side operations + one MFMA) is fenced with a scheduling barrier so
 // the compiler keeps this order and only two operand sets are live.
-#ifndef MOE_RS_ST_SS
-#define MOE_RS_ST_SS 2
-#endif
-#ifndef MOE_RS_LD_SPLIT
-#define MOE_RS_LD_SPLIT 1  // global loads over substeps 0 and 1
-#endif
 template <int MODE, int SS, int S, int NA, int NRB, bool LOAD, bool STORE, bool NEXT>
 __device__ __forceinline__ void rs_substep(f32x16 (&acc)[RWMB][RWNB], RsRegs (&R)[2], RsOps (&op)[2],
                                            const RsSrc& src, u32x4* L0, u32x4* L1, int t, int wr,
@@ -628,15 +503,12 @@ __device__ __forceinline__ void rs_substep(f32x16 (&acc)[RWMB][RWNB], RsRegs (&R
   constexpr int M = NRB * RWNB;                  // MFMAs
   constexpr int NOP = NRB > 0 ? NRB + RWNB : 0;  // operand reads per substep
   constexpr int NLD = NA + RNBL;                 // global loads (and LDS stores) per K step
-  constexpr int ld0 = !LOAD ? 0 : (MOE_RS_LD_SPLIT ? (SS == 0 ? 0 : NLD / 2) : 0);
-  constexpr int n_gl = !LOAD ? 0 : (MOE_RS_LD_SPLIT ? (SS == 0 ? NLD / 2 : SS == 1 ? NLD - NLD / 2 : 0)
-                                                    : (SS == 0 ? NLD : 0));
+  constexpr int ld0 = SS == 0 ? 0 : NLD / 2;   // first global load of this substep
+  constexpr int n_gl = !LOAD ? 0 : SS == 0 ? NLD / 2 : SS == 1 ? NLD - NLD / 2 : 0;
   constexpr int n_rd = SS < 3 ? NOP : (NEXT ? NOP : 0);
-  constexpr int n_st = (SS == MOE_RS_ST_SS && STORE) ? NLD : 0;
+  constexpr int n_st = (SS == 2 && STORE) ? NLD : 0;
   constexpr bool BAR = SS == 3 && NEXT;
-  // before the barrier (substep 3 only): the LDS stores if they belong here
-  constexpr int P_pre = BAR ? n_st : 0;
-  constexpr int P = n_gl + n_rd + n_st - P_pre;  // side operations after the barrier (or all)
+  constexpr int P = n_gl + n_rd + n_st;          // side operations (after the barrier in SS 3)
   constexpr int M0 = BAR ? M / 2 : 0;            // MFMAs before the barrier
   const u32x4* Lc = S == 0 ? L0 : L1;
   u32x4* Ln = S == 0 ? L1 : L0;
@@ -645,35 +517,23 @@ __device__ __forceinline__ void rs_substep(f32x16 (&acc)[RWMB][RWNB], RsRegs (&R
   RsOps& cur = op[SS & 1];
   RsOps& nxt = op[(SS & 1) ^ 1];
 
-  // order: global loads, operand reads, LDS stores (stores of substep 3 before its barrier)
+  // order: global loads, operand reads, LDS stores
   auto side = [&](int q) {
     if (q < n_gl) rs_load1<MODE, NA>(R[S], src, t + 2, ld0 + q);
     else if (q < n_gl + n_rd) rs_read1(nxt, Lr, ra, rb, sr, q - n_gl);
     else rs_store1<NA>(R[1 - S], Ln, wr, q - n_gl - n_rd);
   };
-  auto side_pre = [&](int q) { rs_store1<NA>(R[1 - S], Ln, wr, q); };
   auto mfma = [&](int m) {
     const int ai = m / RWNB, ni = m % RWNB;
     acc[ai][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[ai], cur.b[ni], acc[ai][ni], 0, 0, 0);
   };
 
+#pragma unroll
+  for (int m = 0; m < M0; ++m) {
+    mfma(m);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if constexpr (BAR) {
-    if constexpr (M0 == 0) {
-#pragma unroll
-      for (int q = 0; q < P_pre; ++q) side_pre(q);
-    } else {
-      constexpr int PPM0 = (P_pre + M0 - 1) / M0;
-#pragma unroll
-      for (int m = 0; m < M0; ++m) {
-#pragma unroll
-        for (int j = 0; j < PPM0; ++j) {
-          const int q = m * P_pre / M0 + j;
-          if (q < (m + 1) * P_pre / M0) side_pre(q);
-        }
-        mfma(m);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
     rs_barrier();
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -752,7 +612,7 @@ __device__ __forceinline__ void rs_wave(const GemmArgs& a, const Chunk& ch, int 
   const int l32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const int c = (2 * s + h) ^ rswz(l32);
+    const int c = (2 * s + h) ^ swz8(l32);
     ra[s] = (wm * 32 + l32) * 8 + c;
     rb[s] = (RBM + wn * 128 + l32) * 8 + c;
   }
@@ -832,7 +692,7 @@ __device__ __forceinline__ void rs_run(const GemmArgs& a, const Chunk& ch, int n
 
   // loader: lane -> row (tid / 8) of each 32-row group, logical 16-byte chunk tid % 8
   const int lrow = tid >> 3, lchunk = tid & 7;
-  const int wr = lrow * 8 + (lchunk ^ rswz(lrow));
+  const int wr = lrow * 8 + (lchunk ^ swz8(lrow));
   RsSrc src;
   src.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), (short)0, -1, kBufFlags);
 #pragma unroll
