@@ -100,10 +100,20 @@ def event_ms(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def achievable(torch):
+def achievable(moe, torch):
     """Peaks this box reaches on plain work, next to the published ones: a 2 GiB
-    device copy (torch copy_: read + write bytes) and a dense bf16 GEMM of the
-    gate/up shape with every token on one expert (torch.matmul -> hipBLASLt)."""
+    device copy (torch copy_: read + write bytes), the library's MFMA-only
+    calibration kernel (bf16 MFMAs on register operands, no memory traffic), and a
+    dense bf16 GEMM of the gate/up shape with every token on one expert
+    (torch.matmul -> hipBLASLt)."""
+    sink = torch.empty(moe.MFMA_PEAK_SINK, device="cuda")
+    iters = 2000
+    fl = [0]
+
+    def mfma():
+        fl[0] = moe.mfma_peak(iters, sink)
+    ms_mfma = event_ms(torch, mfma, 10, 3)
+    del sink
     n = 2 ** 31
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -116,9 +126,12 @@ def achievable(torch):
     del a, b
     torch.cuda.empty_cache()
     return {"hbm_copy_GBps": 2.0 * n / (ms_copy * 1e-3) / 1e9,
+            "mfma_loop_bf16_TFLOPs": fl[0] / (ms_mfma * 1e-3) / 1e12,
             "dense_bf16_gemm_TFLOPs": 2.0 * m * kk * nn / (ms_mm * 1e-3) / 1e12,
             "dense_gemm_shape": [m, kk, nn],
-            "note": "copy counts bytes read + written; GEMM is torch.matmul (hipBLASLt), contiguous operands"}
+            "note": "copy counts bytes read + written; the MFMA loop is moe_mfma_peak (v_mfma_f32_32x32x16_bf16 "
+                    "on registers, 2048 workgroups x 4 waves x 4 chains); GEMM is torch.matmul (hipBLASLt), "
+                    "contiguous operands"}
 
 
 def variants(moe, torch, np, s, dev, x, y, ws, steps, warmup):
@@ -320,9 +333,10 @@ def main():
         out["variants"] = variants(moe, torch, np, s, dev, x, y, ws, a.steps, a.warmup)
         print("[bench] routing variants timed", file=sys.stderr, flush=True)
     if not a.no_achievable:
-        out["achievable"] = achievable(torch)
+        out["achievable"] = achievable(moe, torch)
         g = out["achievable"]
         out["roofline"]["frac_of_achievable"] = gateup_tflops / g["dense_bf16_gemm_TFLOPs"]
+        out["roofline"]["frac_of_mfma_loop"] = gateup_tflops / g["mfma_loop_bf16_TFLOPs"]
         print("[bench] achievable peaks measured", file=sys.stderr, flush=True)
 
     if not a.no_cpu_baseline:

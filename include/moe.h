@@ -299,6 +299,16 @@ moe_status moe_route_ec(const moe_config *cfg, const float *scores, int32_t *tok
 moe_status moe_forward_ec(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
                           moe_ec_out *eo, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- calibration (not part of the layer) ----
+ * The bf16 MFMA rate the device sustains with no memory traffic: one launch of
+ * 2048 workgroups x 4 waves, each wave issuing 4 * iters
+ * v_mfma_f32_32x32x16_bf16 on register operands (four independent accumulator
+ * chains) and writing one float of its result into sink (device, float32,
+ * 8192 entries).  *flops (host) receives the launch's floating-point operation
+ * count; the caller times the launch (events on `stream`).  1 <= iters <= 2^24;
+ * MOE_ERR_SHAPE otherwise, MOE_ERR_NULL for a NULL sink or flops. */
+moe_status moe_mfma_peak(int64_t iters, float *sink, int64_t *flops, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

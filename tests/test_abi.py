@@ -142,3 +142,14 @@ def test_expert_choice_host_calls():
     assert L.moe_route_ec(p(good), None, 16, 16, None) == 1
     assert L.moe_route_ec(p(good), 16, 16, 8, None) == 6
     assert L.moe_forward_ec(p(good), None, 16, 16, None, 16, 1 << 30, None) == 1
+
+
+def test_mfma_peak_host_validation():
+    """The calibration entry point rejects bad arguments on the host, before any launch."""
+    L = moe.lib()
+    fl = ctypes.c_int64(-1)
+    assert L.moe_mfma_peak(0, None, ctypes.byref(fl), None) == 2
+    assert L.moe_mfma_peak((1 << 24) + 1, None, ctypes.byref(fl), None) == 2
+    assert L.moe_mfma_peak(10, None, ctypes.byref(fl), None) == 1
+    assert L.moe_mfma_peak(10, None, None, None) == 1
+    assert fl.value == -1

@@ -24,7 +24,7 @@ STAGE_EVENTS = 6
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_capacity", "moe_layer_params",
            "moe_route", "moe_route_sel", "moe_balance_stats", "moe_bias_update", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_timed", "moe_ec_capacity",
-           "moe_ec_workspace_size", "moe_route_ec", "moe_forward_ec", "moe_quantize_fp8", "moe_forward_fp8")
+           "moe_ec_workspace_size", "moe_route_ec", "moe_forward_ec", "moe_quantize_fp8", "moe_forward_fp8", "moe_mfma_peak")
 
 
 class MoeConfig(ctypes.Structure):
@@ -115,6 +115,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_ec.restype = c_int32
         L.moe_forward_ec.argtypes = [P, POINTER(MoeWeights), c_void_p, c_void_p, POINTER(MoeEcOut), c_void_p,
                                      c_size_t, c_void_p]
+        L.moe_mfma_peak.restype = c_int32
+        L.moe_mfma_peak.argtypes = [c_int64, c_void_p, POINTER(c_int64), c_void_p]
         L.moe_quantize_fp8.restype = c_int32
         L.moe_quantize_fp8.argtypes = [c_void_p, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p]
         L.moe_forward_fp8.restype = c_int32
@@ -284,6 +286,17 @@ def forward_ec(cfg, weights, x, y, ws, ec_out=None, stream=None):
 
 
 # ---- FP8 experts ----
+
+MFMA_PEAK_SINK = 8192
+
+
+def mfma_peak(iters, sink, stream=None) -> int:
+    """Launch the MFMA-only calibration kernel (moe_mfma_peak) on `stream`; sink: float32 device tensor of
+    MFMA_PEAK_SINK entries.  Returns the launch's floating-point operation count (time it with events)."""
+    fl = c_int64(0)
+    _check(lib().moe_mfma_peak(int(iters), _ptr(sink), ctypes.byref(fl), _stream(stream)), "moe_mfma_peak")
+    return fl.value
+
 
 def quantize_fp8(w, codes, scales, stream=None):
     """moe_quantize_fp8 of a [G, N, K] bf16 / fp32 tensor into codes (uint8) and scales (fp32)."""

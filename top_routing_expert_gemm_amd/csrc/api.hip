@@ -470,6 +470,15 @@ moe_status moe_quantize_fp8(const void* w, int32_t dtype, int64_t G, int64_t N, 
   return MOE_OK;
 }
 
+moe_status moe_mfma_peak(int64_t iters, float* sink, int64_t* flops, void* stream) {
+  if (iters < 1 || iters > (int64_t(1) << 24)) return MOE_ERR_SHAPE;
+  if (flops == nullptr) return MOE_ERR_NULL;
+  MOE_TRY(need(sink));
+  *flops = mfma_peak_flops(iters);
+  HIP_TRY(launch_mfma_peak((int)iters, sink, S(stream)));
+  return MOE_OK;
+}
+
 moe_status moe_forward_fp8(const moe_config* c, const moe_weights* w, const moe_fp8_experts* q, const void* x,
                            void* y, moe_route_out* ro, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(moe_validate(c));

@@ -168,6 +168,12 @@ hipError_t launch_combine(const void* y_perm, const int32_t* row_of_slot, const 
                           const void* y_shared, void* y, int64_t T, int64_t H, int64_t k,
                           int dtype, hipStream_t s, float scale = 1.f);
 
+// Calibration: MFMA-only kernel (iters rounds of 4 chains per wave), its
+// flop count and its sink length.
+int64_t mfma_peak_flops(int64_t iters);
+int64_t mfma_peak_sink_len();
+hipError_t launch_mfma_peak(int iters, float* sink, hipStream_t s);
+
 // Expert choice: chunk list of E groups of C rows each (+ shared rows), and the
 // per-expert top-C selection from scores [T, E].
 hipError_t launch_chunks_uniform(int64_t E, int64_t C, int64_t shared_rows, int64_t shared_row0, Chunk* chunks,
