@@ -17,28 +17,16 @@ inline size_t esize(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; 
 struct Layout {
   size_t topk_idx, topk_w, counts, offsets, row_of_slot, token_of_row, dscratch, rscratch, chunks, n_chunks, h,
       y_perm, total;
-  int64_t rows;        // permuted row space: T*k routed rows, then T shared rows
-  int64_t max_chunks;  // chunk-list capacity
+  int64_t rows;    // permuted row space: T*k routed rows, then T shared rows
+  ChunkPlan plan;  // chunk lists and their capacities
 };
-
-int64_t cap_of(const moe_config* c);
-
-// Chunk height of the moe_forward family: its row space holds at most T*k
-// routed + T shared rows; the busiest expert is expected to hold its capacity
-// when one is set, else about 1.2x the mean T*k/E (the spread of the synthetic
-// routing of the benchmark shapes stays within it).
-int fwd_bm(const moe_config* c) {
-  const int64_t cap = cap_of(c);
-  const int64_t busiest = cap > 0 ? cap : (c->T * c->k * 6 + 5 * c->E - 1) / (5 * c->E);
-  return gemm_bm(*c, c->T * c->k + c->T, busiest);
-}
 
 Layout layout(const moe_config* c) {
   Layout L;
   const int64_t Tk = c->T * c->k;
   const int64_t sh = c->n_shared ? c->T : 0;
   L.rows = Tk + sh;
-  L.max_chunks = max_chunks(Tk, c->E, sh, fwd_bm(c));
+  L.plan = chunk_plan(*c, Tk, sh);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -53,8 +41,8 @@ Layout layout(const moe_config* c) {
   L.token_of_row = take((size_t)Tk * 4);
   L.dscratch = take(dispatch_scratch_bytes(Tk, c->E));
   L.rscratch = take(route_scratch_bytes(*c));
-  L.chunks = take((size_t)L.max_chunks * sizeof(Chunk));
-  L.n_chunks = take(4);
+  L.chunks = take((size_t)(L.plan.max_a + L.plan.max_b) * sizeof(Chunk));
+  L.n_chunks = take(8);
   L.h = take((size_t)L.rows * c->I * esize(c));
   L.y_perm = take((size_t)L.rows * c->H * esize(c));
   L.total = off;
@@ -71,7 +59,8 @@ int64_t ec_cap_of(const moe_config* c) {
 // Device workspace of moe_forward_ec.
 struct LayoutEC {
   size_t topk_idx, topk_w, scores, rscratch, token_of_row, row_of_pair, chunks, n_chunks, h, y_perm, total;
-  int64_t C, rows, max_chunks;
+  int64_t C, rows;
+  ChunkPlan plan;
 };
 
 LayoutEC layout_ec(const moe_config* c) {
@@ -80,7 +69,7 @@ LayoutEC layout_ec(const moe_config* c) {
   const int64_t R = c->E * L.C;
   const int64_t sh = c->n_shared ? c->T : 0;
   L.rows = R + sh;
-  L.max_chunks = max_chunks(R, c->E, sh, gemm_bm(*c, R + c->T, L.C));
+  L.plan = chunk_plan(*c, R, sh);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -93,8 +82,8 @@ LayoutEC layout_ec(const moe_config* c) {
   L.rscratch = take(route_scratch_bytes(*c));
   L.token_of_row = take((size_t)R * 4);
   L.row_of_pair = take((size_t)c->T * c->E * 4);
-  L.chunks = take((size_t)L.max_chunks * sizeof(Chunk));
-  L.n_chunks = take(4);
+  L.chunks = take((size_t)(L.plan.max_a + L.plan.max_b) * sizeof(Chunk));
+  L.n_chunks = take(8);
   L.h = take((size_t)L.rows * c->I * esize(c));
   L.y_perm = take((size_t)L.rows * c->H * esize(c));
   L.total = off;
@@ -134,6 +123,23 @@ int64_t cap_of(const moe_config* c) {
   if (!(c->capacity_factor > 0.f)) return -1;
   const double v = ceil((double)c->capacity_factor * (double)c->T * (double)c->k / (double)c->E);
   return (int64_t)v;
+}
+
+// One grouped-GEMM pass over the chunk lists of plan p: launch(g) with g on
+// list A, then on list B when the plan has one.
+template <typename F>
+hipError_t each_list(GemmArgs g, const ChunkPlan& p, Chunk* chunks, int32_t* nch, F launch) {
+  g.chunks = chunks;
+  g.n_chunks = nch;
+  g.max_chunks = p.max_a;
+  g.bm = p.cut.bm_a;
+  const hipError_t e = launch(g);
+  if (e != hipSuccess || p.cut.bm_b == 0) return e;
+  g.chunks = chunks + p.cut.off_b;
+  g.n_chunks = nch + 1;
+  g.max_chunks = p.max_b;
+  g.bm = p.cut.bm_b;
+  return launch(g);
 }
 
 }  // namespace
@@ -257,7 +263,7 @@ moe_status moe_dispatch(const moe_config* c, const int32_t* topk_idx, const void
   const Layout L = layout(c);
   HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), topk_idx, counts, offsets, row_of_slot, token_of_row,
                           at(ws, L.dscratch), reinterpret_cast<Chunk*>(at(ws, L.chunks)),
-                          reinterpret_cast<int32_t*>(at(ws, L.n_chunks)), fwd_bm(c), 0, 0, S(stream)));
+                          reinterpret_cast<int32_t*>(at(ws, L.n_chunks)), L.plan.cut, 0, 0, S(stream)));
   if (x_perm != nullptr)
     HIP_TRY(launch_gather(x, token_of_row, offsets, c->E, c->T * c->k, c->H, c->dtype, x_perm, S(stream)));
   return MOE_OK;
@@ -275,18 +281,14 @@ moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t
   MOE_TRY(need(y_perm));
   MOE_TRY(check_ws(c, ws, ws_bytes));
   const Layout L = layout(c);
-  const int bm = fwd_bm(c);
   Chunk* chunks = reinterpret_cast<Chunk*>(at(ws, L.chunks));
   int32_t* nch = reinterpret_cast<int32_t*>(at(ws, L.n_chunks));
-  HIP_TRY(launch_chunks_from_offsets(offsets, c->E, chunks, nch, bm, S(stream)));
+  hipStream_t s = S(stream);
+  HIP_TRY(launch_chunks_from_offsets(offsets, c->E, chunks, nch, L.plan.cut, s));
   GemmArgs g{};
   g.A = x_perm;
   g.gather = nullptr;
   g.shared_row0 = 0;
-  g.chunks = chunks;
-  g.n_chunks = nch;
-  g.max_chunks = max_chunks(c->T * c->k, c->E, 0, bm);
-  g.bm = bm;
   g.w0 = w_gate;
   g.w1 = w_up;
   g.E = c->E;
@@ -294,14 +296,14 @@ moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t
   g.N = c->I;
   g.a_rows = c->T * c->k;
   g.out = at(ws, L.h);
-  HIP_TRY(launch_gateup(g, c->dtype, S(stream)));
+  HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) { return launch_gateup(a, c->dtype, s); }));
   g.A = at(ws, L.h);
   g.w0 = w_down;
   g.w1 = nullptr;
   g.K = c->I;
   g.N = c->H;
   g.out = y_perm;
-  HIP_TRY(launch_down(g, c->dtype, S(stream)));
+  HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) { return launch_down(a, c->dtype, s); }));
   return MOE_OK;
 }
 
@@ -377,7 +379,6 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
     if (events == nullptr || events[i] == nullptr) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
   };
-  const int bm = fwd_bm(c);
   const int64_t Tk = c->T * c->k;
   const int64_t sh = c->n_shared ? c->T : 0;
   Chunk* chunks = reinterpret_cast<Chunk*>(at(ws, L.chunks));
@@ -388,16 +389,12 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
                              r.topk_idx, r.topk_w, at(ws, L.rscratch), s));
   HIP_TRY(mark(1));
   HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), r.topk_idx, r.counts, r.offsets, r.row_of_slot,
-                          r.token_of_row, at(ws, L.dscratch), chunks, nch, bm, sh, Tk, s));
+                          r.token_of_row, at(ws, L.dscratch), chunks, nch, L.plan.cut, sh, Tk, s));
   HIP_TRY(mark(2));
   GemmArgs g{};
   g.A = x;
   g.gather = r.token_of_row;
   g.shared_row0 = Tk;
-  g.chunks = chunks;
-  g.n_chunks = nch;
-  g.max_chunks = L.max_chunks;
-  g.bm = bm;
   if (q == nullptr) {
     g.w0 = w->w_gate;
     g.w1 = w->w_up;
@@ -418,7 +415,9 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
   g.N = c->I;
   g.a_rows = c->T;
   g.out = at(ws, L.h);
-  HIP_TRY(q == nullptr ? launch_gateup(g, c->dtype, s) : launch_gateup_fp8(g, s));
+  HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) {
+    return q == nullptr ? launch_gateup(a, c->dtype, s) : launch_gateup_fp8(a, s);
+  }));
   HIP_TRY(mark(3));
   g.A = at(ws, L.h);
   g.gather = nullptr;
@@ -438,7 +437,9 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
   g.N = c->H;
   g.a_rows = L.rows;
   g.out = at(ws, L.y_perm);
-  HIP_TRY(q == nullptr ? launch_down(g, c->dtype, s) : launch_down_fp8(g, s));
+  HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) {
+    return q == nullptr ? launch_down(a, c->dtype, s) : launch_down_fp8(a, s);
+  }));
   HIP_TRY(mark(4));
   const void* ysh = c->n_shared ? static_cast<const void*>(at(ws, L.y_perm + (size_t)Tk * c->H * esize(c))) : nullptr;
   HIP_TRY(launch_combine(at(ws, L.y_perm), r.row_of_slot, r.topk_w, ysh, y, c->T, c->H, c->k, c->dtype, s));
@@ -548,7 +549,6 @@ moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void*
   MOE_TRY(need(o.row_of_pair));
 
   hipStream_t s = S(stream);
-  const int bm = gemm_bm(*c, c->E * L.C + c->T, L.C);
   const int64_t R = c->E * L.C;
   const int64_t sh = c->n_shared ? c->T : 0;
   Chunk* chunks = reinterpret_cast<Chunk*>(at(ws, L.chunks));
@@ -558,15 +558,11 @@ moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void*
                              reinterpret_cast<int32_t*>(at(ws, L.topk_idx)), reinterpret_cast<float*>(at(ws, L.topk_w)),
                              at(ws, L.rscratch), s));
   HIP_TRY(launch_ec_select(o.scores, c->T, c->E, L.C, o.token_of_row, o.row_of_pair, s));
-  HIP_TRY(launch_chunks_uniform(c->E, L.C, sh, R, chunks, nch, bm, s));
+  HIP_TRY(launch_chunks_uniform(c->E, L.C, sh, R, chunks, nch, L.plan.cut, s));
   GemmArgs g{};
   g.A = x;
   g.gather = o.token_of_row;
   g.shared_row0 = R;
-  g.chunks = chunks;
-  g.n_chunks = nch;
-  g.max_chunks = L.max_chunks;
-  g.bm = bm;
   g.w0 = w->w_gate;
   g.w1 = w->w_up;
   g.ws0 = w->ws_gate;
@@ -576,7 +572,7 @@ moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void*
   g.N = c->I;
   g.a_rows = c->T;
   g.out = at(ws, L.h);
-  HIP_TRY(launch_gateup(g, c->dtype, s));
+  HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) { return launch_gateup(a, c->dtype, s); }));
   g.A = at(ws, L.h);
   g.gather = nullptr;
   g.w0 = w->w_down;
@@ -587,7 +583,7 @@ moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void*
   g.N = c->H;
   g.a_rows = L.rows;
   g.out = at(ws, L.y_perm);
-  HIP_TRY(launch_down(g, c->dtype, s));
+  HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) { return launch_down(a, c->dtype, s); }));
   const void* ysh = c->n_shared ? static_cast<const void*>(at(ws, L.y_perm + (size_t)R * c->H * esize(c))) : nullptr;
   // weight of a chosen pair: its gate score times routed_scaling_factor
   HIP_TRY(launch_combine(at(ws, L.y_perm), o.row_of_pair, o.scores, ysh, y, c->T, c->H, c->E, c->dtype, s,

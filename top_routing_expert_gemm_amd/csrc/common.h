@@ -30,7 +30,7 @@ struct Chunk {
 };
 
 // M-tile heights of the two bf16 grouped GEMM kernels: register-staged (256)
-// and direct-to-LDS (320).  Chunk lists are cut to the one gemm_bm picks.
+// and direct-to-LDS (320).
 #ifndef MOE_GEMM_RS
 #define MOE_GEMM_RS 1
 #endif
@@ -42,26 +42,47 @@ constexpr int kGemmBMf32 = 64;
 constexpr int kGemvBM = 16;
 constexpr int64_t kGemvMaxT = 16;
 
-// Chunk height for a layer whose permuted row space has at most `rows` rows and
-// whose busiest expert group is expected to hold `group_rows` rows: the
-// streaming path when every group fits one 16-row chunk (T <= 16); fp32 uses
-// 64.  For bf16 both MFMA kernels are eligible when the register-staged one's
-// limits hold (both contractions >= 128 long, 32-bit buffer offsets covering
-// x [T, H], the row space and h [rows, I]); a register-staged 256-row chunk
-// costs about 0.88 of a direct-to-LDS 320-row chunk (measured on the DeepSeek-V3,
-// Mixtral and Switch shapes), so the 256-row tile is taken unless it needs
-// more chunks per group than that saves (a group of 257..320 rows: two
-// chunks instead of one).
-inline int gemm_bm(const moe_config& c, int64_t rows, int64_t group_rows) {
-  if (c.dtype != MOE_BF16) return kGemmBMf32;
-  if (c.T <= kGemvMaxT) return kGemvBM;
-  const int64_t lim = int64_t(1) << 32;
-  const bool fits = MOE_GEMM_RS && c.H >= 128 && c.I >= 128 && std::max<int64_t>(c.T, rows) * c.H * 2 < lim &&
-                    rows * c.I * 2 < lim && c.H * c.I * 2 < lim;
-  if (!fits) return kGemmBMdl;
-  const int64_t g = std::max<int64_t>(group_rows, 1);
-  const int64_t n_rs = (g + kGemmBMrs - 1) / kGemmBMrs, n_dl = (g + kGemmBMdl - 1) / kGemmBMdl;
-  return 22 * n_rs <= 25 * n_dl ? kGemmBMrs : kGemmBMdl;
+// How the dispatch step cuts expert groups into row chunks: one list of bm_a-row
+// chunks (bm_b == 0), or two lists, A of bm_a-row chunks at chunks[0] and B of
+// bm_b-row chunks at chunks[off_b], each group going to the list where it costs
+// less (decided on the device from its row count).
+struct ChunkCut {
+  int bm_a;
+  int bm_b;
+  int64_t off_b;
+};
+
+// Max chunk-list entries for `rows_max` routed rows over E groups (+ shared rows).
+int64_t max_chunks(int64_t rows_max, int64_t E, int64_t shared_rows, int bm);
+
+// Chunk lists of a layer with at most `routed` routed rows over E groups plus
+// `shared` shared rows: the streaming path when every group fits one 16-row
+// chunk (T <= 16), 64-row chunks for fp32; for bf16 two lists (256-row
+// register-staged tile, 320-row direct-to-LDS tile) when the register-staged
+// kernel's limits hold (both contractions at least 128 long, 32-bit buffer
+// offsets covering x [T, H], the row space [rows, H] and h [rows, I]), else the
+// 320-row tile alone.  max_a / max_b: capacities of the two lists.
+struct ChunkPlan {
+  ChunkCut cut;
+  int64_t max_a, max_b;
+};
+inline ChunkPlan chunk_plan(const moe_config& c, int64_t routed, int64_t shared) {
+  ChunkPlan p{};
+  const int64_t rows = routed + shared, lim = int64_t(1) << 32;
+  int bm_a = kGemmBMdl, bm_b = 0;
+  if (c.dtype != MOE_BF16) {
+    bm_a = kGemmBMf32;
+  } else if (c.T <= kGemvMaxT) {
+    bm_a = kGemvBM;
+  } else if (MOE_GEMM_RS && c.H >= 128 && c.I >= 128 && std::max<int64_t>(c.T, rows) * c.H * 2 < lim &&
+             rows * c.I * 2 < lim && c.H * c.I * 2 < lim) {
+    bm_a = kGemmBMrs;
+    bm_b = kGemmBMdl;
+  }
+  p.max_a = max_chunks(routed, c.E, shared, bm_a);
+  p.max_b = bm_b ? max_chunks(routed, c.E, shared, bm_b) : 0;
+  p.cut = ChunkCut{bm_a, bm_b, p.max_a};
+  return p;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -106,20 +127,18 @@ hipError_t launch_bias_update(const moe_config& c, const int32_t* counts, float 
 
 // Dispatch scratch sizes (bytes) for T*k assignments and E experts.
 size_t dispatch_scratch_bytes(int64_t Tk, int64_t E);
-// Max chunk-list entries for `rows_max` routed rows over E groups (+ shared rows).
-int64_t max_chunks(int64_t rows_max, int64_t E, int64_t shared_rows, int bm);
 
-// Histogram + scan + capacity + row maps; also writes the chunk list of the
+// Histogram + scan + capacity + row maps; also writes the chunk lists of the
 // routed groups (and the shared group when shared_rows > 0, starting at
-// shared_row0 in the row space).
+// shared_row0 in the row space); n_chunks[0..1] receive the list sizes.
 hipError_t launch_dispatch(int64_t T, int64_t k, int64_t E, int64_t cap, const int32_t* topk_idx,
                            int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
                            int32_t* token_of_row, void* scratch, Chunk* chunks, int32_t* n_chunks,
-                           int bm, int64_t shared_rows, int64_t shared_row0, hipStream_t s);
+                           const ChunkCut& cut, int64_t shared_rows, int64_t shared_row0, hipStream_t s);
 
-// Chunk list from a device offsets array (stage API).
+// Chunk lists from a device offsets array (stage API).
 hipError_t launch_chunks_from_offsets(const int32_t* offsets, int64_t E, Chunk* chunks,
-                                      int32_t* n_chunks, int bm, hipStream_t s);
+                                      int32_t* n_chunks, const ChunkCut& cut, hipStream_t s);
 
 // x_perm[row] = x[token_of_row[row]] for row < offsets[E].
 hipError_t launch_gather(const void* x, const int32_t* token_of_row, const int32_t* offsets,
@@ -177,7 +196,7 @@ hipError_t launch_mfma_peak(int iters, float* sink, hipStream_t s);
 // Expert choice: chunk list of E groups of C rows each (+ shared rows), and the
 // per-expert top-C selection from scores [T, E].
 hipError_t launch_chunks_uniform(int64_t E, int64_t C, int64_t shared_rows, int64_t shared_row0, Chunk* chunks,
-                                 int32_t* n_chunks, int bm, hipStream_t s);
+                                 int32_t* n_chunks, const ChunkCut& cut, hipStream_t s);
 hipError_t launch_ec_select(const float* scores, int64_t T, int64_t E, int64_t C, int32_t* token_of_row,
                             int32_t* row_of_pair, hipStream_t s);
 

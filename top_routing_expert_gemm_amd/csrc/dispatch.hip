@@ -88,17 +88,36 @@ __device__ int block_inclusive_scan(int v, int* tmp) {
   return r;
 }
 
-// Chunk list of E groups with given loads and first rows, then (optionally) the
+// Which list a group of L rows goes to.  With one list (bm_b == 0) every group
+// is cut to bm_a rows.  With two (the register-staged 256-row tile in list A,
+// the 320-row tile in list B), a list-A chunk costs about 0.88 of a list-B
+// chunk (measured on the DeepSeek-V3, Mixtral and Switch shapes), so a group
+// takes list A unless that needs more chunks than the lower cost saves (a group
+// of 257..320 rows: two chunks instead of one).
+__device__ __forceinline__ bool takes_list_a(int64_t L, const ChunkCut& cut) {
+  if (cut.bm_b == 0) return true;
+  const int64_t na = (L + cut.bm_a - 1) / cut.bm_a, nb = (L + cut.bm_b - 1) / cut.bm_b;
+  return 22 * na <= 25 * nb;
+}
+
+// Chunk lists of E groups with given loads and first rows, then (optionally) the
 // shared group over rows shared_row0 .. shared_row0 + shared_rows - 1.  A group
-// of `load` rows takes ceil(load / bm) chunks of balanced height (chunk c holds
-// rows [c load / n, (c + 1) load / n)), so the workgroups that stream the same
-// weight tile for one group do equal work and stay in step.
-__device__ void emit_chunks(int e_valid, int load, int row0, int E, int bm, int64_t shared_rows,
+// of `load` rows takes n = ceil(load / bm) chunks of its list's height bm, of
+// balanced size (chunk c holds rows [c load / n, (c + 1) load / n)), so the
+// workgroups that stream the same weight tile for one group do equal work and
+// stay in step.  List A starts at chunks[0], list B at chunks[cut.off_b]; each
+// list is compact and expert-ordered (shared group last), n_chunks[0] and
+// n_chunks[1] count them.
+__device__ void emit_chunks(int e_valid, int load, int row0, int E, const ChunkCut& cut, int64_t shared_rows,
                             int64_t shared_row0, Chunk* chunks, int32_t* n_chunks, int* tmp) {
   const int tid = threadIdx.x;
+  const bool in_a = takes_list_a(load, cut);
+  const int bm = in_a ? cut.bm_a : cut.bm_b;
   const int nch = e_valid ? (load + bm - 1) / bm : 0;
-  const int incl = block_inclusive_scan(nch, tmp);
-  const int base = incl - nch;
+  const int incl_a = block_inclusive_scan(in_a ? nch : 0, tmp);
+  const int incl_b = block_inclusive_scan(in_a ? 0 : nch, tmp);
+  const int base = in_a ? incl_a - nch : incl_b - nch;
+  Chunk* list = in_a ? chunks : chunks + cut.off_b;
   for (int c = 0; c < nch; ++c) {
     const int r0 = (int)((int64_t)c * load / nch), r1 = (int)((int64_t)(c + 1) * load / nch);
     Chunk ck;
@@ -108,29 +127,39 @@ __device__ void emit_chunks(int e_valid, int load, int row0, int E, int bm, int6
     ck.gfirst = base;
     ck.gcount = nch;
     ck.pad[0] = ck.pad[1] = ck.pad[2] = 0;
-    chunks[base + c] = ck;
+    list[base + c] = ck;
   }
-  __shared__ int total;
-  if (tid == kScanThreads - 1) total = incl;
+  __shared__ int total_a, total_b;
+  if (tid == kScanThreads - 1) {
+    total_a = incl_a;
+    total_b = incl_b;
+  }
   __syncthreads();
-  const int nsh = (int)((shared_rows + bm - 1) / bm);
+  const bool sh_a = takes_list_a(shared_rows, cut);
+  const int64_t sbm = sh_a ? cut.bm_a : cut.bm_b;
+  const int nsh = (int)((shared_rows + sbm - 1) / sbm);
+  const int sbase = sh_a ? total_a : total_b;
+  Chunk* slist = sh_a ? chunks : chunks + cut.off_b;
   for (int c = tid; c < nsh; c += kScanThreads) {
     const int64_t r0 = c * shared_rows / nsh, r1 = (c + 1) * shared_rows / nsh;
     Chunk ck;
     ck.group = E;
     ck.row0 = (int)(shared_row0 + r0);
     ck.nrows = (int)(r1 - r0);
-    ck.gfirst = total;
+    ck.gfirst = sbase;
     ck.gcount = nsh;
     ck.pad[0] = ck.pad[1] = ck.pad[2] = 0;
-    chunks[total + c] = ck;
+    slist[sbase + c] = ck;
   }
-  if (tid == 0) *n_chunks = total + nsh;
+  if (tid == 0) {
+    n_chunks[0] = total_a + (sh_a ? nsh : 0);
+    if (cut.bm_b != 0) n_chunks[1] = total_b + (sh_a ? 0 : nsh);
+  }
 }
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     int32_t* __restrict__ blk_counts, int64_t nb, int E, int64_t cap, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, Chunk* __restrict__ chunks, int32_t* __restrict__ n_chunks, int bm,
+    int32_t* __restrict__ offsets, Chunk* __restrict__ chunks, int32_t* __restrict__ n_chunks, ChunkCut cut,
     int64_t shared_rows, int64_t shared_row0) {
   __shared__ int tmp[kScanThreads];
   const int tid = threadIdx.x;
@@ -162,7 +191,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   const int excl = incl - load;
   if (e < E) offsets[e] = excl;
   if (e == E - 1) offsets[E] = incl;
-  emit_chunks(e < E, load, excl, E, bm, shared_rows, shared_row0, chunks, n_chunks, tmp);
+  emit_chunks(e < E, load, excl, E, cut, shared_rows, shared_row0, chunks, n_chunks, tmp);
 }
 
 __global__ __launch_bounds__(256) void finalize_kernel(const int32_t* __restrict__ idx, int64_t Tk, int k,
@@ -198,7 +227,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const int32_t* __restrict
 __global__ __launch_bounds__(kScanThreads) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, int Tk, int k, int E, int64_t cap, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_of_slot, int32_t* __restrict__ token_of_row,
-    Chunk* __restrict__ chunks, int32_t* __restrict__ n_chunks, int bm, int64_t shared_rows,
+    Chunk* __restrict__ chunks, int32_t* __restrict__ n_chunks, ChunkCut cut, int64_t shared_rows,
     int64_t shared_row0) {
   __shared__ int32_t cnt[kMaxE];
   __shared__ int32_t offs[kMaxE];
@@ -245,7 +274,7 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_small_kernel(
     offs[e] = excl;
   }
   if (e == E - 1) offsets[E] = incl;
-  emit_chunks(e < E, load, excl, E, bm, shared_rows, shared_row0, chunks, n_chunks, tmp);
+  emit_chunks(e < E, load, excl, E, cut, shared_rows, shared_row0, chunks, n_chunks, tmp);
   __syncthreads();
   if (tid < Tk) {
     const int r = rank_s[tid];
@@ -263,19 +292,19 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_small_kernel(
 // Every one of the E groups holds C rows (row0 = e*C), then the shared rows.
 __global__ __launch_bounds__(kScanThreads) void chunks_uniform_kernel(int E, int C, int64_t shared_rows,
                                                                       int64_t shared_row0, Chunk* __restrict__ chunks,
-                                                                      int32_t* __restrict__ n_chunks, int bm) {
+                                                                      int32_t* __restrict__ n_chunks, ChunkCut cut) {
   __shared__ int tmp[kScanThreads];
   const int e = threadIdx.x;
-  emit_chunks(e < E, C, e * C, E, bm, shared_rows, shared_row0, chunks, n_chunks, tmp);
+  emit_chunks(e < E, C, e * C, E, cut, shared_rows, shared_row0, chunks, n_chunks, tmp);
 }
 __global__ __launch_bounds__(kScanThreads) void chunks_from_offsets_kernel(
     const int32_t* __restrict__ offsets, int E, Chunk* __restrict__ chunks, int32_t* __restrict__ n_chunks,
-    int bm) {
+    ChunkCut cut) {
   __shared__ int tmp[kScanThreads];
   const int e = threadIdx.x;
   const int row0 = e < E ? offsets[e] : 0;
   const int load = e < E ? offsets[e + 1] - row0 : 0;
-  emit_chunks(e < E, load, row0, E, bm, 0, 0, chunks, n_chunks, tmp);
+  emit_chunks(e < E, load, row0, E, cut, 0, 0, chunks, n_chunks, tmp);
 }
 
 template <typename V>
@@ -303,11 +332,11 @@ int64_t max_chunks(int64_t rows_max, int64_t E, int64_t shared_rows, int bm) {
 hipError_t launch_dispatch(int64_t T, int64_t k, int64_t E, int64_t cap, const int32_t* topk_idx,
                            int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
                            int32_t* token_of_row, void* scratch, Chunk* chunks, int32_t* n_chunks,
-                           int bm, int64_t shared_rows, int64_t shared_row0, hipStream_t s) {
+                           const ChunkCut& cut, int64_t shared_rows, int64_t shared_row0, hipStream_t s) {
   const int64_t Tk = T * k;
   if (Tk <= kScanThreads) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kScanThreads), 0, s, topk_idx, (int)Tk, (int)k, (int)E,
-                       cap, counts, offsets, row_of_slot, token_of_row, chunks, n_chunks, bm, shared_rows,
+                       cap, counts, offsets, row_of_slot, token_of_row, chunks, n_chunks, cut, shared_rows,
                        shared_row0);
     return hipGetLastError();
   }
@@ -320,7 +349,7 @@ hipError_t launch_dispatch(int64_t T, int64_t k, int64_t E, int64_t cap, const i
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk, nb, (int)E, cap, counts, offsets,
-                     chunks, n_chunks, bm, shared_rows, shared_row0);
+                     chunks, n_chunks, cut, shared_rows, shared_row0);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)nb), dim3(256), 0, s, topk_idx, Tk, (int)k, (int)E, ch,
@@ -329,16 +358,16 @@ hipError_t launch_dispatch(int64_t T, int64_t k, int64_t E, int64_t cap, const i
 }
 
 hipError_t launch_chunks_uniform(int64_t E, int64_t C, int64_t shared_rows, int64_t shared_row0, Chunk* chunks,
-                                 int32_t* n_chunks, int bm, hipStream_t s) {
+                                 int32_t* n_chunks, const ChunkCut& cut, hipStream_t s) {
   hipLaunchKernelGGL(chunks_uniform_kernel, dim3(1), dim3(kScanThreads), 0, s, (int)E, (int)C, shared_rows,
-                     shared_row0, chunks, n_chunks, bm);
+                     shared_row0, chunks, n_chunks, cut);
   return hipGetLastError();
 }
 
 hipError_t launch_chunks_from_offsets(const int32_t* offsets, int64_t E, Chunk* chunks, int32_t* n_chunks,
-                                      int bm, hipStream_t s) {
+                                      const ChunkCut& cut, hipStream_t s) {
   hipLaunchKernelGGL(chunks_from_offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, offsets, (int)E, chunks,
-                     n_chunks, bm);
+                     n_chunks, cut);
   return hipGetLastError();
 }
 

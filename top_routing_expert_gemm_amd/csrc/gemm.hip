@@ -394,8 +394,9 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
 //
 // Against the 320-row kernel: one wave per SIMD hides LDS waits and barriers
 // less well, but the deeper weight prefetch and whole-line loads make a chunk
-// cost about 0.88 of a 320-row chunk; gemm_bm takes this tile when that is
-// worth the smaller chunks.
+// cost about 0.88 of a 320-row chunk; the dispatch step sends an expert group
+// to this tile when that is worth its smaller chunks (a layer runs both
+// kernels, each over its own chunk list).
 //
 // Gate/up pass: the wave's four 32-column blocks are two gate blocks and the
 // matching two up blocks (same I columns), so SwiGLU is applied in registers.
