@@ -31,7 +31,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_traffic_deepseek_v3_prefill.json")
-GEMM_SRC = os.path.join(ROOT, "top_routing_expert_gemm_amd", "csrc", "gemm.hip")
+# the gate/up stage's kernels and the dispatch step that deals the chunks between them
+GEMM_SRCS = [os.path.join(ROOT, "top_routing_expert_gemm_amd", "csrc", n) for n in ("gemm.hip", "dispatch.hip")]
 
 
 def parse():
@@ -49,18 +50,22 @@ def parse():
     return p.parse_args()
 
 
-def src_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def src_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_entry(kernel_ms):
-    """HBM bytes per launch of the gate/up GEMM from the committed counter runs, if still current."""
+    """HBM bytes of one gate/up stage (its two kernel launches) from the committed counter runs, if still
+    current (the record carries the sha256 of the GEMM and dispatch sources it was measured with)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("kernel_src_sha256") != src_sha(GEMM_SRC):
+    if t.get("kernel_src_sha256") != src_sha(GEMM_SRCS):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -260,7 +265,9 @@ def main():
         "config": {"workload": s.name, "T": s.T, "H": s.H, "moe_intermediate": s.I, "E": s.E, "k": s.k,
                    "gate": "sigmoid", "routed_scaling_factor": s.routed_scaling_factor, "n_shared": s.n_shared,
                    "capacity_factor": None, "global_batch": s.T, "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_bf16<gate/up+SwiGLU>",
+        "roofline": {"bound": "mfma",
+                     "kernel": "gate/up+SwiGLU grouped GEMM stage: grouped_gemm_rs<0> (256-row chunk list) + "
+                               "grouped_gemm_bf16<0> (320-row chunk list), one launch each",
                      "achieved": gateup_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": gateup_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "flops_per_launch": fl_gateup, "avg_launch_ms": avg["gateup"]},
