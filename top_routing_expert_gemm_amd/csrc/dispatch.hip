@@ -107,7 +107,8 @@ __device__ __forceinline__ bool takes_list_a(int64_t L, const ChunkCut& cut) {
 // workgroups that stream the same weight tile for one group do equal work and
 // stay in step.  List A starts at chunks[0], list B at chunks[cut.off_b]; each
 // list is compact and expert-ordered (shared group last), n_chunks[0] and
-// n_chunks[1] count them.
+// n_chunks[1] count them.  The shared group goes to list B only when routed
+// groups already went there.
 __device__ void emit_chunks(int e_valid, int load, int row0, int E, const ChunkCut& cut, int64_t shared_rows,
                             int64_t shared_row0, Chunk* chunks, int32_t* n_chunks, int* tmp) {
   const int tid = threadIdx.x;
@@ -135,7 +136,9 @@ __device__ void emit_chunks(int e_valid, int load, int row0, int E, const ChunkC
     total_b = incl_b;
   }
   __syncthreads();
-  const bool sh_a = takes_list_a(shared_rows, cut);
+  // the shared group follows its own cost, except that it never makes list B
+  // on its own: a launch of only its few chunks would leave most CUs idle
+  const bool sh_a = takes_list_a(shared_rows, cut) || total_b == 0;
   const int64_t sbm = sh_a ? cut.bm_a : cut.bm_b;
   const int nsh = (int)((shared_rows + sbm - 1) / sbm);
   const int sbase = sh_a ? total_a : total_b;
