@@ -497,6 +497,35 @@ __device__ __forceinline__ void rs_read1(RsOps& o, const u32x4* L, const int (&r
 //         done), then the operand reads of SS 0 of step t + 1.
 // Each group (side operations + one MFMA) is fenced with a scheduling barrier so
 // the compiler keeps this order and only two operand sets are live.
+// Order of the side operations of a substep with NL global loads, NR operand
+// reads and NS LDS stores: the three sequences merged so each element comes
+// when its share of the substep is due ((2i + 1) / 2n smallest first; reads win
+// ties), computed at compile time.  kind: 0 global load, 1 operand read,
+// 2 LDS store; idx: position within its sequence.
+template <int N>
+struct RsSideTable {
+  int kind[N > 0 ? N : 1];
+  int idx[N > 0 ? N : 1];
+};
+template <int NL, int NR, int NS>
+constexpr RsSideTable<NL + NR + NS> rs_side_table() {
+  RsSideTable<NL + NR + NS> t{};
+  int il = 0, ir = 0, is = 0;
+  for (int q = 0; q < NL + NR + NS; ++q) {
+    // due times (2i + 1) / (2n) as cross-multiplied fractions; 4 / 1 = never
+    const int64_t dl_n = il < NL ? 2 * il + 1 : 4, dl_d = il < NL ? 2 * NL : 1;
+    const int64_t dr_n = ir < NR ? 2 * ir + 1 : 4, dr_d = ir < NR ? 2 * NR : 1;
+    const int64_t ds_n = is < NS ? 2 * is + 1 : 4, ds_d = is < NS ? 2 * NS : 1;
+    int k;
+    if (dr_n * dl_d <= dl_n * dr_d && dr_n * ds_d <= ds_n * dr_d) k = 1;
+    else if (dl_n * ds_d <= ds_n * dl_d) k = 0;
+    else k = 2;
+    t.kind[q] = k;
+    t.idx[q] = k == 0 ? il++ : (k == 1 ? ir++ : is++);
+  }
+  return t;
+}
+
 template <int MODE, int SS, int S, int NA, int NRB, bool LOAD, bool STORE, bool NEXT>
 __device__ __forceinline__ void rs_substep(f32x16 (&acc)[RWMB][RWNB], RsRegs (&R)[2], RsOps (&op)[2],
                                            const RsSrc& src, u32x4* L0, u32x4* L1, int t, int wr,
@@ -518,11 +547,14 @@ __device__ __forceinline__ void rs_substep(f32x16 (&acc)[RWMB][RWNB], RsRegs (&R
   RsOps& cur = op[SS & 1];
   RsOps& nxt = op[(SS & 1) ^ 1];
 
-  // order: global loads, operand reads, LDS stores
+  // the three kinds of side operation, merged in proportion, so the operand
+  // reads are spread over the substep instead of bunched
+  constexpr RsSideTable<n_gl + n_rd + n_st> tab = rs_side_table<n_gl, n_rd, n_st>();
   auto side = [&](int q) {
-    if (q < n_gl) rs_load1<MODE, NA>(R[S], src, t + 2, ld0 + q);
-    else if (q < n_gl + n_rd) rs_read1(nxt, Lr, ra, rb, sr, q - n_gl);
-    else rs_store1<NA>(R[1 - S], Ln, wr, q - n_gl - n_rd);
+    const int kind = tab.kind[q], idx = tab.idx[q];
+    if (kind == 0) rs_load1<MODE, NA>(R[S], src, t + 2, ld0 + idx);
+    else if (kind == 1) rs_read1(nxt, Lr, ra, rb, sr, idx);
+    else rs_store1<NA>(R[1 - S], Ln, wr, idx);
   };
   auto mfma = [&](int m) {
     const int ai = m / RWNB, ni = m % RWNB;
