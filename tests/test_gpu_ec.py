@@ -78,6 +78,9 @@ CASES = {
     # C = 512: two 256-row chunks per expert; 3 K steps in the down pass (I = 192)
     "bf16_C512": MoEShape("bf16_C512", T=1024, H=256, I=192, E=4, k=2, gate=GATE_SIGMOID, n_shared=1,
                           I_shared=192, cfg_id=406),
+    # C = 300: every group, the shared one too, in the 320-row chunk list
+    "bf16_C300": MoEShape("bf16_C300", T=1200, H=256, I=128, E=8, k=2, gate=GATE_SIGMOID, n_shared=1,
+                          I_shared=128, cfg_id=407),
     "deepseek_v3_ec_narrow_experts": MoEShape("deepseek_v3_ec_narrow_experts", T=8192, H=7168, I=64, E=256, k=8,
                                               gate=GATE_SIGMOID, routed_scaling_factor=2.5, n_shared=1,
                                               I_shared=64, cfg_id=405),

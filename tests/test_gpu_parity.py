@@ -26,10 +26,12 @@ SMALL = {
                                    capacity_factor=1.25, logit_skew=True, cfg_id=103),
     "bf16_capacity_k3": MoEShape("bf16_capacity_k3", T=513, H=192, I=256, E=12, k=3, gate=GATE_SIGMOID,
                                  capacity_factor=0.8, cfg_id=104),
-    # ~640 rows per expert: the 256-row tile, three balanced chunks per expert,
-    # an odd number of 64-wide K steps in the down pass (I = 320)
-    "bf16_multichunk_256": MoEShape("bf16_multichunk_256", T=2560, H=256, I=320, E=8, k=2, gate=GATE_SIGMOID,
-                                    routed_scaling_factor=2.5, n_shared=1, I_shared=320, cfg_id=113),
+    # ~512 rows per expert (this seed: 477..533): experts of 321..512 rows go to the
+    # 256-row tile as two balanced chunks, those of 513..640 to the 320-row tile,
+    # the shared one (2048 rows) to the 320-row tile, so both chunk lists are
+    # used; an odd number of 64-wide K steps in the down pass (I = 320)
+    "bf16_two_chunk_lists": MoEShape("bf16_two_chunk_lists", T=2048, H=256, I=320, E=8, k=2, gate=GATE_SIGMOID,
+                                     routed_scaling_factor=2.5, n_shared=1, I_shared=320, cfg_id=113),
     "fp32_tiny": WORKLOADS[TINY],
     "fp32_sigmoid_shared_capacity": MoEShape("fp32_sigmoid_shared_capacity", T=200, H=192, I=128, E=8, k=3,
                                              gate=GATE_SIGMOID, capacity_factor=1.0, n_shared=1, I_shared=128,

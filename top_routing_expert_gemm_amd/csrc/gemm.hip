@@ -485,14 +485,15 @@ __device__ __forceinline__ void rs_read1(RsOps& o, const u32x4* L, const int (&r
 }
 
 // One 16-wide substep SS of K step t (in buffer S), with the memory traffic of
-// the pipeline interleaved between its MFMAs in a fixed order:
+// the pipeline interleaved between its MFMAs (each kind spread over the
+// substep in proportion, rs_side_table):
 //   SS 0: the first half of the global loads of step t + 2 (register set S,
-//         whose previous contents were stored in the step before), operand
-//         reads of SS 1;
-//   SS 1: the second half of those loads, operand reads of SS 2;
-//   SS 2: operand reads of SS 3, then the LDS stores of step t + 1 (register set
-//         1 - S into buffer 1 - S, whose last reads were before the previous
-//         barrier);
+//         whose previous contents were stored in the step before), and the
+//         operand reads of SS 1;
+//   SS 1: the second half of those loads, and the operand reads of SS 2;
+//   SS 2: the operand reads of SS 3, and the LDS stores of step t + 1 (register
+//         set 1 - S into buffer 1 - S, whose last reads were before the
+//         previous barrier);
 //   SS 3: half the MFMAs, the barrier (step t + 1 is in LDS, step t's reads are
 //         done), then the operand reads of SS 0 of step t + 1.
 // Each group (side operations + one MFMA) is fenced with a scheduling barrier so
