@@ -29,10 +29,14 @@ struct Chunk {
   int32_t pad[3];
 };
 
-// M-tile heights of the two bf16 grouped GEMM kernels: register-staged (256)
-// and direct-to-LDS (320).
+// M-tile heights of the bf16 grouped GEMM chunk lists: 256 rows (register-
+// staged, one wave per SIMD) and 320 rows (register-staged with two waves per
+// SIMD where its 32-bit offsets fit, else direct-to-LDS).
 #ifndef MOE_GEMM_RS
 #define MOE_GEMM_RS 1
+#endif
+#ifndef MOE_GEMM_WS
+#define MOE_GEMM_WS 1
 #endif
 constexpr int kGemmBMrs = 256;
 constexpr int kGemmBMdl = 320;

@@ -517,7 +517,7 @@ constexpr RsSideTable<NL + NR + NS> rs_side_table() {
     const int64_t dl_n = il < NL ? 2 * il + 1 : 4, dl_d = il < NL ? 2 * NL : 1;
     const int64_t dr_n = ir < NR ? 2 * ir + 1 : 4, dr_d = ir < NR ? 2 * NR : 1;
     const int64_t ds_n = is < NS ? 2 * is + 1 : 4, ds_d = is < NS ? 2 * NS : 1;
-    int k;
+    int k = 2;
     if (dr_n * dl_d <= dl_n * dr_d && dr_n * ds_d <= ds_n * dr_d) k = 1;
     else if (dl_n * ds_d <= ds_n * dl_d) k = 0;
     else k = 2;
@@ -792,6 +792,347 @@ bool rs_fits(const GemmArgs& a) {
   return a.K >= 2 * RBK && a.a_rows * a.K * 2 < lim && a.N * a.K * 2 < lim;
 }
 
+// ------------------------------------ bf16 register-staged path, 320-row tile
+// The 320 x 256 tile of the direct-to-LDS kernel with whole-line loads of both
+// operands: eight waves (two per SIMD) in a 2 x 4 grid, wave (wm, wn) computing
+// the interleaved 32-row blocks 2a + wm (a < 5) against 64 tile columns
+// (gate/up: 32 gate columns and the same 32 up columns), 160 accumulators per
+// lane.
+//
+// Every load is a whole 128-byte row piece (K steps of 64), for both operands:
+// on this memory system a CU's loads are limited by the requests it has in
+// flight, so a weight row fetched in two 64-byte halves costs nearly twice
+// what one line does.  Two 72 KB LDS buffers; the loads of step t + 1 are
+// issued at the start of step t into the other buffer (free since the barrier
+// that began step t): the weights straight to LDS (buffer_load ... lds, chunks
+// swizzled on the source side), then the token rows into registers (the
+// faster path for L2 hits), written to LDS at the end of step t; one barrier
+// per step publishes both.  Within a 16-wide substep the MFMAs run
+// column-major (every row block against B column block 0, then against block
+// 1), so the next substep's operands are read into the registers the current
+// ones free: B block 0 half-way through, each A block after its last use, B
+// block 1 at the end.
+constexpr int WWM = 2;             // wave rows
+constexpr int WWN = 4;             // wave columns
+constexpr int WNT = 64 * WWM * WWN;
+constexpr int WRB = 5;             // 32-row blocks per wave (at most)
+constexpr int WNB = 2;             // 32-column blocks per wave
+constexpr int WBM = 32 * WRB * WWM;  // 320
+constexpr int WBN = 32 * WNB * WWN;  // 256
+constexpr int WNAL = WBM / 64;     // A loads per lane per K step (64 rows each)
+constexpr int WNBL = WBN / 64;     // B loads per lane per K step
+constexpr int WROWS = WBM + WBN;   // 128-byte LDS rows per buffer
+static_assert(kGemmBMdl == WBM, "chunk lists are cut to the tile height");
+static_assert(2 * WROWS * 128 <= 160 * 1024, "LDS");
+static_assert(WNAL * 64 * 8 * 16 == WBM * 128 && WNBL * 64 * 8 * 16 == WBN * 128, "one 16-byte piece per lane per load");
+
+// The two buffers as distinct objects, so the compiler can tell the direct
+// writes in flight to one from the reads of the other.
+__shared__ __attribute__((aligned(1024))) u32x4 sW0[WROWS * 8];
+__shared__ __attribute__((aligned(1024))) u32x4 sW1[WROWS * 8];
+template <int S>
+__device__ __forceinline__ u32x4* stW() {
+  if constexpr (S == 0) return sW0;
+  else return sW1;
+}
+
+// Barrier that publishes a step: all of this wave's loads (the direct weight
+// writes included, whatever order they were issued in) and LDS operations
+// done, then the workgroup barrier.
+__device__ __forceinline__ void ws_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct WsRegs {
+  u32x4 a[WNAL];
+};
+
+struct WsSrc {
+  __amdgpu_buffer_rsrc_t ra;   // A rows
+  __amdgpu_buffer_rsrc_t rb;   // this wave's weight matrix (gate/up: gate for waves 0-3, up for 4-7)
+  uint32_t aoff[WNAL];         // per-lane byte offset of A piece i at k = 0
+  uint32_t boff;               // per-lane byte offset of the (source-swizzled) piece within a B row group
+  uint32_t bgrp[WNBL];         // byte offset of B row group j within the matrix
+  int wave;
+};
+
+struct WsOps {
+  bf16x8 a[WRB];
+  bf16x8 b[WNB];
+};
+
+// Load q of K step kt into buffer S: q < WNBL the weights of B row group q
+// (LDS rows WBM + 64 q + 8 wave .. + 8, one 1 KB block per wave), else the
+// token rows of A group q - WNBL into registers.
+template <int S, int NAL>
+__device__ __forceinline__ void ws_load1(WsRegs& r, const WsSrc& s, int kt, int q) {
+  const int ko = kt * (RBK * 2);
+  if (q < WNBL)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rb, (lds_void*)(stW<S>() + (WNAL + q) * 512 + s.wave * 64), 16, s.boff,
+                                             (int)s.bgrp[q] + ko, 0, kNonTemporal);
+  else
+    r.a[q - WNBL] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, s.aoff[q - WNBL], ko, 0);
+}
+
+// LDS store q of the token rows into buffer S (LDS rows 64 q + lane row); wr =
+// this lane's slot within a 64-row group.
+template <int S>
+__device__ __forceinline__ void ws_store1(const WsRegs& r, int wr, int q) {
+  stW<S>()[q * 512 + wr] = r.a[q];
+}
+
+// One 16-wide substep SS of K step t (buffer S):
+//   first half, MFMAs (a, 0) for every row block a, carrying
+//     SS 0: the loads of step t + 1 (weights first, then token rows);
+//     SS 3: the LDS stores of step t + 1's token rows into the other buffer,
+//           then the barrier: step t + 1 is in LDS (every wave waits for all
+//           its loads first; by then the waits of its stores have normally
+//           covered them) and every wave is done reading step t - 1's data;
+//   then B block 0 of the next substep (from the other buffer after the
+//   barrier), and the second half, MFMAs (a, 1), each followed by the read of
+//   the next substep's A block a; last, B block 1 of the next substep.
+template <int MODE, int SS, int S, int NAL, int NRB, bool LOAD, bool STORE, bool NEXT>
+__device__ __forceinline__ void ws_substep(f32x16 (&acc)[WRB][WNB], WsRegs& R, WsOps (&op)[2], const WsSrc& src,
+                                           int t, int wr, const int (&ra)[4], const int (&rb)[4]) {
+  constexpr int P = (SS == 0 && LOAD) ? NAL + WNBL : ((SS == 3 && STORE) ? NAL : 0);  // first-half side operations
+  constexpr bool BAR = SS == 3 && NEXT;
+  constexpr bool RD = SS < 3 || NEXT;  // operands of the next substep are read here
+  const u32x4* Lr = (SS < 3) == (S == 0) ? sW0 : sW1;
+  constexpr int sr = (SS + 1) & 3;
+  WsOps& cur = op[SS & 1];
+  WsOps& nxt = op[(SS & 1) ^ 1];
+  auto side = [&](int q) {
+    if constexpr (SS == 0) ws_load1<1 - S, NAL>(R, src, t + 1, q);
+    else ws_store1<1 - S>(R, wr, q);
+  };
+  if constexpr (NRB == 0) {
+#pragma unroll
+    for (int q = 0; q < P; ++q) side(q);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    constexpr int PPM = (P + NRB - 1) / NRB;
+#pragma unroll
+    for (int m = 0; m < NRB; ++m) {
+#pragma unroll
+      for (int j = 0; j < PPM; ++j) {
+        const int q = m * P / NRB + j;
+        if (q < (m + 1) * P / NRB) side(q);
+      }
+      acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[m], cur.b[0], acc[m][0], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if constexpr (BAR) {
+    ws_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (RD && NRB > 0) nxt.b[0] = __builtin_bit_cast(bf16x8, Lr[rb[sr]]);
+#pragma unroll
+  for (int m = 0; m < NRB; ++m) {
+    acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[m], cur.b[1], acc[m][1], 0, 0, 0);
+    if constexpr (RD) nxt.a[m] = __builtin_bit_cast(bf16x8, Lr[ra[sr] + m * 512]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (RD && NRB > 0) nxt.b[1] = __builtin_bit_cast(bf16x8, Lr[rb[sr] + 256]);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MODE, int S, int NAL, int NRB, bool MORE>
+__device__ __forceinline__ void ws_step(f32x16 (&acc)[WRB][WNB], WsRegs& R, WsOps (&op)[2], const WsSrc& src, int t,
+                                        int wr, const int (&ra)[4], const int (&rb)[4]) {
+  ws_substep<MODE, 0, S, NAL, NRB, MORE, MORE, MORE>(acc, R, op, src, t, wr, ra, rb);
+  ws_substep<MODE, 1, S, NAL, NRB, MORE, MORE, MORE>(acc, R, op, src, t, wr, ra, rb);
+  ws_substep<MODE, 2, S, NAL, NRB, MORE, MORE, MORE>(acc, R, op, src, t, wr, ra, rb);
+  ws_substep<MODE, 3, S, NAL, NRB, MORE, MORE, MORE>(acc, R, op, src, t, wr, ra, rb);
+}
+
+// The K loop over nk >= 2 steps (nk odd iff ODD); MORE = a step follows.
+template <int MODE, int NAL, int NRB, bool ODD>
+__device__ __forceinline__ void ws_kloop(f32x16 (&acc)[WRB][WNB], const WsSrc& src, int nk, int wr,
+                                         const int (&ra)[4], const int (&rb)[4]) {
+  WsRegs R;
+  WsOps op[2];
+#pragma unroll
+  for (int q = 0; q < NAL + WNBL; ++q) ws_load1<0, NAL>(R, src, 0, q);
+#pragma unroll
+  for (int q = 0; q < NAL; ++q) ws_store1<0>(R, wr, q);
+  ws_barrier();
+  if constexpr (NRB > 0) {
+    op[0].b[0] = __builtin_bit_cast(bf16x8, sW0[rb[0]]);
+#pragma unroll
+    for (int m = 0; m < NRB; ++m) op[0].a[m] = __builtin_bit_cast(bf16x8, sW0[ra[0] + m * 512]);
+    op[0].b[1] = __builtin_bit_cast(bf16x8, sW0[rb[0] + 256]);
+  }
+  constexpr int TAIL = ODD ? 3 : 2;  // steps after the loop, the first in buffer 0
+  int t = 0;
+  for (; t + TAIL < nk; t += 2) {
+    ws_step<MODE, 0, NAL, NRB, true>(acc, R, op, src, t, wr, ra, rb);
+    ws_step<MODE, 1, NAL, NRB, true>(acc, R, op, src, t + 1, wr, ra, rb);
+  }
+  if constexpr (ODD) {
+    ws_step<MODE, 0, NAL, NRB, true>(acc, R, op, src, t, wr, ra, rb);
+    ws_step<MODE, 1, NAL, NRB, true>(acc, R, op, src, t + 1, wr, ra, rb);
+    ws_step<MODE, 0, NAL, NRB, false>(acc, R, op, src, t + 2, wr, ra, rb);
+  } else {
+    ws_step<MODE, 0, NAL, NRB, true>(acc, R, op, src, t, wr, ra, rb);
+    ws_step<MODE, 1, NAL, NRB, false>(acc, R, op, src, t + 1, wr, ra, rb);
+  }
+}
+
+// K loop and epilogue of one wave, which multiplies NRB row blocks (tile rows
+// (2a + wm) * 32 .. + 32); NAL 64-row A groups are fetched for the workgroup.
+template <int MODE, int NAL, int NRB, bool ODD>
+__device__ __forceinline__ void ws_wave(const GemmArgs& a, const Chunk& ch, int nt, const WsSrc& src, int wave,
+                                        int wm, int wn, int lane, int wr) {
+  const int64_t N = a.N;
+  const int nk = (int)(a.K / RBK);
+  int ra[4], rb[4];
+  const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = (2 * s + h) ^ swz8(l32);
+    ra[s] = (wm * 32 + l32) * 8 + c;
+    rb[s] = (WBM + wn * 64 + l32) * 8 + c;
+  }
+  f32x16 acc[WRB][WNB];
+#pragma unroll
+  for (int i = 0; i < WRB; ++i)
+#pragma unroll
+    for (int j = 0; j < WNB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  ws_kloop<MODE, NAL, NRB, ODD>(acc, src, nk, wr, ra, rb);
+
+  // ---- epilogue: as the 256-row register-staged kernel, through a 16 KB
+  // wave-private LDS region (waves 0-3 in the first buffer, 4-7 in the second;
+  // free once every wave is past the K loop)
+  rs_barrier();
+  if constexpr (NRB > 0) {
+    constexpr int NJ = MODE == MODE_GATEUP ? 1 : WNB;  // 32-column output blocks of this wave
+    constexpr int LDSR = NJ * 32 + 8;                   // padded LDS row (elements)
+    constexpr int CPRW = NJ * 4;                        // 16-byte chunks per output row
+    static_assert(32 * LDSR * 2 <= 16 * 1024 && 4 * 16 * 1024 <= WROWS * 128, "epilogue region");
+    uint16_t* tile = reinterpret_cast<uint16_t*>(wave < 4 ? sW0 : sW1) + (wave & 3) * (16 * 1024 / 2);
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    const int64_t n0 = MODE == MODE_GATEUP ? (int64_t)nt * 128 + wn * 32 : (int64_t)nt * WBN + wn * 64;
+    const bool odd = l32 & 1;
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int p = 0; p < 4; p += 2) {
+            float va, vb;
+            if (MODE == MODE_GATEUP) {
+              va = silu_f(acc[i][0][4 * g + p]) * acc[i][1][4 * g + p];
+              vb = silu_f(acc[i][0][4 * g + p + 1]) * acc[i][1][4 * g + p + 1];
+            } else {
+              va = acc[i][jj][4 * g + p];
+              vb = acc[i][jj][4 * g + p + 1];
+            }
+            // even lane: (row r, cols c, c+1); odd lane: (row r+1, cols c-1, c)
+            const float x = __shfl_xor(odd ? va : vb, 1, kWave);
+            const int r = 8 * g + 4 * h + p;
+            const uint32_t w = odd ? ((uint32_t)f32_to_bf16(x) | ((uint32_t)f32_to_bf16(vb) << 16))
+                                   : ((uint32_t)f32_to_bf16(va) | ((uint32_t)f32_to_bf16(x) << 16));
+            const int lr = odd ? r + 1 : r;
+            *reinterpret_cast<uint32_t*>(tile + lr * LDSR + jj * 32 + (l32 & ~1)) = w;
+          }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+      const int rowb = (2 * i + wm) * 32;
+#pragma unroll
+      for (int q = 0; q < 32 * CPRW / kWave; ++q) {
+        const int idx = q * kWave + lane;
+        const int lr = idx / CPRW, c16 = idx % CPRW;
+        const int row = rowb + lr;
+        const int64_t n = n0 + c16 * 8;
+        if (row < ch.nrows && n < N)
+          *reinterpret_cast<uint4*>(out + ((int64_t)ch.row0 + row) * N + n) =
+              *reinterpret_cast<const uint4*>(tile + lr * LDSR + c16 * 8);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block overwrites the region
+    }
+  }
+}
+
+template <int MODE, int NA, bool ODD>
+__device__ __forceinline__ void ws_run(const GemmArgs& a, const Chunk& ch, int nt) {
+  constexpr int NAL = (NA + 1) / 2;  // 64-row A groups fetched
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const bool shared = ch.group == a.E;
+  const int64_t K = a.K, N = a.N;
+
+  // loader: lane -> row (tid / 8) of each 64-row group, 16-byte chunk tid % 8
+  // (A: the logical chunk, stored at its swizzled slot wr; B: the physical
+  // slot, loaded from the logical chunk that belongs there)
+  const int lrow = tid >> 3, lchunk = tid & 7;
+  const int wr = lrow * 8 + (lchunk ^ swz8(lrow));
+  WsSrc src;
+  src.wave = wave;
+  src.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), (short)0, -1, kBufFlags);
+#pragma unroll
+  for (int i = 0; i < WNAL; ++i) {
+    const int rc = min(i * 64 + lrow, ch.nrows - 1);
+    const int64_t row = (int64_t)ch.row0 + rc;
+    int64_t sr = row;
+    if (a.gather != nullptr) sr = shared ? row - a.shared_row0 : (int64_t)a.gather[row];
+    src.aoff[i] = (uint32_t)((sr * K + lchunk * 8) * 2);  // A spans < 4 GiB (checked by the host)
+  }
+  const int64_t goff = shared ? 0 : (int64_t)ch.group * N * K;
+  const int bchunk = lchunk ^ swz8(lrow);
+  const uint16_t* W;
+  if (MODE == MODE_GATEUP) {
+    // B group j (tile rows 64 j .. 64 j + 63) is wave column j's 32 gate rows then
+    // its 32 up rows; a loader wave's 8 rows are all gate (waves 0-3) or all up
+    const bool up = wave >= 4;
+    W = static_cast<const uint16_t*>(up ? (shared ? a.ws1 : a.w1) : (shared ? a.ws0 : a.w0)) + goff;
+#pragma unroll
+    for (int j = 0; j < WNBL; ++j) src.bgrp[j] = (uint32_t)(min((int64_t)nt * 128 + j * 32, N - 32) * K * 2);
+    src.boff = (uint32_t)(((lrow & 31) * K + bchunk * 8) * 2);
+  } else {
+    W = static_cast<const uint16_t*>(shared ? a.ws0 : a.w0) + goff;
+    // a group past N is clamped to the last 64 rows (loaded, never stored); N is a multiple of 64
+#pragma unroll
+    for (int j = 0; j < WNBL; ++j) src.bgrp[j] = (uint32_t)(min((int64_t)nt * WBN + j * 64, N - 64) * K * 2);
+    src.boff = (uint32_t)((lrow * K + bchunk * 8) * 2);
+  }
+  src.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W), (short)0, -1, kBufFlags);
+
+  if (wm == 0) ws_wave<MODE, NAL, (NA + 1) / 2, ODD>(a, ch, nt, src, wave, wm, wn, lane, wr);
+  else ws_wave<MODE, NAL, NA / 2, ODD>(a, ch, nt, src, wave, wm, wn, lane, wr);
+}
+
+template <int MODE, bool ODD>
+__global__ __launch_bounds__(WNT) void grouped_gemm_ws(GemmArgs a, int n_tiles) {
+  const int V = *a.n_chunks * n_tiles;
+  int L;
+  if (!xcd_map(blockIdx.x, V, L)) return;
+  int ci, nt;
+  tile_of(L, n_tiles, a.chunks, ci, nt);
+  const Chunk ch = a.chunks[ci];
+  switch ((ch.nrows + 31) / 32) {
+    case 1: ws_run<MODE, 1, ODD>(a, ch, nt); break;
+    case 2: ws_run<MODE, 2, ODD>(a, ch, nt); break;
+    case 3: ws_run<MODE, 3, ODD>(a, ch, nt); break;
+    case 4: ws_run<MODE, 4, ODD>(a, ch, nt); break;
+    case 5: ws_run<MODE, 5, ODD>(a, ch, nt); break;
+    case 6: ws_run<MODE, 6, ODD>(a, ch, nt); break;
+    case 7: ws_run<MODE, 7, ODD>(a, ch, nt); break;
+    case 8: ws_run<MODE, 8, ODD>(a, ch, nt); break;
+    case 9: ws_run<MODE, 9, ODD>(a, ch, nt); break;
+    default: ws_run<MODE, 10, ODD>(a, ch, nt); break;
+  }
+  static_assert(WBM / 32 == 10, "row-block dispatch");
+}
+
 // ------------------------------------------------------ bf16 streaming path
 // Small batches (decode): every expert group has at most 16 rows, so the work is
 // streaming each touched expert's weights once.  One wave owns 16 output columns
@@ -1011,6 +1352,13 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
       hipLaunchKernelGGL((grouped_gemm_rs<MODE, true>), dim3((unsigned)grid), dim3(RNT), 0, s, a, n_tiles);
     else
       hipLaunchKernelGGL((grouped_gemm_rs<MODE, false>), dim3((unsigned)grid), dim3(RNT), 0, s, a, n_tiles);
+  } else if (dtype == MOE_BF16 && MOE_GEMM_WS && a.bm == WBM && rs_fits(a)) {
+    const int n_tiles = (int)(MODE == MODE_GATEUP ? (a.N + 127) / 128 : (a.N + WBN - 1) / WBN);
+    const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
+    if ((a.K / RBK) % 2)
+      hipLaunchKernelGGL((grouped_gemm_ws<MODE, true>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles);
+    else
+      hipLaunchKernelGGL((grouped_gemm_ws<MODE, false>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles);
   } else if (dtype == MOE_BF16) {
     const int n_tiles = (int)(MODE == MODE_GATEUP ? (a.N + 127) / 128 : (a.N + BN - 1) / BN);
     const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
