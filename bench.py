@@ -252,6 +252,10 @@ def main():
     rows = R + s.T * s.n_shared
     fl_gateup = 2.0 * rows * s.H * 2 * s.I
     fl_down = 2.0 * rows * s.I * s.H
+    # algorithmic bytes of the gate/up stage: the touched experts' gate and up
+    # weights once, x once, h written once
+    touched = int((counts > 0).sum()) + s.n_shared
+    by_gateup = float(touched * 2 * s.I * s.H * 2 + s.T * s.H * 2 + rows * s.I * 2)
     avg = {n: float(np.mean(v)) for n, v in st.items()}
     gateup_tflops = fl_gateup / (avg["gateup"] * 1e-3) / 1e12
     gemm_tflops = (fl_gateup + fl_down) / ((avg["gateup"] + avg["down"]) * 1e-3) / 1e12
@@ -267,10 +271,15 @@ def main():
                    "capacity_factor": None, "global_batch": s.T, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma",
                      "kernel": "gate/up+SwiGLU grouped GEMM stage: grouped_gemm_rs<0> (256-row chunk list) + "
-                               "grouped_gemm_bf16<0> (320-row chunk list), one launch each",
+                               "grouped_gemm_ws<0> (320-row chunk list), one launch each",
                      "achieved": gateup_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": gateup_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "flops_per_launch": fl_gateup, "avg_launch_ms": avg["gateup"]},
+                     "flops_per_launch": fl_gateup, "avg_launch_ms": avg["gateup"],
+                     "hbm_side": {"algorithmic_bytes_per_launch": by_gateup,
+                                  "achieved_GBps": by_gateup / (avg["gateup"] * 1e-3) / 1e9,
+                                  "frac_hbm_peak": by_gateup / (avg["gateup"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                  "intensity_flop_per_byte": fl_gateup / by_gateup,
+                                  "ridge_flop_per_byte": PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)}},
         "grouped_gemm": {"tflops": gemm_tflops, "frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS,
                          "flops": fl_gateup + fl_down, "ms": avg["gateup"] + avg["down"]},
         "stages_ms": avg,

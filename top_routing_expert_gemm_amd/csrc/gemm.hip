@@ -800,18 +800,22 @@ bool rs_fits(const GemmArgs& a) {
 // lane.
 //
 // Every load is a whole 128-byte row piece (K steps of 64), for both operands:
-// on this memory system a CU's loads are limited by the requests it has in
-// flight, so a weight row fetched in two 64-byte halves costs nearly twice
-// what one line does.  Two 72 KB LDS buffers; the loads of step t + 1 are
-// issued at the start of step t into the other buffer (free since the barrier
-// that began step t): the weights straight to LDS (buffer_load ... lds, chunks
-// swizzled on the source side), then the token rows into registers (the
-// faster path for L2 hits), written to LDS at the end of step t; one barrier
-// per step publishes both.  Within a 16-wide substep the MFMAs run
-// column-major (every row block against B column block 0, then against block
-// 1), so the next substep's operands are read into the registers the current
-// ones free: B block 0 half-way through, each A block after its last use, B
-// block 1 at the end.
+// a CU's loads are limited by the requests it has in flight more than by
+// bytes, and a step that fetches its weight rows as whole lines instead of
+// 64-byte halves moves the same bytes about 18% faster.  The weights go
+// straight to LDS (buffer_load ... lds, chunks swizzled on the source side)
+// through three 32 KB stages, issued two K steps ahead; the token rows (from
+// L2) go through registers, issued one step ahead, into one 40 KB buffer (the
+// faster path for L2 hits, and what leaves LDS room for the third weight
+// stage).  Two barriers per step: before the token rows of step t + 1
+// overwrite those of step t (every wave done reading them), and after (step
+// t + 1 complete in LDS).  Waves w and w + 4 share a SIMD and take the two row
+// halves, so a chunk of 9 row blocks keeps every SIMD equally busy.  Within a
+// 16-wide substep the MFMAs run column-major
+// (every row block against B column block 0, then against block 1), so the
+// next substep's operands are read into the registers the current ones free:
+// B block 0 half-way through, each A block after its last use, B block 1 at
+// the end.
 constexpr int WWM = 2;             // wave rows
 constexpr int WWN = 4;             // wave columns
 constexpr int WNT = 64 * WWM * WWN;
@@ -821,29 +825,22 @@ constexpr int WBM = 32 * WRB * WWM;  // 320
 constexpr int WBN = 32 * WNB * WWN;  // 256
 constexpr int WNAL = WBM / 64;     // A loads per lane per K step (64 rows each)
 constexpr int WNBL = WBN / 64;     // B loads per lane per K step
-constexpr int WROWS = WBM + WBN;   // 128-byte LDS rows per buffer
+constexpr int WBST = 3;            // weight stages
 static_assert(kGemmBMdl == WBM, "chunk lists are cut to the tile height");
-static_assert(2 * WROWS * 128 <= 160 * 1024, "LDS");
+static_assert(WBM * 128 + WBST * WBN * 128 <= 160 * 1024, "LDS");
 static_assert(WNAL * 64 * 8 * 16 == WBM * 128 && WNBL * 64 * 8 * 16 == WBN * 128, "one 16-byte piece per lane per load");
 
-// The two buffers as distinct objects, so the compiler can tell the direct
-// writes in flight to one from the reads of the other.
-__shared__ __attribute__((aligned(1024))) u32x4 sW0[WROWS * 8];
-__shared__ __attribute__((aligned(1024))) u32x4 sW1[WROWS * 8];
-template <int S>
-__device__ __forceinline__ u32x4* stW() {
-  if constexpr (S == 0) return sW0;
-  else return sW1;
-}
-
-// Barrier that publishes a step: all of this wave's loads (the direct weight
-// writes included, whatever order they were issued in) and LDS operations
-// done, then the workgroup barrier.
-__device__ __forceinline__ void ws_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+// Distinct objects, so the compiler can tell the direct writes in flight to
+// one stage from the reads of another.
+__shared__ __attribute__((aligned(1024))) u32x4 sWA[WBM * 8];
+__shared__ __attribute__((aligned(1024))) u32x4 sWB0[WBN * 8];
+__shared__ __attribute__((aligned(1024))) u32x4 sWB1[WBN * 8];
+__shared__ __attribute__((aligned(1024))) u32x4 sWB2[WBN * 8];
+template <int B>
+__device__ __forceinline__ u32x4* stWB() {
+  if constexpr (B == 0) return sWB0;
+  else if constexpr (B == 1) return sWB1;
+  else return sWB2;
 }
 
 struct WsRegs {
@@ -864,54 +861,56 @@ struct WsOps {
   bf16x8 b[WNB];
 };
 
-// Load q of K step kt into buffer S: q < WNBL the weights of B row group q
-// (LDS rows WBM + 64 q + 8 wave .. + 8, one 1 KB block per wave), else the
-// token rows of A group q - WNBL into registers.
-template <int S, int NAL>
-__device__ __forceinline__ void ws_load1(WsRegs& r, const WsSrc& s, int kt, int q) {
-  const int ko = kt * (RBK * 2);
-  if (q < WNBL)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rb, (lds_void*)(stW<S>() + (WNAL + q) * 512 + s.wave * 64), 16, s.boff,
-                                             (int)s.bgrp[q] + ko, 0, kNonTemporal);
-  else
-    r.a[q - WNBL] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, s.aoff[q - WNBL], ko, 0);
+// Token rows of A group i (tile rows 64 i + lane row) of K step kt into registers.
+__device__ __forceinline__ void ws_load_a(WsRegs& r, const WsSrc& s, int kt, int i) {
+  r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, s.aoff[i], kt * (RBK * 2), 0);
+}
+// Weights of B row group j of K step kt straight into stage B (rows 64 j +
+// 8 wave .. + 8: one 1 KB block per wave).
+template <int B>
+__device__ __forceinline__ void ws_load_b(const WsSrc& s, int kt, int j) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rb, (lds_void*)(stWB<B>() + j * 512 + s.wave * 64), 16, s.boff,
+                                           (int)s.bgrp[j] + kt * (RBK * 2), 0, kNonTemporal);
 }
 
-// LDS store q of the token rows into buffer S (LDS rows 64 q + lane row); wr =
-// this lane's slot within a 64-row group.
-template <int S>
-__device__ __forceinline__ void ws_store1(const WsRegs& r, int wr, int q) {
-  stW<S>()[q * 512 + wr] = r.a[q];
-}
-
-// One 16-wide substep SS of K step t (buffer S):
-//   first half, MFMAs (a, 0) for every row block a, carrying
-//     SS 0: the loads of step t + 1 (weights first, then token rows);
-//     SS 3: the LDS stores of step t + 1's token rows into the other buffer,
-//           then the barrier: step t + 1 is in LDS (every wave waits for all
-//           its loads first; by then the waits of its stores have normally
-//           covered them) and every wave is done reading step t - 1's data;
-//   then B block 0 of the next substep (from the other buffer after the
-//   barrier), and the second half, MFMAs (a, 1), each followed by the read of
-//   the next substep's A block a; last, B block 1 of the next substep.
-template <int MODE, int SS, int S, int NAL, int NRB, bool LOAD, bool STORE, bool NEXT>
+// One 16-wide substep SS of K step t, reading weight stage BS:
+//   SS 0, first half (MFMAs (a, 0) for every row block a): the loads of the
+//         token rows of step t + 1 (LA) and then of the weights of step t + 2
+//         into stage (BS + 2) % 3 (LB), each fenced so the issue order holds;
+//   SS 3 (NEXT): the first barrier (every wave is done reading step t's token
+//         rows: its last reads were in SS 2), then the first half carrying the
+//         stores of step t + 1's token rows, then the second barrier, after
+//         waiting for all of this wave's loads but the weights of step t + 2
+//         (issued last): step t + 1 is complete in LDS;
+//   then B block 0 of the next substep (step t + 1's stage in SS 3), and the
+//   second half, MFMAs (a, 1), each followed by the read of the next
+//   substep's A block a; last, B block 1 of the next substep.
+template <int MODE, int SS, int BS, int NAL, int NRB, bool LA, bool LB, bool NEXT>
 __device__ __forceinline__ void ws_substep(f32x16 (&acc)[WRB][WNB], WsRegs& R, WsOps (&op)[2], const WsSrc& src,
                                            int t, int wr, const int (&ra)[4], const int (&rb)[4]) {
-  constexpr int P = (SS == 0 && LOAD) ? NAL + WNBL : ((SS == 3 && STORE) ? NAL : 0);  // first-half side operations
-  constexpr bool BAR = SS == 3 && NEXT;
+  constexpr int NA0 = (SS == 0 && LA) ? NAL : 0;
+  constexpr int P = SS == 0 ? NA0 + (LB ? WNBL : 0) : ((SS == 3 && NEXT) ? NAL : 0);  // first-half side operations
   constexpr bool RD = SS < 3 || NEXT;  // operands of the next substep are read here
-  const u32x4* Lr = (SS < 3) == (S == 0) ? sW0 : sW1;
+  const u32x4* Lb = stWB<SS < 3 ? BS : (BS + 1) % WBST>();
   constexpr int sr = (SS + 1) & 3;
   WsOps& cur = op[SS & 1];
   WsOps& nxt = op[(SS & 1) ^ 1];
   auto side = [&](int q) {
-    if constexpr (SS == 0) ws_load1<1 - S, NAL>(R, src, t + 1, q);
-    else ws_store1<1 - S>(R, wr, q);
+    if constexpr (SS == 0) {
+      if (q < NA0) ws_load_a(R, src, t + 1, q);
+      else ws_load_b<(BS + 2) % WBST>(src, t + 2, q - NA0);
+    } else {
+      sWA[q * 512 + wr] = R.a[q];
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
+  if constexpr (SS == 3 && NEXT) {
+    rs_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if constexpr (NRB == 0) {
 #pragma unroll
     for (int q = 0; q < P; ++q) side(q);
-    __builtin_amdgcn_sched_barrier(0);
   } else {
     constexpr int PPM = (P + NRB - 1) / NRB;
 #pragma unroll
@@ -925,66 +924,77 @@ __device__ __forceinline__ void ws_substep(f32x16 (&acc)[WRB][WNB], WsRegs& R, W
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if constexpr (BAR) {
-    ws_barrier();
+  if constexpr (SS == 3 && NEXT) {
+    stage_barrier<LB ? WNBL : 0>();
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (RD && NRB > 0) nxt.b[0] = __builtin_bit_cast(bf16x8, Lr[rb[sr]]);
+  if constexpr (RD && NRB > 0) nxt.b[0] = __builtin_bit_cast(bf16x8, Lb[rb[sr]]);
 #pragma unroll
   for (int m = 0; m < NRB; ++m) {
     acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[m], cur.b[1], acc[m][1], 0, 0, 0);
-    if constexpr (RD) nxt.a[m] = __builtin_bit_cast(bf16x8, Lr[ra[sr] + m * 512]);
+    if constexpr (RD) nxt.a[m] = __builtin_bit_cast(bf16x8, sWA[ra[sr] + m * 512]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (RD && NRB > 0) nxt.b[1] = __builtin_bit_cast(bf16x8, Lr[rb[sr] + 256]);
+  if constexpr (RD && NRB > 0) nxt.b[1] = __builtin_bit_cast(bf16x8, Lb[rb[sr] + 256]);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MODE, int S, int NAL, int NRB, bool MORE>
+template <int MODE, int BS, int NAL, int NRB, bool LA, bool LB, bool NEXT>
 __device__ __forceinline__ void ws_step(f32x16 (&acc)[WRB][WNB], WsRegs& R, WsOps (&op)[2], const WsSrc& src, int t,
                                         int wr, const int (&ra)[4], const int (&rb)[4]) {
-  ws_substep<MODE, 0, S, NAL, NRB, MORE, MORE, MORE>(acc, R, op, src, t, wr, ra, rb);
-  ws_substep<MODE, 1, S, NAL, NRB, MORE, MORE, MORE>(acc, R, op, src, t, wr, ra, rb);
-  ws_substep<MODE, 2, S, NAL, NRB, MORE, MORE, MORE>(acc, R, op, src, t, wr, ra, rb);
-  ws_substep<MODE, 3, S, NAL, NRB, MORE, MORE, MORE>(acc, R, op, src, t, wr, ra, rb);
+  ws_substep<MODE, 0, BS, NAL, NRB, LA, LB, NEXT>(acc, R, op, src, t, wr, ra, rb);
+  ws_substep<MODE, 1, BS, NAL, NRB, LA, LB, NEXT>(acc, R, op, src, t, wr, ra, rb);
+  ws_substep<MODE, 2, BS, NAL, NRB, LA, LB, NEXT>(acc, R, op, src, t, wr, ra, rb);
+  ws_substep<MODE, 3, BS, NAL, NRB, LA, LB, NEXT>(acc, R, op, src, t, wr, ra, rb);
 }
 
-// The K loop over nk >= 2 steps (nk odd iff ODD); MORE = a step follows.
-template <int MODE, int NAL, int NRB, bool ODD>
+// The K loop over nk >= 2 steps, R3 = (nk - 2) % 3: steps 0 .. nk - 3 load both
+// operands ahead (the loop, unrolled by the three weight stages, then R3 more),
+// step nk - 2 loads only the token rows of the last step, step nk - 1 nothing.
+template <int MODE, int NAL, int NRB, int R3>
 __device__ __forceinline__ void ws_kloop(f32x16 (&acc)[WRB][WNB], const WsSrc& src, int nk, int wr,
                                          const int (&ra)[4], const int (&rb)[4]) {
   WsRegs R;
   WsOps op[2];
 #pragma unroll
-  for (int q = 0; q < NAL + WNBL; ++q) ws_load1<0, NAL>(R, src, 0, q);
+  for (int i = 0; i < NAL; ++i) {
+    ws_load_a(R, src, 0, i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
-  for (int q = 0; q < NAL; ++q) ws_store1<0>(R, wr, q);
-  ws_barrier();
+  for (int j = 0; j < WNBL; ++j) {
+    ws_load_b<0>(src, 0, j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int j = 0; j < WNBL; ++j) {
+    ws_load_b<1>(src, 1, j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < NAL; ++i) sWA[i * 512 + wr] = R.a[i];
+  stage_barrier<WNBL>();  // token rows and weights of step 0 in LDS; step 1's weights may be in flight
   if constexpr (NRB > 0) {
-    op[0].b[0] = __builtin_bit_cast(bf16x8, sW0[rb[0]]);
+    op[0].b[0] = __builtin_bit_cast(bf16x8, sWB0[rb[0]]);
 #pragma unroll
-    for (int m = 0; m < NRB; ++m) op[0].a[m] = __builtin_bit_cast(bf16x8, sW0[ra[0] + m * 512]);
-    op[0].b[1] = __builtin_bit_cast(bf16x8, sW0[rb[0] + 256]);
+    for (int m = 0; m < NRB; ++m) op[0].a[m] = __builtin_bit_cast(bf16x8, sWA[ra[0] + m * 512]);
+    op[0].b[1] = __builtin_bit_cast(bf16x8, sWB0[rb[0] + 256]);
   }
-  constexpr int TAIL = ODD ? 3 : 2;  // steps after the loop, the first in buffer 0
   int t = 0;
-  for (; t + TAIL < nk; t += 2) {
-    ws_step<MODE, 0, NAL, NRB, true>(acc, R, op, src, t, wr, ra, rb);
-    ws_step<MODE, 1, NAL, NRB, true>(acc, R, op, src, t + 1, wr, ra, rb);
+  for (; t + 3 <= nk - 2; t += 3) {
+    ws_step<MODE, 0, NAL, NRB, true, true, true>(acc, R, op, src, t, wr, ra, rb);
+    ws_step<MODE, 1, NAL, NRB, true, true, true>(acc, R, op, src, t + 1, wr, ra, rb);
+    ws_step<MODE, 2, NAL, NRB, true, true, true>(acc, R, op, src, t + 2, wr, ra, rb);
   }
-  if constexpr (ODD) {
-    ws_step<MODE, 0, NAL, NRB, true>(acc, R, op, src, t, wr, ra, rb);
-    ws_step<MODE, 1, NAL, NRB, true>(acc, R, op, src, t + 1, wr, ra, rb);
-    ws_step<MODE, 0, NAL, NRB, false>(acc, R, op, src, t + 2, wr, ra, rb);
-  } else {
-    ws_step<MODE, 0, NAL, NRB, true>(acc, R, op, src, t, wr, ra, rb);
-    ws_step<MODE, 1, NAL, NRB, false>(acc, R, op, src, t + 1, wr, ra, rb);
-  }
+  if constexpr (R3 >= 1) ws_step<MODE, 0, NAL, NRB, true, true, true>(acc, R, op, src, t, wr, ra, rb);
+  if constexpr (R3 >= 2) ws_step<MODE, 1, NAL, NRB, true, true, true>(acc, R, op, src, t + 1, wr, ra, rb);
+  ws_step<MODE, R3 % WBST, NAL, NRB, true, false, true>(acc, R, op, src, t + R3, wr, ra, rb);
+  ws_step<MODE, (R3 + 1) % WBST, NAL, NRB, false, false, false>(acc, R, op, src, t + R3 + 1, wr, ra, rb);
 }
 
 // K loop and epilogue of one wave, which multiplies NRB row blocks (tile rows
 // (2a + wm) * 32 .. + 32); NAL 64-row A groups are fetched for the workgroup.
-template <int MODE, int NAL, int NRB, bool ODD>
+template <int MODE, int NAL, int NRB, int R3>
 __device__ __forceinline__ void ws_wave(const GemmArgs& a, const Chunk& ch, int nt, const WsSrc& src, int wave,
                                         int wm, int wn, int lane, int wr) {
   const int64_t N = a.N;
@@ -995,7 +1005,7 @@ __device__ __forceinline__ void ws_wave(const GemmArgs& a, const Chunk& ch, int 
   for (int s = 0; s < 4; ++s) {
     const int c = (2 * s + h) ^ swz8(l32);
     ra[s] = (wm * 32 + l32) * 8 + c;
-    rb[s] = (WBM + wn * 64 + l32) * 8 + c;
+    rb[s] = (wn * 64 + l32) * 8 + c;
   }
   f32x16 acc[WRB][WNB];
 #pragma unroll
@@ -1005,18 +1015,20 @@ __device__ __forceinline__ void ws_wave(const GemmArgs& a, const Chunk& ch, int 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  ws_kloop<MODE, NAL, NRB, ODD>(acc, src, nk, wr, ra, rb);
+  ws_kloop<MODE, NAL, NRB, R3>(acc, src, nk, wr, ra, rb);
 
   // ---- epilogue: as the 256-row register-staged kernel, through a 16 KB
-  // wave-private LDS region (waves 0-3 in the first buffer, 4-7 in the second;
-  // free once every wave is past the K loop)
+  // wave-private LDS region (two per 32 KB weight stage, waves 6-7 in the token
+  // row buffer; free once every wave is past the K loop)
   rs_barrier();
   if constexpr (NRB > 0) {
     constexpr int NJ = MODE == MODE_GATEUP ? 1 : WNB;  // 32-column output blocks of this wave
     constexpr int LDSR = NJ * 32 + 8;                   // padded LDS row (elements)
     constexpr int CPRW = NJ * 4;                        // 16-byte chunks per output row
-    static_assert(32 * LDSR * 2 <= 16 * 1024 && 4 * 16 * 1024 <= WROWS * 128, "epilogue region");
-    uint16_t* tile = reinterpret_cast<uint16_t*>(wave < 4 ? sW0 : sW1) + (wave & 3) * (16 * 1024 / 2);
+    static_assert(32 * LDSR * 2 <= 16 * 1024 && 2 * 16 * 1024 <= WBN * 128 && 2 * 16 * 1024 <= WBM * 128,
+                  "epilogue region");
+    u32x4* reg = wave < 2 ? sWB0 : wave < 4 ? sWB1 : wave < 6 ? sWB2 : sWA;
+    uint16_t* tile = reinterpret_cast<uint16_t*>(reg) + (wave & 1) * (16 * 1024 / 2);
     uint16_t* out = static_cast<uint16_t*>(a.out);
     const int64_t n0 = MODE == MODE_GATEUP ? (int64_t)nt * 128 + wn * 32 : (int64_t)nt * WBN + wn * 64;
     const bool odd = l32 & 1;
@@ -1061,12 +1073,12 @@ __device__ __forceinline__ void ws_wave(const GemmArgs& a, const Chunk& ch, int 
   }
 }
 
-template <int MODE, int NA, bool ODD>
+template <int MODE, int NA, int R3>
 __device__ __forceinline__ void ws_run(const GemmArgs& a, const Chunk& ch, int nt) {
   constexpr int NAL = (NA + 1) / 2;  // 64-row A groups fetched
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const bool shared = ch.group == a.E;
   const int64_t K = a.K, N = a.N;
 
@@ -1106,11 +1118,11 @@ __device__ __forceinline__ void ws_run(const GemmArgs& a, const Chunk& ch, int n
   }
   src.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W), (short)0, -1, kBufFlags);
 
-  if (wm == 0) ws_wave<MODE, NAL, (NA + 1) / 2, ODD>(a, ch, nt, src, wave, wm, wn, lane, wr);
-  else ws_wave<MODE, NAL, NA / 2, ODD>(a, ch, nt, src, wave, wm, wn, lane, wr);
+  if (wm == 0) ws_wave<MODE, NAL, (NA + 1) / 2, R3>(a, ch, nt, src, wave, wm, wn, lane, wr);
+  else ws_wave<MODE, NAL, NA / 2, R3>(a, ch, nt, src, wave, wm, wn, lane, wr);
 }
 
-template <int MODE, bool ODD>
+template <int MODE, int R3>
 __global__ __launch_bounds__(WNT) void grouped_gemm_ws(GemmArgs a, int n_tiles) {
   const int V = *a.n_chunks * n_tiles;
   int L;
@@ -1119,16 +1131,16 @@ __global__ __launch_bounds__(WNT) void grouped_gemm_ws(GemmArgs a, int n_tiles) 
   tile_of(L, n_tiles, a.chunks, ci, nt);
   const Chunk ch = a.chunks[ci];
   switch ((ch.nrows + 31) / 32) {
-    case 1: ws_run<MODE, 1, ODD>(a, ch, nt); break;
-    case 2: ws_run<MODE, 2, ODD>(a, ch, nt); break;
-    case 3: ws_run<MODE, 3, ODD>(a, ch, nt); break;
-    case 4: ws_run<MODE, 4, ODD>(a, ch, nt); break;
-    case 5: ws_run<MODE, 5, ODD>(a, ch, nt); break;
-    case 6: ws_run<MODE, 6, ODD>(a, ch, nt); break;
-    case 7: ws_run<MODE, 7, ODD>(a, ch, nt); break;
-    case 8: ws_run<MODE, 8, ODD>(a, ch, nt); break;
-    case 9: ws_run<MODE, 9, ODD>(a, ch, nt); break;
-    default: ws_run<MODE, 10, ODD>(a, ch, nt); break;
+    case 1: ws_run<MODE, 1, R3>(a, ch, nt); break;
+    case 2: ws_run<MODE, 2, R3>(a, ch, nt); break;
+    case 3: ws_run<MODE, 3, R3>(a, ch, nt); break;
+    case 4: ws_run<MODE, 4, R3>(a, ch, nt); break;
+    case 5: ws_run<MODE, 5, R3>(a, ch, nt); break;
+    case 6: ws_run<MODE, 6, R3>(a, ch, nt); break;
+    case 7: ws_run<MODE, 7, R3>(a, ch, nt); break;
+    case 8: ws_run<MODE, 8, R3>(a, ch, nt); break;
+    case 9: ws_run<MODE, 9, R3>(a, ch, nt); break;
+    default: ws_run<MODE, 10, R3>(a, ch, nt); break;
   }
   static_assert(WBM / 32 == 10, "row-block dispatch");
 }
@@ -1355,10 +1367,11 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
   } else if (dtype == MOE_BF16 && MOE_GEMM_WS && a.bm == WBM && rs_fits(a)) {
     const int n_tiles = (int)(MODE == MODE_GATEUP ? (a.N + 127) / 128 : (a.N + WBN - 1) / WBN);
     const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
-    if ((a.K / RBK) % 2)
-      hipLaunchKernelGGL((grouped_gemm_ws<MODE, true>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles);
-    else
-      hipLaunchKernelGGL((grouped_gemm_ws<MODE, false>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles);
+    switch ((a.K / RBK - 2) % 3) {
+      case 0: hipLaunchKernelGGL((grouped_gemm_ws<MODE, 0>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles); break;
+      case 1: hipLaunchKernelGGL((grouped_gemm_ws<MODE, 1>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles); break;
+      default: hipLaunchKernelGGL((grouped_gemm_ws<MODE, 2>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles); break;
+    }
   } else if (dtype == MOE_BF16) {
     const int n_tiles = (int)(MODE == MODE_GATEUP ? (a.N + 127) / 128 : (a.N + BN - 1) / BN);
     const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
