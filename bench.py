@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-variants", action="store_true")
     p.add_argument("--no-achievable", action="store_true")
+    p.add_argument("--no-clock", action="store_true", help="skip sampling the shader clock under sustained load")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (reference for HBM counters)")
     return p.parse_args()
@@ -118,6 +119,7 @@ def achievable(moe, torch):
     def mfma():
         fl[0] = moe.mfma_peak(iters, sink)
     ms_mfma = event_ms(torch, mfma, 10, 3)
+    ms_mfma_v = event_ms(torch, lambda: moe.mfma_peak(iters, sink, varied=True), 10, 3)
     del sink
     n = 2 ** 31
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -132,11 +134,48 @@ def achievable(moe, torch):
     torch.cuda.empty_cache()
     return {"hbm_copy_GBps": 2.0 * n / (ms_copy * 1e-3) / 1e9,
             "mfma_loop_bf16_TFLOPs": fl[0] / (ms_mfma * 1e-3) / 1e12,
+            "mfma_loop_varied_bf16_TFLOPs": fl[0] / (ms_mfma_v * 1e-3) / 1e12,
             "dense_bf16_gemm_TFLOPs": 2.0 * m * kk * nn / (ms_mm * 1e-3) / 1e12,
             "dense_gemm_shape": [m, kk, nn],
             "note": "copy counts bytes read + written; the MFMA loop is moe_mfma_peak (v_mfma_f32_32x32x16_bf16 "
-                    "on registers, 2048 workgroups x 4 waves x 4 chains); GEMM is torch.matmul (hipBLASLt), "
-                    "contiguous operands"}
+                    "on registers, 2048 workgroups x 4 waves x 4 chains), with one fixed operand pair or with eight "
+                    "hashed pairs in turn (varied: inputs toggle as on real data); GEMM is torch.matmul "
+                    "(hipBLASLt), contiguous operands"}
+
+
+def sustained_sclk(torch, fn, seconds=2.5):
+    """Median shader clock (MHz) that rocm-smi reports while fn runs back to back for
+    `seconds` (reading only; None where rocm-smi is missing or prints nothing usable)."""
+    import re, shutil, subprocess, threading, time
+    exe = shutil.which("rocm-smi")
+    if exe is None:
+        return None
+    got, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([exe, "--showgpuclocks", "--json"], capture_output=True, text=True, timeout=10)
+                m = re.search(r"sclk clock level[^(]*\((\d+)\s*Mhz\)", r.stdout)
+                if m:
+                    got.append(int(m.group(1)))
+            except Exception:
+                pass
+            time.sleep(0.2)
+
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.time()
+    th.start()
+    while time.time() - t0 < seconds:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    return float(sorted(got)[len(got) // 2]) if got else None
 
 
 def variants(moe, torch, np, s, dev, x, y, ws, steps, warmup):
@@ -353,7 +392,19 @@ def main():
         g = out["achievable"]
         out["roofline"]["frac_of_achievable"] = gateup_tflops / g["dense_bf16_gemm_TFLOPs"]
         out["roofline"]["frac_of_mfma_loop"] = gateup_tflops / g["mfma_loop_bf16_TFLOPs"]
+        out["roofline"]["frac_of_mfma_loop_varied"] = gateup_tflops / g["mfma_loop_varied_bf16_TFLOPs"]
         print("[bench] achievable peaks measured", file=sys.stderr, flush=True)
+
+    if not a.no_clock:
+        sink = torch.empty(moe.MFMA_PEAK_SINK, device="cuda")
+        out["sclk_MHz_sustained"] = {
+            "prefill_layer": sustained_sclk(torch, lambda: moe.forward(cfg, dev, x, y, ws)),
+            "mfma_loop_fixed": sustained_sclk(torch, lambda: moe.mfma_peak(2000, sink)),
+            "mfma_loop_varied": sustained_sclk(torch, lambda: moe.mfma_peak(2000, sink, varied=True)),
+            "nominal": 2400.0,
+            "note": "median of rocm-smi samples while each runs back to back for 2.5 s, after the timed steps"}
+        del sink
+        print("[bench] sustained clocks sampled", file=sys.stderr, flush=True)
 
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, s, a.cpu_sample_tokens)

@@ -304,10 +304,14 @@ moe_status moe_forward_ec(const moe_config *cfg, const moe_weights *w, const voi
  * 2048 workgroups x 4 waves, each wave issuing 4 * iters
  * v_mfma_f32_32x32x16_bf16 on register operands (four independent accumulator
  * chains) and writing one float of its result into sink (device, float32,
- * 8192 entries).  *flops (host) receives the launch's floating-point operation
- * count; the caller times the launch (events on `stream`).  1 <= iters <= 2^24;
- * MOE_ERR_SHAPE otherwise, MOE_ERR_NULL for a NULL sink or flops. */
-moe_status moe_mfma_peak(int64_t iters, float *sink, int64_t *flops, void *stream);
+ * 8192 entries).  varied = 0: every MFMA multiplies the same two operands;
+ * varied = 1: eight operand pairs of hashed bf16 values (sign, exponent 2^-4,
+ * mantissa) in turn, chain c taking pair c on even iterations and pair 4 + c
+ * on odd ones, so the matrix units toggle as on real data.  *flops (host)
+ * receives the launch's floating-point operation count; the caller times the
+ * launch (events on `stream`).  1 <= iters <= 2^24 and varied in {0, 1}, else
+ * MOE_ERR_SHAPE; MOE_ERR_NULL for a NULL sink or flops. */
+moe_status moe_mfma_peak(int64_t iters, int32_t varied, float *sink, int64_t *flops, void *stream);
 
 #ifdef __cplusplus
 }

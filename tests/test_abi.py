@@ -148,8 +148,10 @@ def test_mfma_peak_host_validation():
     """The calibration entry point rejects bad arguments on the host, before any launch."""
     L = moe.lib()
     fl = ctypes.c_int64(-1)
-    assert L.moe_mfma_peak(0, None, ctypes.byref(fl), None) == 2
-    assert L.moe_mfma_peak((1 << 24) + 1, None, ctypes.byref(fl), None) == 2
-    assert L.moe_mfma_peak(10, None, ctypes.byref(fl), None) == 1
-    assert L.moe_mfma_peak(10, None, None, None) == 1
+    assert L.moe_mfma_peak(0, 0, None, ctypes.byref(fl), None) == 2
+    assert L.moe_mfma_peak((1 << 24) + 1, 0, None, ctypes.byref(fl), None) == 2
+    assert L.moe_mfma_peak(10, 2, None, ctypes.byref(fl), None) == 2
+    assert L.moe_mfma_peak(10, -1, None, ctypes.byref(fl), None) == 2
+    assert L.moe_mfma_peak(10, 0, None, ctypes.byref(fl), None) == 1
+    assert L.moe_mfma_peak(10, 1, None, None, None) == 1
     assert fl.value == -1

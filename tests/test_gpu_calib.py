@@ -1,7 +1,8 @@
 """The MFMA calibration kernel (moe_mfma_peak): its flop count, and its result
-against the same product computed on the host (each wave's lane 0 sums column
-0, rows 8g + q (g, q < 4), of four identical accumulator chains of iters
-32 x 32 x 16 products; the operands are fixed bf16 values of the lane id)."""
+against the same products computed on the host.  Each wave's lane 0 sums column
+0, rows 8g + q (g, q < 4), of its four accumulator chains of iters 32 x 32 x 16
+products: with fixed operands (bf16 values of the lane id) the chains are
+identical; with varied ones each chain alternates two of eight hashed pairs."""
 import numpy as np
 import pytest
 import torch
@@ -44,3 +45,47 @@ def test_mfma_peak_result_and_flops():
     want = 4 * C[rows, 0].sum()
     got = bits(sink)
     assert np.all(np.abs(got - want) <= 1e-5 * abs(want) + 1e-9), (got[:4], want)
+
+
+def cal_bits(lane, j, i, ab):
+    """The varied mode's operand bits (bf16): sign, exponent 2^-4 and mantissa from
+    a 32-bit integer hash of (lane, pair j, element i, a or b)."""
+    m = 0xFFFFFFFF
+    h = ((lane * 0x9E3779B1) & m) ^ (((j * 8 + i) * 0x85EBCA77) & m) ^ ((ab * 0xC2B2AE3D) & m)
+    h ^= h >> 15
+    h = (h * 0x2C1B3C6D) & m
+    h ^= h >> 12
+    return 0x3D80 | (h & 0x807F)
+
+
+def varied_operands(j):
+    A = np.zeros((32, 16), np.uint16)
+    B = np.zeros((16, 32), np.uint16)
+    for lane in range(64):
+        for i in range(8):
+            k = 8 * (lane // 32) + i
+            A[lane % 32, k] = cal_bits(lane, j, i, 0)
+            B[k, lane % 32] = cal_bits(lane, j, i, 1)
+    return bf16_bits_to_f32(A).astype(np.float64), bf16_bits_to_f32(B).astype(np.float64)
+
+
+def test_mfma_peak_varied_result():
+    """Varied operands: chain c takes pair c on even iterations and pair 4 + c on odd
+    ones (an odd count, so the single-step tail runs too)."""
+    iters = 63
+    sink = torch.full((moe.MFMA_PEAK_SINK,), float("nan"), device="cuda")
+    flops = moe.mfma_peak(iters, sink, varied=True)
+    torch.cuda.synchronize()
+    assert flops == 2048 * 4 * iters * 4 * 2 * 32 * 32 * 16
+    ops = [varied_operands(j) for j in range(8)]
+    n_even, n_odd = (iters + 1) // 2, iters // 2
+    rows = [8 * g + q for g in range(4) for q in range(4)]
+    want = 0.0
+    scale = 0.0
+    for c in range(4):
+        (A0, B0), (A1, B1) = ops[c], ops[4 + c]
+        C = n_even * (A0 @ B0) + n_odd * (A1 @ B1)
+        want += C[rows, 0].sum()
+        scale += n_even * (np.abs(A0) @ np.abs(B0))[rows, 0].sum() + n_odd * (np.abs(A1) @ np.abs(B1))[rows, 0].sum()
+    got = bits(sink)
+    assert np.all(np.abs(got - want) <= 1e-5 * scale), (got[:4], want, scale)

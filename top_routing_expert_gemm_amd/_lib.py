@@ -116,7 +116,7 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_ec.argtypes = [P, POINTER(MoeWeights), c_void_p, c_void_p, POINTER(MoeEcOut), c_void_p,
                                      c_size_t, c_void_p]
         L.moe_mfma_peak.restype = c_int32
-        L.moe_mfma_peak.argtypes = [c_int64, c_void_p, POINTER(c_int64), c_void_p]
+        L.moe_mfma_peak.argtypes = [c_int64, c_int32, c_void_p, POINTER(c_int64), c_void_p]
         L.moe_quantize_fp8.restype = c_int32
         L.moe_quantize_fp8.argtypes = [c_void_p, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p]
         L.moe_forward_fp8.restype = c_int32
@@ -290,11 +290,13 @@ def forward_ec(cfg, weights, x, y, ws, ec_out=None, stream=None):
 MFMA_PEAK_SINK = 8192
 
 
-def mfma_peak(iters, sink, stream=None) -> int:
+def mfma_peak(iters, sink, stream=None, varied=False) -> int:
     """Launch the MFMA-only calibration kernel (moe_mfma_peak) on `stream`; sink: float32 device tensor of
-    MFMA_PEAK_SINK entries.  Returns the launch's floating-point operation count (time it with events)."""
+    MFMA_PEAK_SINK entries; varied: cycle eight hashed operand pairs instead of one fixed pair.  Returns the
+    launch's floating-point operation count (time it with events)."""
     fl = c_int64(0)
-    _check(lib().moe_mfma_peak(int(iters), _ptr(sink), ctypes.byref(fl), _stream(stream)), "moe_mfma_peak")
+    _check(lib().moe_mfma_peak(int(iters), 1 if varied else 0, _ptr(sink), ctypes.byref(fl), _stream(stream)),
+           "moe_mfma_peak")
     return fl.value
 
 

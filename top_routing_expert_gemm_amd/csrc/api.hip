@@ -471,12 +471,12 @@ moe_status moe_quantize_fp8(const void* w, int32_t dtype, int64_t G, int64_t N, 
   return MOE_OK;
 }
 
-moe_status moe_mfma_peak(int64_t iters, float* sink, int64_t* flops, void* stream) {
-  if (iters < 1 || iters > (int64_t(1) << 24)) return MOE_ERR_SHAPE;
+moe_status moe_mfma_peak(int64_t iters, int32_t varied, float* sink, int64_t* flops, void* stream) {
+  if (iters < 1 || iters > (int64_t(1) << 24) || (varied != 0 && varied != 1)) return MOE_ERR_SHAPE;
   if (flops == nullptr) return MOE_ERR_NULL;
   MOE_TRY(need(sink));
   *flops = mfma_peak_flops(iters);
-  HIP_TRY(launch_mfma_peak((int)iters, sink, S(stream)));
+  HIP_TRY(launch_mfma_peak((int)iters, varied != 0, sink, S(stream)));
   return MOE_OK;
 }
 

@@ -10,22 +10,63 @@ constexpr int kCalWG = 2048;       // workgroups (8 per CU)
 constexpr int kCalThreads = 256;   // 4 waves
 constexpr int kCalChains = 4;      // independent accumulator chains per wave
 
+// Operand bits of the varied mode: set j (< 8), element i of lane l, a or b
+// (ab = 0 / 1): a sign, an exponent of 2^-4 and a mantissa from an integer
+// hash, so consecutive MFMAs see unrelated inputs, as a GEMM's operands are.
+__device__ __forceinline__ uint16_t cal_bits(uint32_t lane, uint32_t j, uint32_t i, uint32_t ab) {
+  uint32_t h = lane * 0x9E3779B1u ^ (j * 8u + i) * 0x85EBCA77u ^ ab * 0xC2B2AE3Du;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  return (uint16_t)(0x3D80u | (h & 0x807Fu));
+}
+
+// VARIED = false: every MFMA multiplies the same two register operands;
+// VARIED = true: eight operand pairs in turn, so every MFMA's inputs differ
+// from the previous one's (the matrix units toggle as on real data, which draws
+// more power and can lower the clock the device holds).
+template <bool VARIED>
 __global__ __launch_bounds__(kCalThreads) void mfma_peak_kernel(int iters, float* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
-  bf16x8 a, b;
+  constexpr int NS = VARIED ? 8 : 1;
+  bf16x8 a[NS], b[NS];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(1e-3f * (float)((lane + i) & 7));
-    b[i] = (__bf16)(1e-3f * (float)((lane * 3 + i) & 7));
-  }
+  for (int j = 0; j < NS; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (VARIED) {
+        a[j][i] = __builtin_bit_cast(__bf16, cal_bits(lane, j, i, 0));
+        b[j][i] = __builtin_bit_cast(__bf16, cal_bits(lane, j, i, 1));
+      } else {
+        a[j][i] = (__bf16)(1e-3f * (float)((lane + i) & 7));
+        b[j][i] = (__bf16)(1e-3f * (float)((lane * 3 + i) & 7));
+      }
+    }
   f32x16 acc[kCalChains];
 #pragma unroll
   for (int c = 0; c < kCalChains; ++c)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
-  for (int it = 0; it < iters; ++it) {
+  if constexpr (VARIED) {
+    // chain c: operand pair c on even iterations, pair 4 + c on odd ones
+    int it = 0;
+    for (; it + 1 < iters; it += 2) {
 #pragma unroll
-    for (int c = 0; c < kCalChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+      for (int c = 0; c < kCalChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b[c], acc[c], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < kCalChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[4 + c], b[4 + c], acc[c], 0, 0, 0);
+    }
+    if (it < iters) {
+#pragma unroll
+      for (int c = 0; c < kCalChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b[c], acc[c], 0, 0, 0);
+    }
+  } else {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < kCalChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], acc[c], 0, 0, 0);
+    }
   }
   float s = 0.f;
 #pragma unroll
@@ -43,8 +84,11 @@ int64_t mfma_peak_flops(int64_t iters) {
 
 int64_t mfma_peak_sink_len() { return (int64_t)kCalWG * (kCalThreads / kWave); }
 
-hipError_t launch_mfma_peak(int iters, float* sink, hipStream_t s) {
-  hipLaunchKernelGGL(mfma_peak_kernel, dim3(kCalWG), dim3(kCalThreads), 0, s, iters, sink);
+hipError_t launch_mfma_peak(int iters, bool varied, float* sink, hipStream_t s) {
+  if (varied)
+    hipLaunchKernelGGL(mfma_peak_kernel<true>, dim3(kCalWG), dim3(kCalThreads), 0, s, iters, sink);
+  else
+    hipLaunchKernelGGL(mfma_peak_kernel<false>, dim3(kCalWG), dim3(kCalThreads), 0, s, iters, sink);
   return hipGetLastError();
 }
 

@@ -195,7 +195,7 @@ hipError_t launch_combine(const void* y_perm, const int32_t* row_of_slot, const 
 // flop count and its sink length.
 int64_t mfma_peak_flops(int64_t iters);
 int64_t mfma_peak_sink_len();
-hipError_t launch_mfma_peak(int iters, float* sink, hipStream_t s);
+hipError_t launch_mfma_peak(int iters, bool varied, float* sink, hipStream_t s);
 
 // Expert choice: chunk list of E groups of C rows each (+ shared rows), and the
 // per-expert top-C selection from scores [T, E].
