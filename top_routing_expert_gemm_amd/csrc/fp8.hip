@@ -107,7 +107,13 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T* __restrict__
 constexpr int FW = MOE_FP8_FW;  // waves per workgroup
 constexpr int FP = MOE_FP8_FP;  // K blocks in flight per wave
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.f + expf(-g)); }
+// silu(g) = g / (1 + e^-g), with e^-g = 2^(-g log2 e) from the hardware base-2
+// exponential and the quotient from the hardware reciprocal (each within about
+// one ulp in fp32): five instructions per value instead of a correctly rounded
+// exponential and division, in epilogues that apply it to every gate/up output.
+__device__ __forceinline__ float silu_f(float g) {
+  return g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
 
 // 8 codes (two dwords) -> 8 bf16, exact
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {

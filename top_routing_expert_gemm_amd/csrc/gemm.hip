@@ -107,7 +107,28 @@ __device__ __forceinline__ void tile_of(int L, int n_tiles, const Chunk* chunks,
   ci = base + q % cnt;
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.f + expf(-g)); }
+// silu(g) = g / (1 + e^-g), with e^-g = 2^(-g log2 e) from the hardware base-2
+// exponential and the quotient from the hardware reciprocal (each within about
+// one ulp in fp32): five instructions per value instead of a correctly rounded
+// exponential and division, in epilogues that apply it to every gate/up output.
+__device__ __forceinline__ float silu_f(float g) {
+  return g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
+
+// The value of the neighbouring lane (lane ^ 1): a DPP quad permutation
+// [1, 0, 3, 2], one VALU move (no LDS round trip as a general shuffle takes).
+__device__ __forceinline__ float lane_swap1(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false));
+}
+
+// Two floats to a pair of bf16 (round to nearest even), lo in bits 0..15: one
+// v_cvt_pk_bf16_f32.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
+}
 
 // Wait until at most N of this wave's vector-memory loads are outstanding and
 // its LDS reads are done, then barrier (no other fence: the stage buffers are
@@ -350,10 +371,9 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
                 vb = acc[i][jj][4 * g + p + 1];
               }
               // even lane: (row ra, cols c, c+1); odd lane: (row ra+1, cols c-1, c)
-              const float x = __shfl_xor(odd ? va : vb, 1, kWave);
+              const float x = lane_swap1(odd ? va : vb);
               const int ra = (i - pass) * 32 + 8 * g + 4 * h + p;
-              const uint32_t w = odd ? ((uint32_t)f32_to_bf16(x) | ((uint32_t)f32_to_bf16(vb) << 16))
-                                     : ((uint32_t)f32_to_bf16(va) | ((uint32_t)f32_to_bf16(x) << 16));
+              const uint32_t w = odd ? pack_bf16x2(x, vb) : pack_bf16x2(va, x);
               const int lr = odd ? ra + 1 : ra;
               const int lc = jj * 32 + (col & ~1);
               *reinterpret_cast<uint32_t*>(tile + lr * LDSR + lc) = w;
@@ -692,10 +712,9 @@ __device__ __forceinline__ void rs_wave(const GemmArgs& a, const Chunk& ch, int 
               vb = acc[i][jj][4 * g + p + 1];
             }
             // even lane: (row ra, cols c, c+1); odd lane: (row ra+1, cols c-1, c)
-            const float x = __shfl_xor(odd ? va : vb, 1, kWave);
+            const float x = lane_swap1(odd ? va : vb);
             const int r = 8 * g + 4 * h + p;
-            const uint32_t w = odd ? ((uint32_t)f32_to_bf16(x) | ((uint32_t)f32_to_bf16(vb) << 16))
-                                   : ((uint32_t)f32_to_bf16(va) | ((uint32_t)f32_to_bf16(x) << 16));
+            const uint32_t w = odd ? pack_bf16x2(x, vb) : pack_bf16x2(va, x);
             const int lr = odd ? r + 1 : r;
             *reinterpret_cast<uint32_t*>(tile + lr * LDSR + jj * 32 + (l32 & ~1)) = w;
           }
@@ -1049,10 +1068,9 @@ __device__ __forceinline__ void ws_wave(const GemmArgs& a, const Chunk& ch, int 
               vb = acc[i][jj][4 * g + p + 1];
             }
             // even lane: (row r, cols c, c+1); odd lane: (row r+1, cols c-1, c)
-            const float x = __shfl_xor(odd ? va : vb, 1, kWave);
+            const float x = lane_swap1(odd ? va : vb);
             const int r = 8 * g + 4 * h + p;
-            const uint32_t w = odd ? ((uint32_t)f32_to_bf16(x) | ((uint32_t)f32_to_bf16(vb) << 16))
-                                   : ((uint32_t)f32_to_bf16(va) | ((uint32_t)f32_to_bf16(x) << 16));
+            const uint32_t w = odd ? pack_bf16x2(x, vb) : pack_bf16x2(va, x);
             const int lr = odd ? r + 1 : r;
             *reinterpret_cast<uint32_t*>(tile + lr * LDSR + jj * 32 + (l32 & ~1)) = w;
           }
