@@ -32,6 +32,16 @@ SMALL = {
     # used; an odd number of 64-wide K steps in the down pass (I = 320)
     "bf16_two_chunk_lists": MoEShape("bf16_two_chunk_lists", T=2048, H=256, I=320, E=8, k=2, gate=GATE_SIGMOID,
                                      routed_scaling_factor=2.5, n_shared=1, I_shared=320, cfg_id=113),
+    # H or I below 128: one chunk list of 320-row chunks, so the 320-row kernels see
+    # every chunk height; the skewed router spreads the expert loads from ~50 to ~570
+    # rows (chunks of 2 to 10 row blocks).  K / 64 of the register-staged pass: 3
+    # (down, I = 192), 4 (down, I = 256) and 5 (gate/up, H = 320)
+    "bf16_h64_i192_skew": MoEShape("bf16_h64_i192_skew", T=1500, H=64, I=192, E=16, k=2, gate=GATE_SOFTMAX,
+                                   logit_skew=True, n_shared=1, I_shared=192, cfg_id=114),
+    "bf16_h64_i256_skew": MoEShape("bf16_h64_i256_skew", T=1400, H=64, I=256, E=16, k=2, gate=GATE_SOFTMAX,
+                                   logit_skew=True, n_shared=1, I_shared=256, cfg_id=115),
+    "bf16_h320_i64_skew": MoEShape("bf16_h320_i64_skew", T=1500, H=320, I=64, E=16, k=2, gate=GATE_SOFTMAX,
+                                   logit_skew=True, n_shared=1, I_shared=64, cfg_id=116),
     "fp32_tiny": WORKLOADS[TINY],
     "fp32_sigmoid_shared_capacity": MoEShape("fp32_sigmoid_shared_capacity", T=200, H=192, I=128, E=8, k=3,
                                              gate=GATE_SIGMOID, capacity_factor=1.0, n_shared=1, I_shared=128,
