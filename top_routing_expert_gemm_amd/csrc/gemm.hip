@@ -6,28 +6,42 @@
 // implementations run the tokens of each expert as one batched ("grouped") GEMM;
 // section "细粒度专家与共享专家": the shared expert sees every token.
 //
-// Work decomposition.  The dispatch step writes a device-side list of row chunks
-// (expert group, first row, rows <= BM).  Workgroup p of the grid takes logical
-// tile L(p) = (chunk, n-tile), with consecutive logical tiles placed on the same
-// XCD (workgroups are dealt to the 8 XCDs round-robin), so the n-tiles of one
-// chunk share its gathered token rows in that XCD's L2.  Workgroups past the
-// device-side tile count exit at once, so the grid is sized on the host for the
-// worst case and no host synchronisation is needed.
+// Work decomposition.  The dispatch step writes device-side lists of row chunks
+// (expert group, first row, rows <= the list's tile height).  Workgroup p of a
+// launch takes logical tile L(p) = (chunk, n-tile), with consecutive logical
+// tiles placed on the same XCD (workgroups are dealt to the 8 XCDs
+// round-robin), so the n-tiles of one chunk share its gathered token rows in
+// that XCD's L2.  Workgroups past the device-side tile count exit at once, so
+// the grid is sized on the host for the worst case and no host synchronisation
+// is needed.
 //
-// 320-row bf16 tile: BM = 320 rows x BN = 256 weight rows, eight waves (two per
-// SIMD) in a 2 x 4 grid, each wave up to 160 x 64 of v_mfma_f32_32x32x16_bf16
-// (fp32 accumulators).  A 320-row chunk holds a whole routed expert of the large
-// workloads, so each expert's weights stream through one workgroup per n-tile.
-// Gate/up pass: the 256 weight rows are 128 gate rows and the same 128 up rows;
-// every wave owns 32 gate columns and the matching 32 up columns, so each lane
-// holds gate and up of the same (row, i) and applies silu(g) * u in registers.
-// Down pass: 256 output columns.  The A tile is gathered straight from x
-// through token_of_row (the gather of the dispatch step is fused into this
-// loader).  Both tiles move global -> LDS with direct (global_load_lds_dwordx4)
-// loads: A (token rows, from L2) in 64-wide K steps, whole 128-byte lines,
-// through two stages, one step ahead; B (weights, from HBM) in 32-wide K steps
-// through four stages, three steps ahead.  The 16-byte chunks of each LDS row
-// are XOR-swizzled by row so the MFMA operand reads are free of bank conflicts.
+// The kernels (launch_gemm picks one per pass and chunk list):
+//   grouped_gemm_rs   256 x 256 tile, four waves, both operands register-staged
+//                     two K steps ahead (bf16 prefill, the 256-row list);
+//   grouped_gemm_ws   320 x 256 tile, eight waves, weights straight to LDS
+//                     through three stages, token rows register-staged (bf16
+//                     prefill, the 320-row list);
+//   grouped_gemm_bf16 320 x 256 tile, eight waves, both operands straight to
+//                     LDS (the 320-row list where the others' 32-bit offsets do
+//                     not fit or K < 128);
+//   grouped_stream_bf16  batches of <= 16 tokens: weights streamed into
+//                     registers, no LDS (decode);
+//   grouped_gemm_f32  fp32 SIMT tiles.
+// In every bf16 tile kernel a wave owns matching gate and up columns in the
+// gate/up pass, so each lane holds gate and up of the same (row, i) and applies
+// silu(g) * u in registers; the A tile is gathered straight from x through
+// token_of_row (the gather of the dispatch step is fused into the loader); the
+// 16-byte chunks of each LDS row are XOR-swizzled by row so the MFMA operand
+// reads are free of bank conflicts.
+//
+// 320-row direct-to-LDS tile: BM = 320 rows x BN = 256 weight rows, eight waves
+// (two per SIMD) in a 2 x 4 grid, each wave up to 160 x 64 of
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulators).  A 320-row chunk holds a whole
+// routed expert of the large workloads, so each expert's weights stream through
+// one workgroup per n-tile.  Both tiles move global -> LDS with direct
+// (global_load_lds_dwordx4) loads: A (token rows, from L2) in 64-wide K steps,
+// whole 128-byte lines, through two stages, one step ahead; B (weights, from
+// HBM) in 32-wide K steps through four stages, three steps ahead.
 //
 // Tile order: within one expert the chunks of an n-tile are adjacent (groups of
 // up to four chunks), so a second row chunk of an expert reads the same weight
