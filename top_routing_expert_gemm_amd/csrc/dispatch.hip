@@ -89,9 +89,10 @@ __device__ int block_inclusive_scan(int v, int* tmp) {
 }
 
 // Which list a group of L rows goes to.  With one list (bm_b == 0) every group
-// is cut to bm_a rows.  With two (the register-staged 256-row tile in list A,
-// the 320-row tile in list B), a list-A chunk costs about 0.88 of a list-B
-// chunk (measured on the DeepSeek-V3, Mixtral and Switch shapes), so a group
+// is cut to bm_a rows.  With two (the 256-row tile in list A, the 320-row tile
+// in list B), a list-A chunk costs about 0.88-0.91 of a list-B chunk (measured
+// on the DeepSeek-V3, Mixtral and Switch shapes; 0.91 with the current 320-row
+// kernel, expert choice with every group on one tile or the other), so a group
 // takes list A unless that needs more chunks than the lower cost saves (a group
 // of 257..320 rows: two chunks instead of one).
 __device__ __forceinline__ bool takes_list_a(int64_t L, const ChunkCut& cut) {
