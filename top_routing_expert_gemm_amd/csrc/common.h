@@ -62,9 +62,10 @@ int64_t max_chunks(int64_t rows_max, int64_t E, int64_t shared_rows, int bm);
 // Chunk lists of a layer with at most `routed` routed rows over E groups plus
 // `shared` shared rows: the streaming path when every group fits one 16-row
 // chunk (T <= 16), 64-row chunks for fp32; for bf16 two lists (256-row and
-// 320-row tiles) when the register-staged kernels' limits hold (both contractions at least 128 long, 32-bit buffer
-// offsets covering x [T, H], the row space [rows, H] and h [rows, I]), else the
-// 320-row tile alone.  max_a / max_b: capacities of the two lists.
+// 320-row tiles) when the register-staged kernels' limits hold (both
+// contractions at least 128 long, 32-bit buffer offsets covering x [T, H], the
+// row space [rows, H] and h [rows, I]), else the 320-row tile alone.
+// max_a / max_b: capacities of the two lists.
 struct ChunkPlan {
   ChunkCut cut;
   int64_t max_a, max_b;
