@@ -60,6 +60,21 @@ def test_forward_graph_replays(T):
                    [y, r["topk_idx"], r["topk_w"], r["counts"], r["row_of_slot"]])
 
 
+def test_forward_two_lists_graph_replays():
+    """Loads around 512 rows per expert: both chunk lists of each GEMM pass hold
+    work (the 256-row and the 320-row kernel both run inside the graph)."""
+    s = MoEShape("graph_two_lists", T=2048, H=256, I=320, E=8, k=2, gate=GATE_SIGMOID, routed_scaling_factor=2.5,
+                 n_shared=1, I_shared=320, cfg_id=704)
+    inp = make_inputs(s)
+    dev = upload(inp)
+    cfg = moe.config_from_shape(s)
+    y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device="cuda")
+    r = alloc_route(s)
+    ws = workspace(cfg)
+    replay_matches(lambda: moe.forward(cfg, dev, dev["x"], y, ws, route_out=r),
+                   [y, r["topk_idx"], r["topk_w"], r["counts"], r["row_of_slot"]])
+
+
 def test_forward_ec_graph_replays():
     s = MoEShape("graph_ec", T=300, H=256, I=128, E=8, k=2, gate=GATE_SIGMOID, cfg_id=702)
     inp = make_inputs(s)
