@@ -11,11 +11,15 @@
 // of the token are read and compacted in slot order, then each thread
 // accumulates one 16-byte column vector of those y_perm rows in float32 in slot
 // order j = 0..k-1, adds the shared row, and stores.  A gather, not a scatter: no atomics, so the result is bitwise
-// reproducible.  HBM bound: reads (kept slots + shared) rows, writes one row.
+// reproducible.  HBM bound: reads (kept slots + shared) rows, writes one row.  The row loads of a
+// thread are issued kCombineBatch at a time before any is accumulated, so that the memory system has
+// that many requests of each thread in flight rather than one.
 #include "common.h"
 
 namespace moe {
 namespace {
+
+constexpr int kCombineBatch = 8;
 
 __device__ __forceinline__ void acc_bf16x8(float (&acc)[8], const uint4& v, float w) {
   const uint32_t u[4] = {v.x, v.y, v.z, v.w};
@@ -38,9 +42,10 @@ __device__ __forceinline__ int load_pairs(const int32_t* __restrict__ ros, const
     const int j = j0 + threadIdx.x;
     int row = -1;
     float w = 0.f;
-    if (j < k) {
+    if (j < k) {  // both loads issued together; the weight is kept only for a kept slot
       row = ros[t * k + j];
-      if (row >= 0) w = tw[t * k + j];
+      const float wj = tw[t * k + j];
+      if (row >= 0) w = wj;
     }
     const uint64_t b = __ballot(row >= 0);
     if (lane == 0) s_cnt[wave] = __popcll(b);
@@ -81,9 +86,17 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __res
       float acc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-      for (int j = 0; j < n; ++j)
-        acc_bf16x8(acc, reinterpret_cast<const uint4*>(yp + (int64_t)s_row[j] * H)[c], s_w[j]);
-      if (ysh != nullptr) acc_bf16x8(acc, reinterpret_cast<const uint4*>(ysh + t * H)[c], 1.f);
+      const uint4 vsh = ysh != nullptr ? reinterpret_cast<const uint4*>(ysh + t * H)[c] : uint4{0, 0, 0, 0};
+      for (int j0 = 0; j0 < n; j0 += kCombineBatch) {
+        uint4 v[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+          if (j0 + u < n) v[u] = reinterpret_cast<const uint4*>(yp + (int64_t)s_row[j0 + u] * H)[c];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+          if (j0 + u < n) acc_bf16x8(acc, v[u], s_w[j0 + u]);
+      }
+      if (ysh != nullptr) acc_bf16x8(acc, vsh, 1.f);
       uint4 o;
       o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
       o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
@@ -111,16 +124,24 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
     const int64_t c = (wi % nch) * blockDim.x + threadIdx.x;
     if (c < hv) {
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int j = 0; j < n; ++j) {
-        const float4 v = reinterpret_cast<const float4*>(yp + (int64_t)s_row[j] * H)[c];
-        const float w = s_w[j];
-        acc.x = fmaf(w, v.x, acc.x);
-        acc.y = fmaf(w, v.y, acc.y);
-        acc.z = fmaf(w, v.z, acc.z);
-        acc.w = fmaf(w, v.w, acc.w);
+      const float4 vsh = ysh != nullptr ? reinterpret_cast<const float4*>(ysh + t * H)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j0 = 0; j0 < n; j0 += kCombineBatch) {
+        float4 v[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+          if (j0 + u < n) v[u] = reinterpret_cast<const float4*>(yp + (int64_t)s_row[j0 + u] * H)[c];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+          if (j0 + u < n) {
+            const float w = s_w[j0 + u];
+            acc.x = fmaf(w, v[u].x, acc.x);
+            acc.y = fmaf(w, v[u].y, acc.y);
+            acc.z = fmaf(w, v[u].z, acc.z);
+            acc.w = fmaf(w, v[u].w, acc.w);
+          }
       }
       if (ysh != nullptr) {
-        const float4 v = reinterpret_cast<const float4*>(ysh + t * H)[c];
+        const float4 v = vsh;
         acc.x += v.x;
         acc.y += v.y;
         acc.z += v.z;
