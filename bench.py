@@ -126,6 +126,15 @@ def achievable(moe, torch):
     dst = torch.empty_like(src)
     ms_copy = event_ms(torch, lambda: dst.copy_(src), 10, 3)
     del src, dst
+    # read-only stream over 8 GiB (the layer's GEMM and decode passes read far more than they write)
+    rbuf = torch.empty(2 ** 33, dtype=torch.uint8, device="cuda")
+    rsink = torch.empty(moe.HBM_READ_SINK, dtype=torch.int32, device="cuda")
+    nread = [0]
+
+    def read():
+        nread[0] = moe.hbm_read_peak(rbuf, rsink)
+    ms_read = event_ms(torch, read, 10, 3)
+    del rbuf, rsink
     m, kk, nn = 8192 * 9, 7168, 4096
     a = torch.randn(m, kk, device="cuda").to(torch.bfloat16)
     b = torch.randn(kk, nn, device="cuda").to(torch.bfloat16)
@@ -133,11 +142,14 @@ def achievable(moe, torch):
     del a, b
     torch.cuda.empty_cache()
     return {"hbm_copy_GBps": 2.0 * n / (ms_copy * 1e-3) / 1e9,
+            "hbm_read_GBps": nread[0] / (ms_read * 1e-3) / 1e9,
             "mfma_loop_bf16_TFLOPs": fl[0] / (ms_mfma * 1e-3) / 1e12,
             "mfma_loop_varied_bf16_TFLOPs": fl[0] / (ms_mfma_v * 1e-3) / 1e12,
             "dense_bf16_gemm_TFLOPs": 2.0 * m * kk * nn / (ms_mm * 1e-3) / 1e12,
             "dense_gemm_shape": [m, kk, nn],
-            "note": "copy counts bytes read + written; the MFMA loop is moe_mfma_peak (v_mfma_f32_32x32x16_bf16 "
+            "note": "copy counts bytes read + written; the read stream is moe_hbm_read_peak over 8 GiB (4096 "
+                    "workgroups, 32 KiB blocks, loads of the next block issued before the current one is used); "
+                    "the MFMA loop is moe_mfma_peak (v_mfma_f32_32x32x16_bf16 "
                     "on registers, 2048 workgroups x 4 waves x 4 chains), with one fixed operand pair or with eight "
                     "hashed pairs in turn (varied: inputs toggle as on real data); GEMM is torch.matmul "
                     "(hipBLASLt), contiguous operands"}
@@ -393,6 +405,13 @@ def main():
         out["roofline"]["frac_of_achievable"] = gateup_tflops / g["dense_bf16_gemm_TFLOPs"]
         out["roofline"]["frac_of_mfma_loop"] = gateup_tflops / g["mfma_loop_bf16_TFLOPs"]
         out["roofline"]["frac_of_mfma_loop_varied"] = gateup_tflops / g["mfma_loop_varied_bf16_TFLOPs"]
+        hs = out["roofline"]["hbm_side"]
+        hs["frac_of_read_stream"] = hs["achieved_GBps"] / g["hbm_read_GBps"]
+        if traffic is not None:
+            hs["traffic_GBps"] = traffic / (avg["gateup"] * 1e-3) / 1e9
+            hs["traffic_frac_of_read_stream"] = hs["traffic_GBps"] / g["hbm_read_GBps"]
+        if "decode" in out:
+            out["decode"]["frac_of_read_stream"] = out["decode"]["achieved_GBps"] / g["hbm_read_GBps"]
         print("[bench] achievable peaks measured", file=sys.stderr, flush=True)
 
     if not a.no_clock:

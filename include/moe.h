@@ -313,6 +313,18 @@ moe_status moe_forward_ec(const moe_config *cfg, const moe_weights *w, const voi
  * MOE_ERR_SHAPE; MOE_ERR_NULL for a NULL sink or flops. */
 moe_status moe_mfma_peak(int64_t iters, int32_t varied, float *sink, int64_t *flops, void *stream);
 
+/* The rate at which the device reads HBM with no arithmetic to speak of: one
+ * launch of 4096 workgroups reads `bytes` of buf (device) once, as 32 KiB
+ * blocks, block b by workgroup b mod 4096, each block one contiguous sweep of
+ * 16-byte loads.  sink (device, uint32, 4096 entries) receives in entry w the
+ * XOR of every 32-bit word of the blocks w, w + 4096, w + 8192, ... (0 when
+ * there are none), so the loads cannot be dropped and the result can be
+ * checked.  The caller times the launch (events on `stream`); the buffer
+ * should be far larger than the last-level cache (say >= 4 GiB).  bytes a
+ * positive multiple of 32768 and at most 2^40, else MOE_ERR_SHAPE;
+ * MOE_ERR_NULL / MOE_ERR_ALIGN for a NULL or not 16-byte aligned buf or sink. */
+moe_status moe_hbm_read_peak(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

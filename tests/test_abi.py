@@ -155,3 +155,17 @@ def test_mfma_peak_host_validation():
     assert L.moe_mfma_peak(10, 0, None, ctypes.byref(fl), None) == 1
     assert L.moe_mfma_peak(10, 1, None, None, None) == 1
     assert fl.value == -1
+
+
+def test_hbm_read_peak_host_validation():
+    """The read-stream calibration entry point rejects a size that is not a positive multiple of 32 KiB (or
+    above 2^40) and a NULL or misaligned pointer, on the host, before any launch."""
+    L = moe.lib()
+    assert L.moe_hbm_read_peak(16, 0, 16, None) == 2
+    assert L.moe_hbm_read_peak(16, 32768 + 16, 16, None) == 2
+    assert L.moe_hbm_read_peak(16, -32768, 16, None) == 2
+    assert L.moe_hbm_read_peak(16, (1 << 40) + 32768, 16, None) == 2
+    assert L.moe_hbm_read_peak(None, 32768, 16, None) == 1
+    assert L.moe_hbm_read_peak(16, 32768, None, None) == 1
+    assert L.moe_hbm_read_peak(8, 32768, 16, None) == 6
+    assert L.moe_hbm_read_peak(16, 32768, 4, None) == 6

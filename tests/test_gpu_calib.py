@@ -89,3 +89,21 @@ def test_mfma_peak_varied_result():
         scale += n_even * (np.abs(A0) @ np.abs(B0))[rows, 0].sum() + n_odd * (np.abs(A1) @ np.abs(B1))[rows, 0].sum()
     got = bits(sink)
     assert np.all(np.abs(got - want) <= 1e-5 * scale), (got[:4], want, scale)
+
+
+@pytest.mark.parametrize("nblocks", [3, 4096 * 2 + 5])
+def test_hbm_read_peak_result(nblocks):
+    """Entry w of the sink is the XOR of every 32-bit word of the 32 KiB blocks w, w + 4096, ... of the
+    buffer (0 where there are none): the launch read every byte once, in the documented assignment."""
+    words = np.random.default_rng(1234 + nblocks).integers(0, 2 ** 32, size=nblocks * 8192, dtype=np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).to("cuda")
+    sink = torch.full((moe.HBM_READ_SINK,), -1, dtype=torch.int32, device="cuda")
+    got_bytes = moe.hbm_read_peak(buf, sink)
+    torch.cuda.synchronize()
+    assert got_bytes == nblocks * moe.HBM_READ_BLOCK
+    per_block = np.bitwise_xor.reduce(words.reshape(nblocks, 8192), axis=1)
+    want = np.zeros(moe.HBM_READ_SINK, np.uint32)
+    for b in range(nblocks):
+        want[b % moe.HBM_READ_SINK] ^= per_block[b]
+    got = sink.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, want)

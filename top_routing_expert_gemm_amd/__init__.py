@@ -6,13 +6,15 @@ package is its thin ctypes binding.  The entry points keep the C names:
     moe_route, moe_route_sel, moe_dispatch, moe_expert_ffn, moe_combine, moe_forward,
     moe_balance_stats, moe_bias_update, moe_validate, moe_workspace_size, moe_capacity,
     moe_layer_params, moe_ec_capacity, moe_ec_workspace_size, moe_route_ec, moe_forward_ec,
-    moe_quantize_fp8, moe_forward_fp8, and the calibration entry point moe_mfma_peak
+    moe_quantize_fp8, moe_forward_fp8, and the calibration entry points moe_mfma_peak and
+    moe_hbm_read_peak
 """
-from ._lib import (BF16, EXPORTS, F32, GATE_SIGMOID, GATE_SOFTMAX, MFMA_PEAK_SINK, STAGE_EVENTS,  # noqa: F401
+from ._lib import (BF16, EXPORTS, F32, GATE_SIGMOID, GATE_SOFTMAX, HBM_READ_BLOCK, HBM_READ_SINK,  # noqa: F401
+                   MFMA_PEAK_SINK, STAGE_EVENTS,
                    MoeConfig, MoeError,
                    MoeEcOut, MoeFp8Experts, MoeRouteOut, MoeWeights, balance_stats, bias_update, capacity, combine,
                    config_from_shape, dispatch, ec_capacity, ec_workspace_size, expert_ffn, forward, forward_ec,
-                   forward_fp8, quantize_fp8, mfma_peak,
+                   forward_fp8, quantize_fp8, mfma_peak, hbm_read_peak,
                    layer_params, lib, make_config, route, route_ec, route_sel, status_str, validate,
                    workspace_size)
 
@@ -35,3 +37,4 @@ moe_forward_ec = forward_ec
 moe_quantize_fp8 = quantize_fp8
 moe_forward_fp8 = forward_fp8
 moe_mfma_peak = mfma_peak
+moe_hbm_read_peak = hbm_read_peak

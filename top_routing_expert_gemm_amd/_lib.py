@@ -24,7 +24,8 @@ STAGE_EVENTS = 6
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_capacity", "moe_layer_params",
            "moe_route", "moe_route_sel", "moe_balance_stats", "moe_bias_update", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_timed", "moe_ec_capacity",
-           "moe_ec_workspace_size", "moe_route_ec", "moe_forward_ec", "moe_quantize_fp8", "moe_forward_fp8", "moe_mfma_peak")
+           "moe_ec_workspace_size", "moe_route_ec", "moe_forward_ec", "moe_quantize_fp8", "moe_forward_fp8", "moe_mfma_peak",
+           "moe_hbm_read_peak")
 
 
 class MoeConfig(ctypes.Structure):
@@ -117,6 +118,8 @@ def lib() -> ctypes.CDLL:
                                      c_size_t, c_void_p]
         L.moe_mfma_peak.restype = c_int32
         L.moe_mfma_peak.argtypes = [c_int64, c_int32, c_void_p, POINTER(c_int64), c_void_p]
+        L.moe_hbm_read_peak.restype = c_int32
+        L.moe_hbm_read_peak.argtypes = [c_void_p, c_int64, c_void_p, c_void_p]
         L.moe_quantize_fp8.restype = c_int32
         L.moe_quantize_fp8.argtypes = [c_void_p, c_int32, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p]
         L.moe_forward_fp8.restype = c_int32
@@ -298,6 +301,19 @@ def mfma_peak(iters, sink, stream=None, varied=False) -> int:
     _check(lib().moe_mfma_peak(int(iters), 1 if varied else 0, _ptr(sink), ctypes.byref(fl), _stream(stream)),
            "moe_mfma_peak")
     return fl.value
+
+
+HBM_READ_SINK = 4096
+HBM_READ_BLOCK = 32768
+
+
+def hbm_read_peak(buf, sink, stream=None) -> int:
+    """Launch the read-stream calibration kernel (moe_hbm_read_peak) over every byte of the device tensor
+    `buf` (a multiple of HBM_READ_BLOCK bytes) on `stream`; sink: int32 device tensor of HBM_READ_SINK
+    entries.  Returns the bytes read (time the launch with events)."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().moe_hbm_read_peak(_ptr(buf), int(nbytes), _ptr(sink), _stream(stream)), "moe_hbm_read_peak")
+    return nbytes
 
 
 def quantize_fp8(w, codes, scales, stream=None):

@@ -480,6 +480,14 @@ moe_status moe_mfma_peak(int64_t iters, int32_t varied, float* sink, int64_t* fl
   return MOE_OK;
 }
 
+moe_status moe_hbm_read_peak(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < kReadBlockBytes || bytes % kReadBlockBytes != 0 || bytes > (int64_t(1) << 40)) return MOE_ERR_SHAPE;
+  MOE_TRY(need(buf));
+  MOE_TRY(need(sink));
+  HIP_TRY(launch_hbm_read(buf, bytes / kReadBlockBytes, sink, S(stream)));
+  return MOE_OK;
+}
+
 moe_status moe_forward_fp8(const moe_config* c, const moe_weights* w, const moe_fp8_experts* q, const void* x,
                            void* y, moe_route_out* ro, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(moe_validate(c));

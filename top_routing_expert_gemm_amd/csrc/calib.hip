@@ -1,6 +1,7 @@
-// Calibration kernel (not part of the layer): the bf16 MFMA rate the device
-// sustains, to set the grouped GEMMs' measured rate against what the matrix
-// cores reach with no memory traffic at all.
+// Calibration kernels (not part of the layer): the bf16 MFMA rate the device
+// sustains with no memory traffic at all, and the rate at which it reads a
+// large buffer from HBM with no arithmetic to speak of, to set the layer's
+// kernels against what each side of the chip reaches on its own.
 #include "common.h"
 
 namespace moe {
@@ -76,7 +77,61 @@ __global__ __launch_bounds__(kCalThreads) void mfma_peak_kernel(int iters, float
   if (lane == 0) sink[blockIdx.x * (kCalThreads / kWave) + threadIdx.x / kWave] = s;
 }
 
+constexpr int kReadWG = 4096;                // workgroups of the read stream
+constexpr int kReadThreads = 256;
+constexpr int kReadLoads = 8;                // 16-byte loads per thread per block
+static_assert(kReadThreads * kReadLoads * 16 == 32768, "one block is 32 KiB");
+
+__device__ __forceinline__ void read_block(uint4 (&r)[kReadLoads], const uint4* __restrict__ p, int64_t b) {
+  const uint4* q = p + b * (kReadThreads * kReadLoads) + threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kReadLoads; ++j) r[j] = q[j * kReadThreads];
+}
+
+__device__ __forceinline__ void xor_in(uint32_t& acc, const uint4 (&r)[kReadLoads]) {
+#pragma unroll
+  for (int j = 0; j < kReadLoads; ++j) acc ^= r[j].x ^ r[j].y ^ r[j].z ^ r[j].w;
+}
+
+// Workgroup w reads the 32 KiB blocks w, w + kReadWG, w + 2 kReadWG, ... (each
+// thread eight 16-byte vectors of a block, a block's loads one contiguous
+// sweep), the next block's loads issued before the current one is folded in,
+// and writes the XOR of every 32-bit word it read to sink[w].
+__global__ __launch_bounds__(kReadThreads) void hbm_read_kernel(const uint4* __restrict__ p, int64_t nblocks,
+                                                               uint32_t* __restrict__ sink) {
+  __shared__ uint32_t part[kReadThreads / kWave];
+  uint32_t acc = 0;
+  uint4 a[kReadLoads], b[kReadLoads];
+  int64_t blk = blockIdx.x;
+  if (blk < nblocks) read_block(a, p, blk);
+  for (; blk < nblocks; blk += 2 * kReadWG) {
+    const bool has_b = blk + kReadWG < nblocks;
+    if (has_b) read_block(b, p, blk + kReadWG);
+    xor_in(acc, a);
+    if (blk + 2 * kReadWG < nblocks) read_block(a, p, blk + 2 * kReadWG);
+    if (has_b) xor_in(acc, b);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m);
+  if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int w = 0; w < kReadThreads / kWave; ++w) v ^= part[w];
+    sink[blockIdx.x] = v;
+  }
+}
+
 }  // namespace
+
+int64_t hbm_read_sink_len() { return kReadWG; }
+
+hipError_t launch_hbm_read(const void* buf, int64_t nblocks, uint32_t* sink, hipStream_t s) {
+  hipLaunchKernelGGL(hbm_read_kernel, dim3(kReadWG), dim3(kReadThreads), 0, s, static_cast<const uint4*>(buf),
+                     nblocks, sink);
+  return hipGetLastError();
+}
 
 int64_t mfma_peak_flops(int64_t iters) {
   return (int64_t)kCalWG * (kCalThreads / kWave) * iters * kCalChains * (2LL * 32 * 32 * 16);

@@ -196,6 +196,11 @@ hipError_t launch_combine(const void* y_perm, const int32_t* row_of_slot, const 
 int64_t mfma_peak_flops(int64_t iters);
 int64_t mfma_peak_sink_len();
 hipError_t launch_mfma_peak(int iters, bool varied, float* sink, hipStream_t s);
+// Calibration: one read of nblocks 32 KiB blocks of buf; sink holds
+// hbm_read_sink_len() XORs of the words each workgroup read.
+constexpr int64_t kReadBlockBytes = 32768;
+int64_t hbm_read_sink_len();
+hipError_t launch_hbm_read(const void* buf, int64_t nblocks, uint32_t* sink, hipStream_t s);
 
 // Expert choice: chunk list of E groups of C rows each (+ shared rows), and the
 // per-expert top-C selection from scores [T, E].
