@@ -108,6 +108,27 @@ __device__ __forceinline__ bool xcd_map(int p, int V, int& L) {
   return true;
 }
 
+// Physical workgroup id -> logical tile id, dealing blocks of S consecutive
+// logical tiles to the XCDs in turn (block b to XCD b % 8, each XCD taking its
+// blocks in order); the tiles past the last whole round of 8 blocks are split
+// into contiguous ranges as above.  With S = SUPER * n_tiles a block is one
+// group of chunks that share weight tiles, so that sharing stays within one
+// XCD's L2, while every XCD gets its share of each part of the list: the
+// shared expert's chunks (last in a list, four to a weight tile, so lighter
+// on HBM) spread over all XCDs instead of filling the last one or two.
+__device__ __forceinline__ bool xcd_map_cyclic(int p, int V, int S, int& L) {
+  if (p >= V) return false;
+  const int Vm = V / (kXcds * S) * (kXcds * S);
+  if (p < Vm) {
+    const int x = p % kXcds, k = p / kXcds;
+    L = ((k / S) * kXcds + x) * S + k % S;
+    return true;
+  }
+  xcd_map(p - Vm, V - Vm, L);
+  L += Vm;
+  return true;
+}
+
 // Logical tile -> (chunk, n-tile): groups of up to SUPER chunks of one expert
 // take the n-tiles in turn, so they share each weight tile.
 __device__ __forceinline__ void tile_of(int L, int n_tiles, const Chunk* chunks, int& ci, int& nt) {
@@ -258,7 +279,7 @@ template <int MODE>
 __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles) {
   const int V = *a.n_chunks * n_tiles;
   int L;
-  if (!xcd_map(blockIdx.x, V, L)) return;
+  if (!xcd_map_cyclic(blockIdx.x, V, SUPER * n_tiles, L)) return;
   int ci, nt;
   tile_of(L, n_tiles, a.chunks, ci, nt);
   const Chunk ch = a.chunks[ci];
@@ -797,7 +818,7 @@ __global__ __launch_bounds__(RNT) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(1024))) u32x4 lds[2 * RROWS * 8];
   const int V = *a.n_chunks * n_tiles;
   int L;
-  if (!xcd_map(blockIdx.x, V, L)) return;
+  if (!xcd_map_cyclic(blockIdx.x, V, SUPER * n_tiles, L)) return;
   int ci, nt;
   tile_of(L, n_tiles, a.chunks, ci, nt);
   const Chunk ch = a.chunks[ci];
@@ -1158,7 +1179,7 @@ template <int MODE, int R3>
 __global__ __launch_bounds__(WNT) void grouped_gemm_ws(GemmArgs a, int n_tiles) {
   const int V = *a.n_chunks * n_tiles;
   int L;
-  if (!xcd_map(blockIdx.x, V, L)) return;
+  if (!xcd_map_cyclic(blockIdx.x, V, SUPER * n_tiles, L)) return;
   int ci, nt;
   tile_of(L, n_tiles, a.chunks, ci, nt);
   const Chunk ch = a.chunks[ci];
