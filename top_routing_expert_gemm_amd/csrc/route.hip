@@ -446,9 +446,19 @@ __global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __re
 #pragma unroll
         for (int j = 0; j < TPB; ++j) s[j] += q[u][j];
     }
-    for (; ks < nsplit; ++ks)
+    if (ks < nsplit) {  // the last < 8 slices: loads issued together, then added in slice order
+      float q[8][TPB];
 #pragma unroll
-      for (int j = 0; j < TPB; ++j) s[j] += t0 + j < T ? pp[ks * stride + (int64_t)j * Epad] : 0.f;
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < TPB; ++j)
+          q[u][j] = (ks + u < nsplit && t0 + j < T) ? pp[(ks + u) * stride + (int64_t)j * Epad] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (ks + u < nsplit)
+#pragma unroll
+          for (int j = 0; j < TPB; ++j) s[j] += q[u][j];
+    }
 #pragma unroll
     for (int j = 0; j < TPB; ++j) zs[j][e] = s[j];
   }
