@@ -421,8 +421,11 @@ __global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __re
                                                                RouteSel rs, int32_t* __restrict__ topk_idx,
                                                                float* __restrict__ topk_w) {
   constexpr int TPB = kRThreads / kWave;  // tokens per workgroup, one wave each for the top-k
-  __shared__ float wscr[TPB][kMaxE];
-  __shared__ float zs[TPB][kMaxE];
+  // dynamic LDS sized by E (topk_lds_bytes): the summed logits of the TPB tokens, then each wave's group
+  // scratch, E floats each, so a small E leaves room for more workgroups per CU
+  extern __shared__ __attribute__((aligned(16))) float tk_lds[];
+  float* zs = tk_lds;                 // [TPB][E]
+  float* wscr = tk_lds + TPB * E;     // [TPB][E]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * TPB;
   const int Epad = (E + 31) / 32 * 32;
@@ -460,7 +463,7 @@ __global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __re
           for (int j = 0; j < TPB; ++j) s[j] += q[u][j];
     }
 #pragma unroll
-    for (int j = 0; j < TPB; ++j) zs[j][e] = s[j];
+    for (int j = 0; j < TPB; ++j) zs[j * E + e] = s[j];
   }
   __syncthreads();
   const int t = t0 + wave;
@@ -469,9 +472,9 @@ __global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __re
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int e = lane + kWave * v;
-    z[v] = e < E ? (bias != nullptr ? zs[wave][e] + bias[e] : zs[wave][e]) : -INFINITY;
+    z[v] = e < E ? (bias != nullptr ? zs[wave * E + e] + bias[e] : zs[wave * E + e]) : -INFINITY;
   }
-  const SelOpts o{rs.sbias, rs.n_group, rs.topk_group, wscr[wave]};
+  const SelOpts o{rs.sbias, rs.n_group, rs.topk_group, wscr + wave * E};
   topk_token<VPL>(z, E, k, gate, renorm, scale, o, rs.scores ? rs.scores + (int64_t)t * E : nullptr,
                   topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
 }
@@ -574,7 +577,8 @@ hipError_t launch_route_split_t(const moe_config& c, const void* x, const void* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int tpb = kRThreads / kWave;
-  hipLaunchKernelGGL(route_topk_kernel<2 * NBW>, dim3((unsigned)((c.T + tpb - 1) / tpb)), dim3(kRThreads), 0, s,
+  const size_t lds = (size_t)2 * tpb * c.E * sizeof(float);
+  hipLaunchKernelGGL(route_topk_kernel<2 * NBW>, dim3((unsigned)((c.T + tpb - 1) / tpb)), dim3(kRThreads), lds, s,
                      part, nsplit_eff, (int)c.T, (int)c.E, bias, (int)c.k, c.gate, c.renormalize,
                      c.routed_scaling_factor, rs, idx, tw);
   return hipGetLastError();
