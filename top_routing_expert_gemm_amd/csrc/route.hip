@@ -379,9 +379,11 @@ __global__ __launch_bounds__(kRThreads) void route_bf16_kernel(
 }
 
 // Split-K router, part 1: workgroup (m, s) computes the partial logits of RBT*32
-// tokens over the s-th slice of H and stores them to part[s][t][0..Epad).
+// tokens over the s-th slice of H and stores them to part[s][t][0..Epad).  The
+// 128-token tiles of the largest batches are held to two waves per SIMD (within
+// 256 VGPRs), so two workgroups share a CU and hide each other's load latency.
 template <int NBW, int RBT>
-__global__ __launch_bounds__(kRThreads) void route_partial_bf16_kernel(
+__global__ __launch_bounds__(kRThreads) __attribute__((amdgpu_waves_per_eu(RBT == 4 ? 2 : 1))) void route_partial_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T, int H, int E, int ksteps_per_split,
     float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2 * RBT * kRBM * kRBK];
@@ -546,8 +548,7 @@ hipError_t launch_route_f32(const moe_config& c, const void* x, const void* w, c
 // and 64 for large ones (fewer passes over the router weights per token), 32
 // otherwise and for E > 512 (register budget).
 // Split factor of the K dimension: enough workgroups to cover the chip twice
-// (once with 128-token blocks, whose partials are twice as many per token),
-// each slice at least four K steps long.
+// (two 128-token workgroups fit per CU), each slice at least four K steps long.
 inline int route_rbt(int64_t T, int64_t E) {
   if (T >= 8192 && E <= 256) return 4;
   return T >= 4096 && E <= 512 ? 2 : 1;
@@ -557,7 +558,7 @@ inline int route_nsplit(int64_t T, int64_t H, int64_t E) {
   const int64_t rows = rbt * kRBM;
   const int64_t mt = (T + rows - 1) / rows;
   const int64_t nk = H / kRBK;
-  const int64_t target = rbt == 4 ? 256 : 512;
+  const int64_t target = 512;
   int64_t ns = (target + mt - 1) / mt;
   ns = std::min<int64_t>(ns, std::max<int64_t>(1, nk / 4));
   return (int)std::max<int64_t>(1, ns);
