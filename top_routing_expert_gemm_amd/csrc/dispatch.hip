@@ -72,20 +72,22 @@ __global__ __launch_bounds__(64) void hist_rank_kernel(const int32_t* __restrict
   for (int e = lane; e < E; e += 64) blk_counts[b * E + e] = cnt[e];
 }
 
-// Inclusive scan over the block (one value per thread, blockDim.x == kScanThreads).
+// Inclusive scan over the block (one value per thread, blockDim.x == kScanThreads):
+// a shuffle scan within each wave, then each wave adds the totals of the waves
+// before it (tmp[0 .. kScanThreads / 64) holds them); two barriers in all.
 __device__ int block_inclusive_scan(int v, int* tmp) {
-  const int tid = threadIdx.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int add = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
   }
-  const int r = tmp[tid];
+  if (lane == kWave - 1) tmp[wave] = x;
   __syncthreads();
-  return r;
+  for (int w = 0; w < wave; ++w) x += tmp[w];
+  __syncthreads();  // tmp is free again when this returns
+  return x;
 }
 
 // Which list a group of L rows goes to.  With one list (bm_b == 0) every group
@@ -168,29 +170,55 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   __shared__ int tmp[kScanThreads];
   const int tid = threadIdx.x;
   const int e = tid;
-  int load = 0;
-  if (e < E) {
-    // exclusive block bases, sixteen independent loads per round, summed in block order
-    int run = 0;
-    int64_t b = 0;
-    for (; b + 16 <= nb; b += 16) {
+  // exclusive block bases per expert, in block order: P threads per expert (thread q * E + e2 takes
+  // blocks [q nb / P, (q + 1) nb / P) of expert e2), each summing its range, then rewriting it from
+  // the sum of the ranges before it; sixteen independent loads per round
+  const int P = max(1, kScanThreads / E);
+  const int q = tid / E, e2 = tid - q * E;
+  const bool part = q < P;
+  const int64_t b0 = part ? q * nb / P : 0, b1 = part ? (q + 1) * nb / P : 0;
+  int sum = 0;
+  {
+    int64_t b = b0;
+    for (; b + 16 <= b1; b += 16) {
       int c[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) c[u] = blk_counts[(b + u) * E + e];
+      for (int u = 0; u < 16; ++u) c[u] = blk_counts[(b + u) * E + e2];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) sum += c[u];
+    }
+    for (; b < b1; ++b) sum += blk_counts[b * E + e2];
+  }
+  tmp[tid] = sum;
+  __syncthreads();
+  if (part) {
+    int run = 0;
+    for (int r = 0; r < q; ++r) run += tmp[r * E + e2];
+    int64_t b = b0;
+    for (; b + 16 <= b1; b += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c[u] = blk_counts[(b + u) * E + e2];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        blk_counts[(b + u) * E + e] = run;
+        blk_counts[(b + u) * E + e2] = run;
         run += c[u];
       }
     }
-    for (; b < nb; ++b) {
-      const int c = blk_counts[b * E + e];
-      blk_counts[b * E + e] = run;
+    for (; b < b1; ++b) {
+      const int c = blk_counts[b * E + e2];
+      blk_counts[b * E + e2] = run;
       run += c;
     }
+  }
+  int load = 0;
+  if (e < E) {
+    int run = 0;
+    for (int r = 0; r < P; ++r) run += tmp[r * E + e];
     counts[e] = run;
     load = cap < 0 ? run : (int)min((int64_t)run, cap);
   }
+  __syncthreads();  // tmp is reused by the scans below
   const int incl = block_inclusive_scan(load, tmp);
   const int excl = incl - load;
   if (e < E) offsets[e] = excl;
