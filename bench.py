@@ -136,8 +136,9 @@ def achievable(moe, torch):
     ms_read = event_ms(torch, read, 10, 3)
     del rbuf, rsink
     m, kk, nn = 8192 * 9, 7168, 4096
-    a = torch.randn(m, kk, device="cuda").to(torch.bfloat16)
-    b = torch.randn(kk, nn, device="cuda").to(torch.bfloat16)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn(m, kk, device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn(kk, nn, device="cuda", generator=g).to(torch.bfloat16)
     ms_mm = event_ms(torch, lambda: torch.matmul(a, b), 10, 3)
     del a, b
     torch.cuda.empty_cache()
