@@ -92,13 +92,33 @@ def test_capacity_reading():
         ref.select_expert_choice(np.zeros((3, 2)), 4)
 
 
-def test_pins_catch_planted_mistakes():
-    """Plausible slips in the selection fail the brute-force pin."""
-    r = np.random.default_rng(11)
-    s = r.random((7, 3))
-    C = 3
-    wrong_order = np.sort(np.argsort(s, axis=0, kind="stable")[:C], axis=0).T     # lowest scores
-    wrong_axis = np.sort(np.argsort(-s, axis=1, kind="stable")[:, :C], axis=1)    # per token, not per expert
-    truth = [brute_choice(s[:, e], C) for e in range(3)]
-    assert [list(r_) for r_ in wrong_order] != truth
-    assert wrong_axis.shape != (3, C) or [list(r_) for r_ in wrong_axis[:3]] != truth
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Plausible slips planted in the oracle's selection fail the brute-force pin:
+    the C lowest scores instead of the highest, and a per-token top-C (along the
+    wrong axis) instead of per expert."""
+    def lowest(scores, C):
+        order = np.argsort(scores, axis=0, kind="stable")
+        return np.sort(order[:C], axis=0).T, np.ones(scores.shape[1])
+
+    def per_token(scores, C):
+        T, E = scores.shape
+        order = np.argsort(-scores, axis=1, kind="stable")[:, :min(C, E)]
+        out = np.zeros((E, C), dtype=np.int64)
+        for e in range(E):       # expert e takes the tokens whose own top-C holds e, padded with token 0
+            mine = [t for t in range(T) if e in order[t]][:C]
+            out[e, :len(mine)] = mine
+        return np.sort(out, axis=1), np.ones(E)
+
+    def pin():
+        for T, E in ((5, 1), (6, 2), (7, 3)):
+            test_selection_brute_force(T, E)
+    pin()
+    for name, bad in (("lowest scores", lowest), ("per-token top-C", per_token)):
+        with monkeypatch.context() as m:
+            m.setattr(ref, "select_expert_choice", bad)
+            try:
+                pin()
+                caught = False
+            except AssertionError:
+                caught = True
+        assert caught, name

@@ -79,10 +79,64 @@ def test_zero_block_and_shape_checks():
         ref.quantize_fp8_blockwise(np.zeros((1, 100, 128), dtype=np.float32))
 
 
-def test_pins_catch_planted_mistakes():
-    """Round-half-up instead of ties-to-even, or a 2^-7 subnormal step (the other
-    common E4M3 variant), each fail a pin above."""
-    c_up = int(np.searchsorted(ref.E4M3_VALUES[:0x7F], 1.0625, side="right"))   # half-up picks 0x39
-    assert c_up != 0x38
-    fnuz_smallest = 2.0 ** -10
-    assert ref.E4M3_VALUES[0x01] != fnuz_smallest
+def _fails(check):
+    try:
+        check()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Plausible slips planted in the oracle's quantiser each fail a pin above:
+    round-half-up instead of ties to the even code, truncation toward zero, the
+    other common E4M3 variant (exponent bias 8: subnormal step 2^-10, largest
+    finite 240) and a scale that maps the block maximum to 240 instead of 448."""
+    pins = (test_e4m3_table_closed_forms, test_representable_values_round_trip_exactly,
+            test_ties_go_to_the_even_code, test_rounding_bound_and_block_max)
+    for p in pins:          # the oracle as it stands passes every pin
+        p()
+    pos = ref._E4M3_POS
+
+    def half_up(q32):
+        a = np.abs(q32.astype(np.float64))
+        hi = np.clip(np.searchsorted(pos, a, side="left"), 1, 0x7E)
+        lo = hi - 1
+        code = np.where(a - pos[lo] < pos[hi] - a, lo, hi)
+        code = np.where(a >= pos[0x7E], 0x7E, np.where(a == 0, 0, code))
+        return (code | np.where(np.signbit(q32), 0x80, 0)).astype(np.uint8)
+
+    def toward_zero(q32):
+        a = np.abs(q32.astype(np.float64))
+        code = np.clip(np.searchsorted(pos, a, side="right") - 1, 0, 0x7E)
+        return (code | np.where(np.signbit(q32), 0x80, 0)).astype(np.uint8)
+
+    def fnuz_value(code):
+        sign = -1.0 if code & 0x80 else 1.0
+        e, m = (code >> 3) & 15, code & 7
+        if code == 0x80:
+            return float("nan")
+        return sign * (m / 8.0 * 2.0 ** -7 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 8))
+    fnuz = np.array([fnuz_value(c) for c in range(256)])
+
+    def scale_240(w_bits, block=128):
+        w = ref.widen(w_bits).astype(np.float32)
+        G, N, K = w.shape
+        blk = w.reshape(G, N // block, block, K // block, block)
+        amax = np.abs(blk).max(axis=(2, 4))
+        scale = np.where(amax > 0, amax / np.float32(240.0), np.float32(1.0)).astype(np.float32)
+        q = (blk / scale[:, :, None, :, None]).astype(np.float32)
+        return ref._nearest_e4m3(q).reshape(G, N, K), scale
+
+    slips = {
+        "round half up": {"_nearest_e4m3": half_up},
+        "truncate toward zero": {"_nearest_e4m3": toward_zero},
+        "bias-8 variant": {"E4M3_VALUES": fnuz, "_E4M3_POS": fnuz[:0x7F]},
+        "block max to 240": {"quantize_fp8_blockwise": scale_240},
+    }
+    for name, patch in slips.items():
+        with monkeypatch.context() as m:
+            for attr, v in patch.items():
+                m.setattr(ref, attr, v)
+            caught = [p.__name__ for p in pins if _fails(p)]
+        assert caught, f"no pin catches the planted slip: {name}"
