@@ -13,8 +13,13 @@ The decode layer (T=16 through the same weights) is timed too and reported
 under "decode", with bf16 and with FP8 (E4M3, 128x128 block scales) expert
 weights.  "variants" times the other routing paths on the prefill workload:
 DeepSeek-V3 group-limited selection with a selection bias, the routing
-statistics and bias step, and expert-choice routing.  The CPU baseline is the
-float64 oracle on a bounded sample of the same workload, on the host cores.
+statistics and bias step, and expert-choice routing.  "workloads" times the
+other layer workloads at full size (the skewed Switch-style layer with a
+capacity limit, the Mixtral-shaped layer, the tiny fp32 layer), each against
+both published roofs.  The CPU baseline is the float64 oracle on a bounded
+sample of the same workload, on the host cores.
+
+    python bench.py --workload switch_capacity_bf16   # one other workload alone (profiling)
 """
 from __future__ import annotations
 
@@ -46,6 +51,10 @@ def parse():
     p.add_argument("--no-variants", action="store_true")
     p.add_argument("--no-achievable", action="store_true")
     p.add_argument("--no-clock", action="store_true", help="skip sampling the shader clock under sustained load")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="skip timing the Switch, Mixtral and tiny workloads after the main one")
+    p.add_argument("--workload", default=None,
+                   help="time only this workload (a name of synth.WORKLOADS) and print its line; for profiling")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (reference for HBM counters)")
     return p.parse_args()
@@ -158,23 +167,35 @@ def achievable(moe, torch):
 
 def sustained_sclk(torch, fn, seconds=2.5):
     """Median shader clock (MHz) that rocm-smi reports while fn runs back to back for
-    `seconds` (reading only; None where rocm-smi is missing or prints nothing usable)."""
+    `seconds` (reading only; None where rocm-smi is missing or prints nothing usable).
+    The poller keeps the handle of its one rocm-smi child and, when told to stop,
+    terminates (then kills) and reaps it, so no child outlives this call."""
     import re, shutil, subprocess, threading, time
     exe = shutil.which("rocm-smi")
     if exe is None:
         return None
     got, stop = [], threading.Event()
+    child = {"p": None}
 
     def poll():
         while not stop.is_set():
             try:
-                r = subprocess.run([exe, "--showgpuclocks", "--json"], capture_output=True, text=True, timeout=10)
-                m = re.search(r"sclk clock level[^(]*\((\d+)\s*Mhz\)", r.stdout)
+                p = subprocess.Popen([exe, "--showgpuclocks", "--json"], stdout=subprocess.PIPE,
+                                     stderr=subprocess.DEVNULL, text=True)
+                child["p"] = p
+                try:
+                    out, _ = p.communicate(timeout=10)
+                except subprocess.TimeoutExpired:
+                    p.kill()
+                    p.communicate()
+                    out = ""
+                child["p"] = None
+                m = re.search(r"sclk clock level[^(]*\((\d+)\s*Mhz\)", out or "")
                 if m:
                     got.append(int(m.group(1)))
             except Exception:
                 pass
-            time.sleep(0.2)
+            stop.wait(0.2)
 
     for _ in range(3):
         fn()
@@ -188,6 +209,15 @@ def sustained_sclk(torch, fn, seconds=2.5):
         torch.cuda.synchronize()
     stop.set()
     th.join(timeout=15)
+    p = child["p"]
+    if p is not None and p.poll() is None:   # a poll still running: end it and reap it
+        p.terminate()
+        try:
+            p.wait(timeout=5)
+        except subprocess.TimeoutExpired:
+            p.kill()
+            p.wait()
+    th.join(timeout=5)
     return float(sorted(got)[len(got) // 2]) if got else None
 
 
@@ -230,6 +260,75 @@ def variants(moe, torch, np, s, dev, x, y, ws, steps, warmup):
     return res
 
 
+def layer_roofline(s, counts, R, ms_step, ms_gemm, esz):
+    """Algorithmic work of one layer step and where it sits against both published roofs.
+
+    flops: the grouped GEMMs, 2 (R + shared rows) 3 H I (plus the router GEMM,
+    reported apart).  bytes: every touched expert's weights once, the router
+    weights, x once, h written and read once, y_perm written and read once, y
+    written once.  bound: "hbm" when flops / bytes is below the ridge
+    (2.5 PFLOP/s over 8 TB/s), else "mfma"; frac is against that roof."""
+    rows = R + s.T * s.n_shared
+    touched = int((counts > 0).sum()) + s.n_shared
+    fl_gemm = 2.0 * rows * 3 * s.H * s.I
+    fl_router = 2.0 * s.T * s.H * s.E
+    by = float(touched * 3 * s.H * s.I * esz + s.E * s.H * esz + s.T * s.H * esz
+               + 2 * rows * s.I * esz + 2 * rows * s.H * esz + s.T * s.H * esz)
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    inten = (fl_gemm + fl_router) / by
+    gbps = by / (ms_step * 1e-3) / 1e9
+    tflops_gemm = fl_gemm / (ms_gemm * 1e-3) / 1e12
+    bound = "hbm" if inten < ridge else "mfma"
+    return {"bound": bound, "intensity_flop_per_byte": inten, "ridge_flop_per_byte": ridge,
+            "algorithmic_bytes": by, "layer_GBps": gbps, "frac_hbm_peak": gbps / PEAK_HBM_GBPS,
+            "grouped_gemm_flops": fl_gemm, "grouped_gemm_TFLOPs": tflops_gemm,
+            "frac_mfma_peak": tflops_gemm / PEAK_BF16_TFLOPS,
+            "layer_TFLOPs": (fl_gemm + fl_router) / (ms_step * 1e-3) / 1e12,
+            "frac": gbps / PEAK_HBM_GBPS if bound == "hbm" else tflops_gemm / PEAK_BF16_TFLOPS,
+            "touched_experts": touched - s.n_shared, "kept_rows": R}
+
+
+def other_workloads(moe, torch, np, names, steps, warmup):
+    """The other layer workloads at full size, each timed like the main one (stage
+    events in every step), with their place against both roofs."""
+    from synth import WORKLOADS, make_inputs
+    from synth.device import bits, upload
+    res = {}
+    for name in names:
+        s = WORKLOADS[name]
+        inp = make_inputs(s)
+        dev = upload(inp)
+        cfg = moe.config_from_shape(s)
+        dt = torch.bfloat16 if s.dtype == moe.BF16 else torch.float32
+        y = torch.empty((s.T, s.H), dtype=dt, device="cuda")
+        ws = torch.empty(moe.workspace_size(cfg), dtype=torch.uint8, device="cuda")
+        route = {"counts": torch.empty((s.E,), dtype=torch.int32, device="cuda"),
+                 "offsets": torch.empty((s.E + 1,), dtype=torch.int32, device="cuda")}
+        secs, st, per_step = timed_forward(moe, torch, cfg, dev, dev["x"], y, ws, route, steps, warmup)
+        counts = bits(route["counts"])
+        R = int(bits(route["offsets"])[-1])
+        avg = {n: float(np.mean(v)) for n, v in st.items()}
+        ms = secs / steps * 1e3
+        esz = 2 if s.dtype == moe.BF16 else 4
+        line = {"workload": s.name, "T": s.T, "H": s.H, "moe_intermediate": s.I, "E": s.E, "k": s.k,
+                "capacity_factor": s.capacity_factor or None, "dtype": "bf16" if esz == 2 else "f32",
+                "ms_per_step": ms, "tokens_per_s": s.T / (ms * 1e-3), "stages_ms": avg,
+                "step_ms_events": {"median": float(np.median(per_step)), "min": float(np.min(per_step)),
+                                   "max": float(np.max(per_step))},
+                "dropped_assignments": int(s.T * s.k - R)}
+        if esz == 2:
+            line["roofline"] = layer_roofline(s, counts, R, float(np.median(per_step)),
+                                              avg["gateup"] + avg["down"], esz)
+        else:
+            line["roofline"] = {"bound": "launch", "note": "correctness workload: a few microseconds of work "
+                                                           "per stage, launch latency dominates"}
+        res[s.name] = line
+        del dev, y, ws, inp
+        torch.cuda.empty_cache()
+        print(f"[bench] {s.name}: {ms:.3f} ms per step", file=sys.stderr, flush=True)
+    return res
+
+
 def cpu_baseline(inp, s, n_tok):
     """The float64 oracle, as it stands, on the first n_tok tokens of the batch as a layer of their own."""
     import numpy as np
@@ -262,11 +361,14 @@ def main():
     import torch
 
     import top_routing_expert_gemm_amd as moe
-    from synth import DS_DECODE, DS_PREFILL, WORKLOADS, make_inputs
+    from synth import DS_DECODE, DS_PREFILL, MIXTRAL, SWITCH, TINY, WORKLOADS, make_inputs
     from synth.device import bits, to_torch, upload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.lib()
+    if a.workload is not None and a.workload != DS_PREFILL:
+        print(json.dumps({"workload_only": other_workloads(moe, torch, np, [a.workload], a.steps, a.warmup)}))
+        return
     s = WORKLOADS[DS_PREFILL]
     t_gen = time.perf_counter()
     inp = make_inputs(s)
@@ -312,6 +414,30 @@ def main():
     gateup_tflops = fl_gateup / (avg["gateup"] * 1e-3) / 1e12
     gemm_tflops = (fl_gateup + fl_down) / ((avg["gateup"] + avg["down"]) * 1e-3) / 1e12
     traffic = traffic_entry(avg["gateup"])
+    # the gate/up stage against both published roofs: its intensity (flops over its
+    # algorithmic bytes) below the ridge puts it on the HBM side, and frac is then
+    # the HBM fraction; the MFMA fraction is kept beside it
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    gateup_gbps = by_gateup / (avg["gateup"] * 1e-3) / 1e9
+    intensity = fl_gateup / by_gateup
+    hbm_bound = intensity < ridge
+    roof = {"bound": "hbm" if hbm_bound else "mfma",
+            "kernel": "gate/up+SwiGLU grouped GEMM stage: grouped_gemm_rs<0> (256-row chunk list) + "
+                      "grouped_gemm_ws<0> (320-row chunk list), one launch each",
+            "achieved": gateup_gbps if hbm_bound else gateup_tflops,
+            "peak": PEAK_HBM_GBPS if hbm_bound else PEAK_BF16_TFLOPS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": gateup_gbps / PEAK_HBM_GBPS if hbm_bound else gateup_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "avg_launch_ms": avg["gateup"],
+            "intensity_flop_per_byte": intensity, "ridge_flop_per_byte": ridge,
+            "mfma_side": {"flops_per_launch": fl_gateup, "achieved_TFLOPs": gateup_tflops,
+                          "frac_mfma_peak": gateup_tflops / PEAK_BF16_TFLOPS},
+            "hbm_side": {"algorithmic_bytes_per_launch": by_gateup, "achieved_GBps": gateup_gbps,
+                         "frac_hbm_peak": gateup_gbps / PEAK_HBM_GBPS},
+            "down_pass": {"flops_per_launch": fl_down, "avg_launch_ms": avg["down"],
+                          "achieved_TFLOPs": fl_down / (avg["down"] * 1e-3) / 1e12,
+                          "frac_mfma_peak": fl_down / (avg["down"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
 
     out = {
         "metric": "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), DeepSeek-V3 shape",
@@ -321,17 +447,7 @@ def main():
         "config": {"workload": s.name, "T": s.T, "H": s.H, "moe_intermediate": s.I, "E": s.E, "k": s.k,
                    "gate": "sigmoid", "routed_scaling_factor": s.routed_scaling_factor, "n_shared": s.n_shared,
                    "capacity_factor": None, "global_batch": s.T, "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma",
-                     "kernel": "gate/up+SwiGLU grouped GEMM stage: grouped_gemm_rs<0> (256-row chunk list) + "
-                               "grouped_gemm_ws<0> (320-row chunk list), one launch each",
-                     "achieved": gateup_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gateup_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "flops_per_launch": fl_gateup, "avg_launch_ms": avg["gateup"],
-                     "hbm_side": {"algorithmic_bytes_per_launch": by_gateup,
-                                  "achieved_GBps": by_gateup / (avg["gateup"] * 1e-3) / 1e9,
-                                  "frac_hbm_peak": by_gateup / (avg["gateup"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                                  "intensity_flop_per_byte": fl_gateup / by_gateup,
-                                  "ridge_flop_per_byte": PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)}},
+        "roofline": roof,
         "grouped_gemm": {"tflops": gemm_tflops, "frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS,
                          "flops": fl_gateup + fl_down, "ms": avg["gateup"] + avg["down"]},
         "stages_ms": avg,
@@ -400,12 +516,15 @@ def main():
     if not a.no_variants:
         out["variants"] = variants(moe, torch, np, s, dev, x, y, ws, a.steps, a.warmup)
         print("[bench] routing variants timed", file=sys.stderr, flush=True)
+    if not a.no_workloads:
+        out["workloads"] = other_workloads(moe, torch, np, [SWITCH, MIXTRAL, TINY], a.steps, a.warmup)
     if not a.no_achievable:
         out["achievable"] = achievable(moe, torch)
         g = out["achievable"]
-        out["roofline"]["frac_of_achievable"] = gateup_tflops / g["dense_bf16_gemm_TFLOPs"]
-        out["roofline"]["frac_of_mfma_loop"] = gateup_tflops / g["mfma_loop_bf16_TFLOPs"]
-        out["roofline"]["frac_of_mfma_loop_varied"] = gateup_tflops / g["mfma_loop_varied_bf16_TFLOPs"]
+        ms_ = out["roofline"]["mfma_side"]
+        ms_["frac_of_achievable"] = gateup_tflops / g["dense_bf16_gemm_TFLOPs"]
+        ms_["frac_of_mfma_loop"] = gateup_tflops / g["mfma_loop_bf16_TFLOPs"]
+        ms_["frac_of_mfma_loop_varied"] = gateup_tflops / g["mfma_loop_varied_bf16_TFLOPs"]
         hs = out["roofline"]["hbm_side"]
         hs["frac_of_read_stream"] = hs["achieved_GBps"] / g["hbm_read_GBps"]
         if traffic is not None:

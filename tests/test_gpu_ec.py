@@ -13,8 +13,8 @@ import torch
 
 import oracle.moe_ref as ref
 import top_routing_expert_gemm_amd as moe
-from moe_gpu import NEAR_TIE, TOL, bits, check_rows, require_gpu, widen_out
-from synth import BF16, F32, GATE_SIGMOID, GATE_SOFTMAX, MoEShape, balance_inputs, make_inputs
+from moe_gpu import bits, ec_parity, require_gpu
+from synth import F32, GATE_SIGMOID, GATE_SOFTMAX, MoEShape, balance_inputs, make_inputs
 from synth.device import to_torch, upload
 
 pytestmark = pytest.mark.gpu
@@ -98,39 +98,7 @@ def sample(T, n, seed):
 def test_forward_ec(name):
     s = CASES[name]
     inp = make_inputs(s)
-    dev = upload(inp)
-    cfg = moe.config_from_shape(s)
-    C = moe.ec_capacity(cfg)
-    dt = torch.bfloat16 if s.dtype == BF16 else torch.float32
-    y = torch.full((s.T, s.H), float("nan"), dtype=dt, device="cuda")
-    out = {"scores": torch.empty((s.T, s.E), dtype=torch.float32, device="cuda"),
-           "token_of_row": torch.full((s.E * C,), -7, dtype=torch.int32, device="cuda"),
-           "row_of_pair": torch.full((s.T, s.E), -7, dtype=torch.int32, device="cuda")}
-    ws = torch.empty(moe.ec_workspace_size(cfg), dtype=torch.uint8, device="cuda")
-    moe.forward_ec(cfg, dev, dev["x"], y, ws, ec_out=out)
-    torch.cuda.synchronize()
-
-    tok = sample(s.T, 24, s.cfg_id)
-    shared = (inp.ws_gate, inp.ws_up, inp.ws_down) if s.n_shared else None
-    yref, rr = ref.moe_forward_ec(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down,
-                                  gate=s.gate, routed_scaling_factor=float(np.float32(s.routed_scaling_factor)),
-                                  C=C, shared=shared, tokens=tok)
-    assert np.abs(bits(out["scores"]).astype(np.float64) - rr["scores"]).max() <= 1e-5
-    g_chosen = bits(out["token_of_row"]).reshape(s.E, C)
-    ties = np.nonzero(rr["gap"] < NEAR_TIE)[0]
-    ok = np.setdiff1d(np.arange(s.E), ties)
-    assert np.array_equal(g_chosen[ok], rr["chosen"][ok]), "chosen tokens differ from the oracle's"
-    # tokens whose pairs a near-tie expert may have decided differently
-    moved = set()
-    for e in ties:
-        moved |= set(np.setxor1d(g_chosen[e], rr["chosen"][e]).tolist())
-    keep = np.array([int(t) not in moved for t in tok])
-    assert keep.mean() >= 0.9
-    yg = widen_out(y)[tok]
-    worst = check_rows(yg[keep], yref[keep], s.dtype, s.name)
-    per_token = np.bincount(rr["chosen"].ravel(), minlength=s.T)
-    print(f"{name}: C={C} near-tie experts={len(ties)} unchosen tokens={(per_token == 0).sum()} "
-          f"worst_row_rel_err={worst:.3e}")
+    ec_parity(s, inp, upload(inp), lambda chosen: sample(s.T, 24, s.cfg_id))
 
 
 def test_unchosen_tokens_get_exactly_zero_without_shared():

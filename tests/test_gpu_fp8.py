@@ -63,24 +63,22 @@ def test_quantize_fp32_matches_oracle():
     assert np.array_equal(scales, rs) and np.array_equal(codes, rc)
 
 
-def oracle_fp8(inp, s, experts):
-    """Oracle codes/scales of the listed routed experts (others zero) and of the shared expert."""
+def oracle_fp8(inp, s, experts, threads=8):
+    """Oracle codes/scales of the listed routed experts (others zero) and of the
+    shared expert, plus e -> dequantised (gate, up, down) computed on demand
+    (code value x block scale, exact in float64) and the dequantised shared expert."""
     E, I, H = s.E, s.I, s.H
     q = {"w_gate": np.zeros((E, I, H), np.uint8), "w_up": np.zeros((E, I, H), np.uint8),
          "w_down": np.zeros((E, H, I), np.uint8), "s_gate": np.ones((E, I // 128, H // 128), np.float32),
          "s_up": np.ones((E, I // 128, H // 128), np.float32), "s_down": np.ones((E, H // 128, I // 128), np.float32)}
-    deq = {}
 
     def one(e):
         g, u, d = (inp.w_gate[e], inp.w_up[e], inp.w_down[e]) if inp.w_gate is not None else expert_weights(s, e)
-        out = []
         for name, w in (("gate", g), ("up", u), ("down", d)):
             c, sc = ref.quantize_fp8_blockwise(w[None])
             q["w_" + name][e], q["s_" + name][e] = c[0], sc[0]
-            out.append(ref.dequantize_fp8_blockwise(c, sc)[0])
-        deq[e] = tuple(out)
 
-    with ThreadPoolExecutor(8) as ex:
+    with ThreadPoolExecutor(threads) as ex:
         list(ex.map(one, experts))
     shared = None
     if s.n_shared:
@@ -90,17 +88,21 @@ def oracle_fp8(inp, s, experts):
             q["ws_" + name], q["ss_" + name] = c[0], sc[0]
             sh.append(ref.dequantize_fp8_blockwise(c, sc)[0])
         shared = tuple(sh)
+
+    def deq(e):
+        return tuple(ref.dequantize_fp8_blockwise(q["w_" + n][e][None], q["s_" + n][e][None])[0]
+                     for n in ("gate", "up", "down"))
     return q, deq, shared
 
 
-def run_fp8_case(s, n_touch_all=True):
+def run_fp8_case(s, n_touch_all=True, threads=8):
     inp = make_inputs(s, with_experts=n_touch_all)
     T = s.T
     # the oracle's routing decides which experts it needs
     r0 = ref.route(inp.x, inp.w_router, inp.router_bias, s.k, s.gate, s.renormalize,
                    float(np.float32(s.routed_scaling_factor)))
     experts = sorted(set(r0["topk_idx"].ravel().tolist())) if not n_touch_all else list(range(s.E))
-    q, deq, shared = oracle_fp8(inp, s, experts)
+    q, deq, shared = oracle_fp8(inp, s, experts, threads)
     dev = {"x": to_torch(inp.x, "cuda"), "w_router": to_torch(inp.w_router, "cuda")}
     qd = {k: to_torch(v, "cuda") for k, v in q.items()}
     cfg = moe.config_from_shape(s)
@@ -109,7 +111,7 @@ def run_fp8_case(s, n_touch_all=True):
     ws = torch.empty(moe.workspace_size(cfg), dtype=torch.uint8, device="cuda")
     moe.forward_fp8(cfg, dev, qd, dev["x"], y, ws, route_out=r)
     torch.cuda.synchronize()
-    yref, rr = ref.moe_forward(inp.x, inp.w_router, inp.router_bias, lambda e: deq[e], None, None,
+    yref, rr = ref.moe_forward(inp.x, inp.w_router, inp.router_bias, deq, None, None,
                                shared=shared, **oracle_kwargs(s))
     ties = compare_routing(s, rr, bits(r["topk_idx"]), bits(r["topk_w"]))
     keep = np.ones(T, dtype=bool)
@@ -138,6 +140,17 @@ def test_forward_fp8_deepseek_routing_narrow_experts():
     s = MoEShape("deepseek_v3_fp8_decode_narrow", T=16, H=7168, I=128, E=256, k=8, gate=GATE_SIGMOID,
                  routed_scaling_factor=2.5, n_shared=1, I_shared=128, cfg_id=604)
     run_fp8_case(s, n_touch_all=False)
+
+
+@pytest.mark.timeout(900)
+def test_forward_fp8_deepseek_full_width():
+    """The DeepSeek-V3 decode layer at its real width (T 16, H 7168, I 2048, E 256,
+    top-8 sigmoid x2.5, shared expert), so the FP8 down pass runs at K = 2048;
+    only the experts the oracle routes to are quantised (on the host, by the
+    oracle's quantiser)."""
+    s = MoEShape("deepseek_v3_fp8_decode", T=16, H=7168, I=2048, E=256, k=8, gate=GATE_SIGMOID,
+                 routed_scaling_factor=2.5, n_shared=1, I_shared=2048, cfg_id=605)
+    run_fp8_case(s, n_touch_all=False, threads=16)
 
 
 def test_forward_fp8_rejects_unsupported():

@@ -1,8 +1,9 @@
 """GPU parity: every entry point of the C ABI against the float64 oracle.
 
 Small shapes span several tiles and a ragged tail; the five layer workloads run
-at full size with outputs compared on sampled tokens (routing and dispatch on
-all tokens).  Comparison rules are documented in tests/moe_gpu.py.
+at full size with outputs compared on sampled tokens, among them every token of
+chosen expert groups (whole row chunks of both chunk lists and of the shared
+expert); routing and dispatch on all tokens.  Comparison rules are documented in tests/moe_gpu.py.
 """
 import zlib
 
@@ -12,9 +13,11 @@ import torch
 
 import oracle.moe_ref as ref
 import top_routing_expert_gemm_amd as moe
-from moe_gpu import (TOL, alloc_route, bits, check_rows, compare_dispatch, compare_routing, full_parity,
-                     gpu_forward, oracle_kwargs, require_gpu, widen_out, workspace)
-from synth import BF16, DS_DECODE, DS_PREFILL, F32, MIXTRAL, SWITCH, TINY, WORKLOADS, GATE_SIGMOID, GATE_SOFTMAX, MoEShape, make_inputs
+from moe_gpu import (TOL, alloc_route, bits, check_rows, compare_dispatch, compare_routing, ec_parity,
+                     expert_tokens, full_parity, gpu_forward, oracle_kwargs, require_gpu, sample_tokens, widen_out,
+                     workspace)
+from synth import (BF16, DS_DECODE, DS_PREFILL, F32, GATE_SIGMOID, GATE_SOFTMAX, MIXTRAL, NOAUX, SWITCH, TINY,
+                   WORKLOADS, MoEShape, make_inputs)
 from synth.device import to_torch, upload
 
 pytestmark = pytest.mark.gpu
@@ -271,8 +274,9 @@ _cache = {}
 
 
 def _inputs(name):
-    """Inputs of one workload; keeps at most one weight namespace resident."""
-    s = WORKLOADS[name]
+    """Inputs of one workload (a name of WORKLOADS or a shape); keeps at most one
+    weight namespace resident."""
+    s = WORKLOADS[name] if isinstance(name, str) else name
     if _cache.get("wid") != s.wid:
         _cache.clear()
         torch.cuda.empty_cache()
@@ -285,14 +289,49 @@ def _inputs(name):
         setattr(inp, n, getattr(base, n))
     dev = dict(_cache["dev"])
     dev["x"] = to_torch(inp.x, "cuda")
+    if inp.score_bias is not None:
+        dev["score_bias"] = to_torch(inp.score_bias, "cuda")
     return s, inp, dev
 
 
-@pytest.mark.parametrize("name,n_sample", [(TINY, None), (SWITCH, 96), (MIXTRAL, 32), (DS_PREFILL, 16),
-                                            (DS_DECODE, None)])
-def test_forward_workload(name, n_sample):
+def _whole_groups(name, s):
+    """Token picks of a full-size workload: random tokens plus every token of chosen
+    expert groups, so that whole row chunks of both chunk lists (and of the
+    shared expert) are compared row by row at the real contraction lengths."""
+    rand = sample_tokens(s.T, {SWITCH: 96, MIXTRAL: 32, DS_PREFILL: 16}[name], seed=s.cfg_id)
+
+    def pick(r):
+        load = np.diff(r["offsets"])
+        parts = [rand]
+        if name == DS_PREFILL:
+            # a group of <= 256 rows is one chunk of the 256-row list; one of
+            # 257..320 rows is one chunk of the 320-row list
+            small = np.nonzero((load > 0) & (load <= 256))[0]
+            big = np.nonzero((load > 256) & (load <= 320))[0]
+            assert len(small) and (len(big) or s.n_group)
+            parts.append(expert_tokens(r, int(small[np.argmax(load[small])])))
+            if len(big):
+                parts.append(expert_tokens(r, int(big[np.argmax(load[big])])))
+            parts.append(np.arange(320))   # the shared expert's first chunk (its rows are token order)
+        elif name == MIXTRAL:
+            # groups of ~1000 rows: the first 320 rows of the most and the least
+            # loaded expert hold each one's first chunk whichever list it took
+            for e in (int(np.argmax(load)), int(np.argmin(load))):
+                parts.append(expert_tokens(r, e)[:320])
+        elif name == SWITCH:
+            # the hot expert at capacity and the least-loaded expert that kept any row
+            nz = np.nonzero(load > 0)[0]
+            parts += [expert_tokens(r, int(np.argmax(load))), expert_tokens(r, int(nz[np.argmin(load[nz])]))]
+        return np.concatenate(parts)
+    return pick
+
+
+@pytest.mark.parametrize("name", [TINY, SWITCH, MIXTRAL, DS_PREFILL, DS_DECODE])
+def test_forward_workload(name):
     s, inp, dev = _inputs(name)
-    res = full_parity(s, inp, dev=dev, n_sample=n_sample)
+    pick = _whole_groups(name, s) if name in (SWITCH, MIXTRAL, DS_PREFILL) else None
+    res = full_parity(s, inp, dev=dev, tokens=pick)
+    print(f"{s.name}: compared {len(res['tokens'])} tokens")
     print(f"{s.name}: ties={res['ties']} worst_row_rel_err={res['worst']:.3e}")
     if name == SWITCH:
         ros = bits(res["route"]["row_of_slot"])
@@ -302,3 +341,34 @@ def test_forward_workload(name, n_sample):
         print(f"decode: {touched} distinct experts touched (uniform model: "
               f"{ref.expected_touched_experts(256, 8, 16):.1f})")
         assert 80 <= touched <= 128
+
+
+# --------------------------------------- the NEXT rows at DeepSeek-V3 width
+
+def test_noaux_layer_full_width():
+    """DeepSeek-V3 selection (8 groups, 4 kept, selection-only bias) through the
+    whole prefill layer at its real width (I = 2048, shared expert): whole expert
+    groups of both chunk lists and the shared expert's first chunk, row by row."""
+    s, inp, dev = _inputs(NOAUX["prefill"])
+    assert inp.score_bias is not None and s.I == 2048
+    res = full_parity(s, inp, dev=dev, tokens=_whole_groups(DS_PREFILL, s))
+    print(f"{s.name}: compared {len(res['tokens'])} tokens, ties={res['ties']} worst_row_rel_err={res['worst']:.3e}")
+
+
+def test_expert_choice_layer_full_width():
+    """Expert-choice routing (C = T k / E = 256) through the DeepSeek-V3 prefill
+    layer at its real width: random tokens plus every token of two experts'
+    groups (whole 256-row chunks) and the shared expert's first chunk."""
+    s, inp, dev = _inputs(DS_PREFILL)
+
+    def pick(chosen):
+        return np.concatenate([sample_tokens(s.T, 16, seed=7), chosen[0], chosen[s.E - 1], np.arange(320)])
+    res = ec_parity(s, inp, dev, pick)
+    assert res["C"] == 256
+
+
+def test_noaux_decode_full_width():
+    """The DeepSeek-V3 decode batch (16 tokens, streaming path) with groups and the selection bias."""
+    s, inp, dev = _inputs(NOAUX["decode"])
+    res = full_parity(s, inp, dev=dev)
+    print(f"{s.name}: ties={res['ties']} worst_row_rel_err={res['worst']:.3e}")
