@@ -54,7 +54,8 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = 3, /* a valid option the library does not implement */
   MOE_ERR_WORKSPACE = 4,   /* workspace missing or smaller than moe_workspace_size() */
   MOE_ERR_HIP = 5,         /* a HIP launch or runtime call failed */
-  MOE_ERR_ALIGN = 6        /* a device pointer is not 16-byte aligned */
+  MOE_ERR_ALIGN = 6,       /* a device pointer is not 16-byte aligned */
+  MOE_ERR_SCRATCH = 7      /* moe_forward_noalloc: the layer's workspace exceeds the static scratch */
 } moe_status;
 
 /* Gate of [MoE-10] "路由器怎样选专家：top-k 与两种门控": softmax over all experts
@@ -218,6 +219,22 @@ moe_status moe_combine(const moe_config *cfg, const void *y_perm, const int32_t 
  * kept in the workspace instead (scores: not computed). */
 moe_status moe_forward(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
                        moe_route_out *route_out, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments as moe_forward minus the workspace: the library keeps a static
+ * device scratch of MOE_STATIC_SCRATCH_BYTES (64 MiB) on every GPU it runs on,
+ * held until the process ends, and this call neither allocates nor frees.
+ * Returns MOE_ERR_SCRATCH, with nothing launched, when moe_workspace_size(cfg)
+ * exceeds it (e.g. the DeepSeek-V3 decode layer, 16 tokens, needs about 3 MB;
+ * prefill batches of a few hundred tokens fit).  Every call on one GPU shares
+ * that GPU's scratch: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.  Returns MOE_ERR_HIP if
+ * the scratch address cannot be obtained on the current device. */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+size_t moe_static_scratch_bytes(void);
+moe_status moe_forward_noalloc(const moe_config *cfg, const moe_weights *w, const void *x, void *y,
+                               moe_route_out *route_out, void *stream);
 
 /* moe_forward that also records `events` (an array of MOE_STAGE_EVENTS hipEvent_t
  * created by the caller, or NULL) on `stream` around its stages, for timing:

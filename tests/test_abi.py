@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         assert moe.status_str(code) != "unknown status"
     assert moe.status_str(99) == "unknown status"
 
@@ -123,6 +123,14 @@ def test_launch_entry_points_reject_before_launch():
     assert L.moe_dispatch(p(good), 16, 16, 16, 16, 16, 16, None, None, 0, None) == 4   # no workspace
     assert L.moe_expert_ffn(p(good), 16, 16, 16, 16, 16, 16, 16, 8, None) == 4       # workspace too small
     assert L.moe_forward(p(good), None, 16, 16, None, 16, 1 << 30, None) == 1       # no weights
+    # the no-allocation entry point: invalid shapes, and layers whose workspace
+    # exceeds the static scratch, are refused before any HIP call
+    assert L.moe_forward_noalloc(p(bad), None, 16, 16, None, None) == 2
+    ds = moe.make_config(8192, 7168, 2048, 256, 8, moe.GATE_SIGMOID, True, 2.5, 0.0, 1, 2048, moe.BF16)
+    assert moe.workspace_size(ds) > moe.static_scratch_bytes() == 64 << 20
+    assert L.moe_forward_noalloc(p(ds), None, 16, 16, None, None) == 7
+    dec = moe.make_config(16, 7168, 2048, 256, 8, moe.GATE_SIGMOID, True, 2.5, 0.0, 1, 2048, moe.BF16)
+    assert moe.workspace_size(dec) <= moe.static_scratch_bytes()
 
 
 def test_expert_choice_host_calls():

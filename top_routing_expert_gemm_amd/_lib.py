@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
-                4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP", 6: "MOE_ERR_ALIGN"}
+                4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP", 6: "MOE_ERR_ALIGN", 7: "MOE_ERR_SCRATCH"}
 GATE_SOFTMAX, GATE_SIGMOID = 0, 1
 F32, BF16 = 0, 1
 STAGE_EVENTS = 6
@@ -23,7 +23,8 @@ STAGE_EVENTS = 6
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_str", "moe_validate", "moe_workspace_size", "moe_capacity", "moe_layer_params",
            "moe_route", "moe_route_sel", "moe_balance_stats", "moe_bias_update", "moe_dispatch",
-           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_timed", "moe_ec_capacity",
+           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_timed", "moe_static_scratch_bytes",
+           "moe_forward_noalloc", "moe_ec_capacity",
            "moe_ec_workspace_size", "moe_route_ec", "moe_forward_ec", "moe_quantize_fp8", "moe_forward_fp8", "moe_mfma_peak",
            "moe_hbm_read_peak")
 
@@ -107,6 +108,11 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_timed.restype = c_int32
         L.moe_forward_timed.argtypes = [P, POINTER(MoeWeights), c_void_p, c_void_p, POINTER(MoeRouteOut),
                                         c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]
+        L.moe_static_scratch_bytes.restype = c_size_t
+        L.moe_static_scratch_bytes.argtypes = []
+        L.moe_forward_noalloc.restype = c_int32
+        L.moe_forward_noalloc.argtypes = [P, POINTER(MoeWeights), c_void_p, c_void_p, POINTER(MoeRouteOut),
+                                          c_void_p]
         L.moe_ec_capacity.restype = c_int64
         L.moe_ec_capacity.argtypes = [P]
         L.moe_ec_workspace_size.restype = c_int32
@@ -258,6 +264,20 @@ def forward(cfg, weights, x, y, ws, route_out=None, stream=None, events=None):
     st = lib().moe_forward_timed(ctypes.byref(cfg), ctypes.byref(W), _ptr(x), _ptr(y), rp, _ptr(ws), nbytes,
                                  _stream(stream), arr)
     _check(st, "moe_forward_timed")
+
+
+def static_scratch_bytes() -> int:
+    """Bytes of the static device scratch behind moe_forward_noalloc."""
+    return int(lib().moe_static_scratch_bytes())
+
+
+def forward_noalloc(cfg, weights, x, y, route_out=None, stream=None):
+    """moe_forward_noalloc: moe_forward on the library's static device scratch (no workspace argument)."""
+    W = weights if isinstance(weights, MoeWeights) else weights_struct(weights)
+    R = route_out if isinstance(route_out, MoeRouteOut) or route_out is None else route_out_struct(route_out)
+    rp = ctypes.byref(R) if R is not None else None
+    _check(lib().moe_forward_noalloc(ctypes.byref(cfg), ctypes.byref(W), _ptr(x), _ptr(y), rp, _stream(stream)),
+           "moe_forward_noalloc")
 
 
 # ---- expert choice ----

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 
 using namespace moe;
@@ -155,6 +157,7 @@ const char* moe_status_str(moe_status s) {
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch or runtime error";
     case MOE_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case MOE_ERR_SCRATCH: return "layer needs more workspace than the static device scratch holds";
   }
   return "unknown status";
 }
@@ -455,6 +458,49 @@ moe_status moe_forward_timed(const moe_config* c, const moe_weights* w, const vo
 moe_status moe_forward(const moe_config* c, const moe_weights* w, const void* x, void* y, moe_route_out* ro,
                        void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(c, w, nullptr, x, y, ro, ws, ws_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+// ---- moe_forward without allocation: a static device scratch per GPU ----
+// The workspace lives in a file-scope device array.  On the host its name is
+// only a stand-in for the symbol: the device address of each GPU's copy comes
+// from hipGetSymbolAddress with that GPU current, taken once per device and
+// kept; kernels and copies get that address, never the array's name.
+namespace {
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch, or nullptr on failure.
+void* static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchSlot& sl = g_scratch[dev];
+  std::call_once(sl.once, [&sl] { sl.err = hipGetSymbolAddress(&sl.ptr, HIP_SYMBOL(scratch)); });
+  return sl.err == hipSuccess ? sl.ptr : nullptr;
+}
+}  // namespace
+
+extern "C" {
+
+size_t moe_static_scratch_bytes(void) { return MOE_STATIC_SCRATCH_BYTES; }
+
+moe_status moe_forward_noalloc(const moe_config* c, const moe_weights* w, const void* x, void* y,
+                               moe_route_out* ro, void* stream) {
+  MOE_TRY(moe_validate(c));
+  if (layout(c).total > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = static_scratch();
+  if (ws == nullptr) return MOE_ERR_HIP;
+  // every stage writes what a later one reads (no counter or flag starts from a
+  // cleared value), so the scratch is not cleared between calls
+  return forward_impl(c, w, nullptr, x, y, ro, ws, MOE_STATIC_SCRATCH_BYTES, stream, nullptr);
 }
 
 // ---- FP8 expert weights ----
