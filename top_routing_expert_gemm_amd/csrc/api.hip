@@ -15,6 +15,12 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 inline size_t esize(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
+int64_t cap_of(const moe_config* c) {
+  if (!(c->capacity_factor > 0.f)) return -1;
+  const double v = ceil((double)c->capacity_factor * (double)c->T * (double)c->k / (double)c->E);
+  return (int64_t)v;
+}
+
 // Device workspace of moe_forward; the stage entry points use the same layout.
 struct Layout {
   size_t topk_idx, topk_w, counts, offsets, row_of_slot, token_of_row, dscratch, rscratch, chunks, n_chunks, h,
@@ -28,7 +34,7 @@ Layout layout(const moe_config* c) {
   const int64_t Tk = c->T * c->k;
   const int64_t sh = c->n_shared ? c->T : 0;
   L.rows = Tk + sh;
-  L.plan = chunk_plan(*c, Tk, sh);
+  L.plan = chunk_plan(*c, Tk, sh, cap_of(c));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -41,7 +47,7 @@ Layout layout(const moe_config* c) {
   L.offsets = take((size_t)(c->E + 1) * 4);
   L.row_of_slot = take((size_t)Tk * 4);
   L.token_of_row = take((size_t)Tk * 4);
-  L.dscratch = take(dispatch_scratch_bytes(Tk, c->E));
+  L.dscratch = take(dispatch_scratch_bytes(c->T, c->k, c->E));
   L.rscratch = take(route_scratch_bytes(*c));
   L.chunks = take((size_t)(L.plan.max_a + L.plan.max_b) * sizeof(Chunk));
   L.n_chunks = take(8);
@@ -71,7 +77,7 @@ LayoutEC layout_ec(const moe_config* c) {
   const int64_t R = c->E * L.C;
   const int64_t sh = c->n_shared ? c->T : 0;
   L.rows = R + sh;
-  L.plan = chunk_plan(*c, R, sh);
+  L.plan = chunk_plan(*c, R, sh, L.C);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -121,11 +127,6 @@ moe_status check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
 moe_status need(const void* p) { return p == nullptr ? MOE_ERR_NULL : (aligned16(p) ? MOE_OK : MOE_ERR_ALIGN); }
 moe_status opt(const void* p) { return p == nullptr || aligned16(p) ? MOE_OK : MOE_ERR_ALIGN; }
 
-int64_t cap_of(const moe_config* c) {
-  if (!(c->capacity_factor > 0.f)) return -1;
-  const double v = ceil((double)c->capacity_factor * (double)c->T * (double)c->k / (double)c->E);
-  return (int64_t)v;
-}
 
 // One grouped-GEMM pass over the chunk lists of plan p: launch(g) with g on
 // list A, then on list B when the plan has one.
@@ -388,11 +389,18 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
   int32_t* nch = reinterpret_cast<int32_t*>(at(ws, L.n_chunks));
 
   HIP_TRY(mark(0));
-  HIP_TRY(launch_route_split(*c, x, w->w_router, w->router_bias, route_sel_of(*c, w->score_bias, r.scores),
-                             r.topk_idx, r.topk_w, at(ws, L.rscratch), s));
-  HIP_TRY(mark(1));
-  HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), r.topk_idx, r.counts, r.offsets, r.row_of_slot,
-                          r.token_of_row, at(ws, L.dscratch), chunks, nch, L.plan.cut, sh, Tk, s));
+  if (c->dtype == MOE_BF16) {
+    HIP_TRY(launch_route_dispatch(*c, x, w->w_router, w->router_bias, route_sel_of(*c, w->score_bias, r.scores),
+                                  r.topk_idx, r.topk_w, at(ws, L.rscratch), cap_of(c), r.counts, r.offsets,
+                                  r.row_of_slot, r.token_of_row, at(ws, L.dscratch), chunks, nch, L.plan.cut, sh, Tk,
+                                  s, [&] { return mark(1); }));
+  } else {
+    HIP_TRY(launch_route(*c, x, w->w_router, w->router_bias, route_sel_of(*c, w->score_bias, r.scores),
+                         r.topk_idx, r.topk_w, s));
+    HIP_TRY(mark(1));
+    HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), r.topk_idx, r.counts, r.offsets, r.row_of_slot,
+                            r.token_of_row, at(ws, L.dscratch), chunks, nch, L.plan.cut, sh, Tk, s));
+  }
   HIP_TRY(mark(2));
   GemmArgs g{};
   g.A = x;

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <functional>
 
 #include "moe.h"
 
@@ -65,12 +66,15 @@ int64_t max_chunks(int64_t rows_max, int64_t E, int64_t shared_rows, int bm);
 // 320-row tiles) when the register-staged kernels' limits hold (both
 // contractions at least 128 long, 32-bit buffer offsets covering x [T, H], the
 // row space [rows, H] and h [rows, I]), else the 320-row tile alone.
-// max_a / max_b: capacities of the two lists.
+// max_a / max_b: capacities of the two lists.  group_max (-1: unknown) bounds
+// the rows of one routed group: at most 256 rows, every group takes the
+// 256-row list (and so does the shared group, which never makes the other list
+// on its own), so the 320-row list is left out and its launches skipped.
 struct ChunkPlan {
   ChunkCut cut;
   int64_t max_a, max_b;
 };
-inline ChunkPlan chunk_plan(const moe_config& c, int64_t routed, int64_t shared) {
+inline ChunkPlan chunk_plan(const moe_config& c, int64_t routed, int64_t shared, int64_t group_max = -1) {
   ChunkPlan p{};
   const int64_t rows = routed + shared, lim = int64_t(1) << 32;
   int bm_a = kGemmBMdl, bm_b = 0;
@@ -81,7 +85,7 @@ inline ChunkPlan chunk_plan(const moe_config& c, int64_t routed, int64_t shared)
   } else if (MOE_GEMM_RS && c.H >= 128 && c.I >= 128 && std::max<int64_t>(c.T, rows) * c.H * 2 < lim &&
              rows * c.I * 2 < lim && c.H * c.I * 2 < lim) {
     bm_a = kGemmBMrs;
-    bm_b = kGemmBMdl;
+    bm_b = (group_max >= 0 && group_max <= kGemmBMrs) ? 0 : kGemmBMdl;
   }
   p.max_a = max_chunks(routed, c.E, shared, bm_a);
   p.max_b = bm_b ? max_chunks(routed, c.E, shared, bm_b) : 0;
@@ -114,9 +118,14 @@ inline RouteSel route_sel_of(const moe_config& c, const float* sbias, float* sco
 hipError_t launch_route(const moe_config& c, const void* x, const void* w, const float* bias, const RouteSel& rs,
                         int32_t* topk_idx, float* topk_w, hipStream_t s);
 
+// Router partial logits (bf16): part[s][t][0 .. 32 ceil(E/32)) float32 over
+// route_partial_slices(c) slices of H, in `part` (route_scratch_bytes).
+int route_partial_slices(const moe_config& c);
+size_t route_scratch_bytes(const moe_config& c);
+hipError_t launch_route_partials(const moe_config& c, const void* x, const void* w, float* part, hipStream_t s);
+
 // Split-K router (bf16): partial logits in `scratch` (route_scratch_bytes), then
 // a per-token reduce + gate + top-k.  fp32 configs fall back to launch_route.
-size_t route_scratch_bytes(const moe_config& c);
 hipError_t launch_route_split(const moe_config& c, const void* x, const void* w, const float* bias,
                               const RouteSel& rs, int32_t* topk_idx, float* topk_w, void* scratch, hipStream_t s);
 
@@ -129,8 +138,23 @@ hipError_t launch_balance_stats(const moe_config& c, const int32_t* counts, cons
 hipError_t launch_bias_update(const moe_config& c, const int32_t* counts, float gamma, float* score_bias,
                               hipStream_t s);
 
-// Dispatch scratch sizes (bytes) for T*k assignments and E experts.
-size_t dispatch_scratch_bytes(int64_t Tk, int64_t E);
+// Dispatch scratch sizes (bytes) for T tokens, k slots and E experts.
+size_t dispatch_scratch_bytes(int64_t T, int64_t k, int64_t E);
+
+// The layer's routing and dispatch (bf16): router partials, the select step
+// (sum of the partials, gate, top-k) with the dispatch's block step, then the
+// expert scan and the row maps and chunk lists; `routed` runs after the select
+// step (the stage boundary between routing and dispatch).  Batches of <= 16
+// tokens do the select step and the whole dispatch in one launch
+// (route_dispatch_fused).  rscratch: route_scratch_bytes; dscratch:
+// dispatch_scratch_bytes.
+bool route_dispatch_fused(const moe_config& c);
+hipError_t launch_route_dispatch(const moe_config& c, const void* x, const void* w, const float* bias,
+                                 const RouteSel& rs, int32_t* topk_idx, float* topk_w, void* rscratch, int64_t cap,
+                                 int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* token_of_row,
+                                 void* dscratch, Chunk* chunks, int32_t* n_chunks, const ChunkCut& cut,
+                                 int64_t shared_rows, int64_t shared_row0, hipStream_t s,
+                                 const std::function<hipError_t()>& routed);
 
 // Histogram + scan + capacity + row maps; also writes the chunk lists of the
 // routed groups (and the shared group when shared_rows > 0, starting at

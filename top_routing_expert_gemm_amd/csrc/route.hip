@@ -16,6 +16,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
@@ -24,212 +25,14 @@ constexpr int kRBM = 32;   // tokens per workgroup
 constexpr int kRBK = 64;   // K step
 constexpr int kRThreads = 256;
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
-}
-// Larger value wins; equal values -> lower expert index.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    float v2 = __shfl_xor(v, off, kWave);
-    int i2 = __shfl_xor(i, off, kWave);
-    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
-  }
-}
-
-// Options of the DeepSeek-V3 selection: selection-only bias and group limit.
-struct SelOpts {
-  const float* sbias;  // [E] or NULL
-  int n_group;         // 0: no groups
-  int topk_group;
-  float* wbuf;         // this wave's LDS scratch of E floats (used when n_group > 0)
-};
-
-// Gate score of every expert of one token (one wave), the same arithmetic as
-// the selection below: softmax over the E logits, or a sigmoid per logit.
-template <int VPL>
-__device__ void write_scores(const float (&z)[VPL], int E, int gate, float* out) {
-  const int lane = threadIdx.x & (kWave - 1);
-  float m = -INFINITY, den = 0.f;
-  if (gate == MOE_GATE_SOFTMAX) {
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if (lane + kWave * v < E) m = fmaxf(m, z[v]);
-    m = wave_max(m);
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if (lane + kWave * v < E) den += expf(z[v] - m);
-    den = wave_sum(den);
-  }
-#pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    const int e = lane + kWave * v;
-    if (e < E) out[e] = gate == MOE_GATE_SOFTMAX ? expf(z[v] - m) / den : 1.f / (1.f + expf(-z[v]));
-  }
-}
-
-// Gate + top-k of one token, run by one whole wave.  z[v] holds the logit of
-// expert lane + 64 v (-inf past E).
-//  * Plain selection: both gates are increasing functions of z, so the k best
-//    scores are the k largest logits; selection is done on z, which keeps full
-//    fp32 resolution.
-//  * With a selection bias or groups ([MoE-10] "DeepSeek-V3 的无辅助损失偏置"):
-//    experts are ranked by gate score + bias, groups by the sum of their two
-//    best ranking scores, only the topk_group best groups stay eligible, and
-//    the weights are the unbiased scores of the picks.
-// Ties go to the lower expert (or group) index.  Lanes j < k write pick j.
-template <int VPL>
-__device__ void topk_token(float (&z)[VPL], int E, int k, int gate, int renorm, float scale, const SelOpts& o,
-                           float* out_scores, int32_t* out_idx, float* out_w) {
-  const int lane = threadIdx.x & (kWave - 1);
-  if (out_scores != nullptr) write_scores<VPL>(z, E, gate, out_scores);
-  const bool plain = o.sbias == nullptr && o.n_group == 0;
-  bool taken[VPL];
-#pragma unroll
-  for (int v = 0; v < VPL; ++v) taken[v] = false;
-  float selz = -INFINITY, selsc = 0.f;
-  int seli = 0;
-
-  if (plain) {
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const int e = lane + kWave * v;
-        if (e < E && !taken[v] && (z[v] > bv || bi == 0x7fffffff)) { bv = z[v]; bi = e; }
-      }
-      wave_argmax(bv, bi);
-#pragma unroll
-      for (int v = 0; v < VPL; ++v)
-        if (lane + kWave * v == bi) taken[v] = true;
-      if (lane == j) { selz = bv; seli = bi; }
-    }
-    const bool mine = lane < k;
-    float w;
-    if (gate == MOE_GATE_SOFTMAX) {
-      if (renorm) {
-        // p_j / sum_sel p = exp(z_j - z_best) / sum_sel exp(z - z_best)
-        const float zbest = __shfl(selz, 0, kWave);
-        const float ex = mine ? expf(selz - zbest) : 0.f;
-        w = ex / wave_sum(ex);
-      } else {
-        // full softmax over all E experts
-        float m = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-          if (lane + kWave * v < E) m = fmaxf(m, z[v]);
-        m = wave_max(m);
-        float s = 0.f;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-          if (lane + kWave * v < E) s += expf(z[v] - m);
-        s = wave_sum(s);
-        w = mine ? expf(selz - m) / s : 0.f;
-      }
-    } else {
-      const float sg = mine ? 1.f / (1.f + expf(-selz)) : 0.f;
-      w = renorm ? sg / wave_sum(sg) : sg;
-    }
-    if (mine) {
-      out_idx[lane] = seli;
-      out_w[lane] = w * scale;
-    }
-    return;
-  }
-
-  // ---- DeepSeek-V3 selection ----
-  float m = -INFINITY, den = 0.f;
-  if (gate == MOE_GATE_SOFTMAX) {
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if (lane + kWave * v < E) m = fmaxf(m, z[v]);
-    m = wave_max(m);
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if (lane + kWave * v < E) den += expf(z[v] - m);
-    den = wave_sum(den);
-  }
-  float sc[VPL], sel[VPL];
-#pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    const int e = lane + kWave * v;
-    if (e < E) {
-      sc[v] = gate == MOE_GATE_SOFTMAX ? expf(z[v] - m) / den : 1.f / (1.f + expf(-z[v]));
-      sel[v] = o.sbias != nullptr ? sc[v] + o.sbias[e] : sc[v];
-    } else {
-      sc[v] = 0.f;
-      sel[v] = -INFINITY;
-    }
-  }
-  if (o.n_group > 0) {
-    const int G = E / o.n_group;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int e = lane + kWave * v;
-      if (e < E) o.wbuf[e] = sel[v];
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's scratch writes are done
-    __builtin_amdgcn_wave_barrier();
-    float gs = -INFINITY;
-    if (lane < o.n_group) {  // group score: sum of its two best ranking scores
-      float b1 = -INFINITY, b2 = -INFINITY;
-      for (int i = 0; i < G; ++i) {
-        const float v = o.wbuf[lane * G + i];
-        if (v > b1) { b2 = b1; b1 = v; }
-        else if (v > b2) b2 = v;
-      }
-      gs = G >= 2 ? b1 + b2 : b1;
-    }
-    uint64_t kept = 0;
-    for (int q = 0; q < o.topk_group; ++q) {
-      const bool cand = lane < o.n_group && !((kept >> lane) & 1);
-      float bv = cand ? gs : -INFINITY;
-      int bi = cand ? lane : 0x7fffffff;
-      wave_argmax(bv, bi);
-      if (bi < 64) kept |= 1ull << bi;  // always a group id when topk_group <= n_group
-    }
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int e = lane + kWave * v;
-      if (e < E && !((kept >> (e / G)) & 1)) sel[v] = -INFINITY;
-    }
-    __builtin_amdgcn_wave_barrier();  // scratch reads done before a later token's writes
-  }
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY, cs = 0.f;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int e = lane + kWave * v;
-      if (e < E && !taken[v] && (sel[v] > bv || bi == 0x7fffffff)) { bv = sel[v]; bi = e; cs = sc[v]; }
-    }
-    wave_argmax(bv, bi);
-    const float wsc = __shfl(cs, bi & (kWave - 1), kWave);  // the owner's local best is the winner
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if (lane + kWave * v == bi) taken[v] = true;
-    if (lane == j) { selsc = wsc; seli = bi; }
-  }
-  const bool mine = lane < k;
-  const float w0 = mine ? selsc : 0.f;
-  const float w = renorm ? w0 / wave_sum(w0) : w0;
-  if (mine) {
-    out_idx[lane] = seli;
-    out_w[lane] = w * scale;
-  }
-}
-
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
+
+// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row: the 16 lanes
+// of one ds_read_b128 cycle (rows r .. r + 15, one logical chunk) land on
+// distinct banks of the 64-bank LDS (rows r and r + 8 differ in the low bit).
+__device__ __forceinline__ int rswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // Router GEMM core shared by the fused and the split-K kernels: RBT blocks of
 // 32 tokens (rows t0 ..) x all E experts, contraction over x columns
@@ -252,7 +55,7 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x, cons
   for (int i = 0; i < RBT; ++i) {
     const int r = ar + 32 * i;
     aptr[i] = x + (int64_t)min(t0 + r, T - 1) * H + ac * 8;
-    a_lds[i] = r * kRBK + ((ac ^ (r & 7)) * 8);
+    a_lds[i] = r * kRBK + ((ac ^ rswz(r)) * 8);
   }
   // B operand rows of this wave's blocks: lane -> expert (lane & 31), k half (lane >> 5)
   const uint16_t* bptr[NBW];
@@ -305,7 +108,7 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x, cons
       for (int r = 0; r < RBT; ++r) {
         const int row = r * 32 + arow;
         const bf16x8 av = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(Ab + row * kRBK + ((chunk ^ (row & 7)) * 8)));
+            bf16x8, *reinterpret_cast<const uint4*>(Ab + row * kRBK + ((chunk ^ rswz(row)) * 8)));
 #pragma unroll
         for (int i = 0; i < NBW; ++i)
           if (bval[i])
@@ -413,74 +216,6 @@ __global__ __launch_bounds__(kRThreads) __attribute__((amdgpu_waves_per_eu(RBT =
     }
 }
 
-// Split-K router, part 2: one wave per token sums the partial logits in slice
-// order (fixed, so the result is reproducible), adds the bias and runs the gate
-// and top-k.
-template <int VPL>
-__global__ __launch_bounds__(kRThreads) void route_topk_kernel(const float* __restrict__ part, int nsplit, int T,
-                                                               int E, const float* __restrict__ bias, int k,
-                                                               int gate, int renorm, float scale,
-                                                               RouteSel rs, int32_t* __restrict__ topk_idx,
-                                                               float* __restrict__ topk_w) {
-  constexpr int TPB = kRThreads / kWave;  // tokens per workgroup, one wave each for the top-k
-  // dynamic LDS sized by E (topk_lds_bytes): the summed logits of the TPB tokens, then each wave's group
-  // scratch, E floats each, so a small E leaves room for more workgroups per CU
-  extern __shared__ __attribute__((aligned(16))) float tk_lds[];
-  float* zs = tk_lds;                 // [TPB][E]
-  float* wscr = tk_lds + TPB * E;     // [TPB][E]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * TPB;
-  const int Epad = (E + 31) / 32 * 32;
-  const int64_t stride = (int64_t)T * Epad;
-  // The whole workgroup sums the slice partials of its TPB tokens: thread -> expert,
-  // all tokens at once, eight slices per round, added strictly in slice order.
-  for (int e = threadIdx.x; e < E; e += kRThreads) {
-    float s[TPB];
-#pragma unroll
-    for (int j = 0; j < TPB; ++j) s[j] = 0.f;
-    const float* pp = part + (int64_t)t0 * Epad + e;
-    int ks = 0;
-    for (; ks + 8 <= nsplit; ks += 8) {
-      float q[8][TPB];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int j = 0; j < TPB; ++j) q[u][j] = t0 + j < T ? pp[(ks + u) * stride + (int64_t)j * Epad] : 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int j = 0; j < TPB; ++j) s[j] += q[u][j];
-    }
-    if (ks < nsplit) {  // the last < 8 slices: loads issued together, then added in slice order
-      float q[8][TPB];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int j = 0; j < TPB; ++j)
-          q[u][j] = (ks + u < nsplit && t0 + j < T) ? pp[(ks + u) * stride + (int64_t)j * Epad] : 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (ks + u < nsplit)
-#pragma unroll
-          for (int j = 0; j < TPB; ++j) s[j] += q[u][j];
-    }
-#pragma unroll
-    for (int j = 0; j < TPB; ++j) zs[j * E + e] = s[j];
-  }
-  __syncthreads();
-  const int t = t0 + wave;
-  if (t >= T) return;
-  float z[VPL];
-#pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    const int e = lane + kWave * v;
-    z[v] = e < E ? (bias != nullptr ? zs[wave * E + e] + bias[e] : zs[wave * E + e]) : -INFINITY;
-  }
-  const SelOpts o{rs.sbias, rs.n_group, rs.topk_group, wscr + wave * E};
-  topk_token<VPL>(z, E, k, gate, renorm, scale, o, rs.scores ? rs.scores + (int64_t)t * E : nullptr,
-                  topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
-}
-
 // fp32 path: one wave per token computes its E logits with lane-strided dot
 // products and a fixed-order wave reduction, then runs the same gate / top-k.
 template <int VPL>
@@ -544,74 +279,307 @@ hipError_t launch_route_f32(const moe_config& c, const void* x, const void* w, c
   return hipGetLastError();
 }
 
-// Token blocks per workgroup: 128 tokens for the largest batches with E <= 256
-// and 64 for large ones (fewer passes over the router weights per token), 32
-// otherwise and for E > 512 (register budget).
-// Split factor of the K dimension: enough workgroups to cover the chip twice
-// (two 128-token workgroups fit per CU), each slice at least four K steps long.
-inline int route_rbt(int64_t T, int64_t E) {
-  if (T >= 8192 && E <= 256) return 4;
-  return T >= 4096 && E <= 512 ? 2 : 1;
+// ------------------------------------------------------------------------
+// Router partial logits of the layer path: part[s][t][0 .. Epad) = the logits of
+// token t over the s-th slice of H (Epad = 32 ceil(E / 32); columns past E are
+// not used).  The select step (dispatch.hip) adds the slices in slice order, so
+// the sums are reproducible.
+
+// Large batches, E <= 256: one workgroup = 256 tokens x all experts over one
+// slice of H.  Four waves, one per SIMD; wave w computes tokens 64 w .. + 64 (two
+// 32-row blocks) against every 32-expert block (NB of them), so the whole tile's
+// 256 x 32 NB accumulators live in the workgroup's registers.  Both operand
+// tiles go through LDS (double buffered, 128-byte rows, 16-byte chunks
+// XOR-swizzled by row): every thread fetches the next K step's 16-byte pieces
+// into registers while the current step is multiplied, then stores them; one
+// barrier per step.  Per step the workgroup moves 32 KB of token rows and
+// 4 NB KB of router weights for 256 x 32 NB x 64 multiply-adds: a 256-token
+// tile reads the router weights once per 256 tokens, twice fewer times than
+// 128-token tiles.
+constexpr int kGT = 256;     // tokens per workgroup
+constexpr int kGThreads = 256;
+
+template <int NB>
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void route_gemm_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T, int H, int E, int steps_per_split,
+    float* __restrict__ part) {
+  constexpr int EB = NB * 32;              // experts of the tile
+  constexpr int NA = kGT * 8 / kGThreads;  // 16-byte A pieces per thread per step (8)
+  constexpr int NBL = EB * 8 / kGThreads;  // B pieces per thread per step (NB)
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kGT * kRBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][EB * kRBK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * kGT;
+  const int ks = blockIdx.y;
+  const int nk = H / kRBK;
+  const int kb = ks * steps_per_split, ke = min(kb + steps_per_split, nk);
+  const int Epad = (E + 31) / 32 * 32;
+
+  // loader: thread -> row tid / 8 + 32 i, 16-byte chunk tid % 8 (stored at its swizzled slot)
+  const int lr = tid >> 3, lc = tid & 7;
+  const uint16_t* ap[NA];
+  const uint16_t* bp[NBL];
+  int aslot[NA], bslot[NBL];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int r = lr + 32 * i;
+    ap[i] = x + (int64_t)min(t0 + r, T - 1) * H + lc * 8;
+    aslot[i] = r * kRBK + ((lc ^ rswz(r)) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) {
+    const int r = lr + 32 * i;
+    bp[i] = w + (int64_t)min(r, E - 1) * H + lc * 8;
+    bslot[i] = r * kRBK + ((lc ^ rswz(r)) * 8);
+  }
+
+  f32x16 acc[2][NB];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][n][v] = 0.f;
+
+  // two register sets: set P holds K step kt + 2 (issued during step kt), set
+  // 1 - P step kt + 1 (issued during the previous step), stored to LDS at the
+  // end of step kt; refills past the slice are clamped to its last step (loaded,
+  // never used), so every step issues the same loads and the wait before each
+  // store is an exact count
+  uint4 ra[2][NA], rbv[2][NBL];
+  auto load = [&](int set, int kt) {
+    const int kc = min(kt, ke - 1) * kRBK;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) ra[set][i] = ldg16(ap[i] + kc);
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) rbv[set][i] = ldg16(bp[i] + kc);
+  };
+  auto store = [&](int set, int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) *reinterpret_cast<uint4*>(&sA[buf][aslot[i]]) = ra[set][i];
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) *reinterpret_cast<uint4*>(&sB[buf][bslot[i]]) = rbv[set][i];
+  };
+  const int l32 = lane & 31, h = lane >> 5;
+  auto compute = [&](int buf) {
+    const uint16_t* A = sA[buf];
+    const uint16_t* B = sB[buf];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      // substep s2, lane half h: k = 32 h + 8 s2 .. + 8 of the step, for A and B alike
+      const int c = h * 4 + s2;
+      bf16x8 av[2], bv[NB];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wave * 64 + j * 32 + l32;
+        av[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(A + r * kRBK + ((c ^ rswz(r)) * 8)));
+      }
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const int r = n * 32 + l32;
+        bv[n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(B + r * kRBK + ((c ^ rswz(r)) * 8)));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[j][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], bv[n], acc[j][n], 0, 0, 0);
+    }
+  };
+  load(0, kb);
+  load(1, kb + 1);
+  store(0, 0);
+  __syncthreads();
+  int kt = kb;
+  for (; kt + 1 < ke; kt += 2) {  // the fences keep each refill issued before the step's MFMAs
+    load(0, kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    store(1, 1);
+    __syncthreads();
+    load(1, kt + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    store(0, 0);
+    __syncthreads();
+  }
+  if (kt < ke) compute(0);
+
+  // lane holds expert column l32 of each block and token rows 8 g + 4 h + q
+  float* out = part + (int64_t)ks * T * Epad;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int e = n * 32 + l32;
+      if (e >= Epad) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = t0 + wave * 64 + j * 32 + 8 * g + 4 * h + q;
+          if (t < T) out[(int64_t)t * Epad + e] = acc[j][n][4 * g + q];
+        }
+    }
 }
-inline int route_nsplit(int64_t T, int64_t H, int64_t E) {
-  const int rbt = route_rbt(T, E);
-  const int64_t rows = rbt * kRBM;
+
+// Small batches (T <= 16): every workgroup owns 16 experts and one slice of H;
+// its 16 waves split the slice's 64-wide K blocks between them (block i to wave
+// i mod 16), stream the weight rows straight into registers (every block of a
+// wave in flight at once) and multiply them with v_mfma_f32_16x16x32_bf16
+// against the token rows (padded to 16 by repeating the last).  The waves'
+// 16 x 16 partial logits are then added in LDS in wave order and written once
+// per workgroup, so the select step reads only nsplit x T x E partials.
+constexpr int kVWaves = 16;
+constexpr int kVMaxBlk = 4;    // 64-wide K blocks per wave, at most
+
+__global__ __launch_bounds__(kVWaves * 64) void route_gemv_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ w, int T, int H,
+                                                                 int E, int nsplit, float* __restrict__ part) {
+  __shared__ float red[kVWaves][16 * 16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = blockIdx.x, ks = blockIdx.y;
+  const int nk = H / kRBK;
+  const int kb = (int)((int64_t)ks * nk / nsplit), ke = (int)((int64_t)(ks + 1) * nk / nsplit);
+  const int Epad = (E + 31) / 32 * 32;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  // lane group g4 supplies k = 16 g4 .. + 16 of every 64-wide block, for A and B alike
+  const uint16_t* pa = x + (int64_t)min(r16, T - 1) * H + g4 * 16;
+  const uint16_t* pb = w + (int64_t)min(grp * 16 + r16, E - 1) * H + g4 * 16;
+  uint4 a[kVMaxBlk][2], b[kVMaxBlk][2];
+  int nb = 0;
+#pragma unroll
+  for (int i = 0; i < kVMaxBlk; ++i) {
+    const int blk = kb + wave + kVWaves * i;
+    if (blk < ke) {
+      nb = i + 1;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        a[i][u] = ldg16(pa + blk * kRBK + 8 * u);
+        b[i][u] = ldg16(pb + blk * kRBK + 8 * u);
+      }
+    }
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kVMaxBlk; ++i)
+    if (i < nb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i][u]),
+                                                      __builtin_bit_cast(bf16x8, b[i][u]), acc, 0, 0, 0);
+  // lane holds expert column r16, token rows 4 g4 + q
+#pragma unroll
+  for (int q = 0; q < 4; ++q) red[wave][(4 * g4 + q) * 16 + r16] = acc[q];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int t = threadIdx.x >> 4, el = threadIdx.x & 15, e = grp * 16 + el;
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < kVWaves; ++v) s += red[v][threadIdx.x];
+    if (t < T && e < E) part[((int64_t)ks * T + t) * Epad + e] = s;
+  }
+}
+
+// Layers with E > 256 keep the 32-token-block tiles of the fused router: token
+// blocks per workgroup 64 for large batches with E <= 512, 32 otherwise
+// (register budget); K split so that the workgroups cover the chip twice, each
+// slice at least four K steps long.
+inline int route_rbt(int64_t T, int64_t E) { return T >= 4096 && E <= 512 ? 2 : 1; }
+inline int route_nsplit_wide(int64_t T, int64_t H, int64_t E) {
+  const int64_t rows = route_rbt(T, E) * kRBM;
   const int64_t mt = (T + rows - 1) / rows;
   const int64_t nk = H / kRBK;
-  const int64_t target = 512;
-  int64_t ns = (target + mt - 1) / mt;
+  int64_t ns = (512 + mt - 1) / mt;
   ns = std::min<int64_t>(ns, std::max<int64_t>(1, nk / 4));
   return (int)std::max<int64_t>(1, ns);
 }
 
-template <int NBW, int RBT>
-hipError_t launch_route_split_t(const moe_config& c, const void* x, const void* w, const float* bias,
-                                const RouteSel& rs, int32_t* idx, float* tw, float* part, hipStream_t s) {
-  const int nsplit = route_nsplit(c.T, c.H, c.E);
+enum RouteKind { RK_GEMV = 0, RK_GEMM = 1, RK_WIDE = 2 };
+struct RoutePlan {
+  int kind;
+  int nsplit;     // slices of H that hold partial logits
+  int per;        // K steps per slice (RK_GEMM, RK_WIDE)
+};
+
+RoutePlan route_plan(const moe_config& c) {
+  RoutePlan p{};
   const int nk = (int)(c.H / kRBK);
-  const int per = (nk + nsplit - 1) / nsplit;
-  const int nsplit_eff = (nk + per - 1) / per;
-  dim3 grid((unsigned)((c.T + RBT * kRBM - 1) / (RBT * kRBM)), (unsigned)nsplit_eff);
-  hipLaunchKernelGGL((route_partial_bf16_kernel<NBW, RBT>), grid, dim3(kRThreads), 0, s,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), (int)c.T, (int)c.H,
-                     (int)c.E, per, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int tpb = kRThreads / kWave;
-  const size_t lds = (size_t)2 * tpb * c.E * sizeof(float);
-  hipLaunchKernelGGL(route_topk_kernel<2 * NBW>, dim3((unsigned)((c.T + tpb - 1) / tpb)), dim3(kRThreads), lds, s,
-                     part, nsplit_eff, (int)c.T, (int)c.E, bias, (int)c.k, c.gate, c.renormalize,
-                     c.routed_scaling_factor, rs, idx, tw);
+  if (c.T <= kGemvMaxT) {
+    // about 64 workgroups in all, each slice at least one block per wave of half the waves
+    p.kind = RK_GEMV;
+    const int ngrp = (int)((c.E + 15) / 16);
+    int ns = std::max(1, 64 / ngrp);
+    ns = std::min(ns, std::max(1, nk / (kVWaves / 2)));
+    ns = std::max(ns, (nk + kVWaves * kVMaxBlk - 1) / (kVWaves * kVMaxBlk));  // at most kVMaxBlk blocks per wave
+    p.nsplit = ns;
+    p.per = 0;
+    return p;
+  }
+  if (c.E <= 256) {
+    // one 256-token workgroup per CU in all, each slice at least four K steps long
+    p.kind = RK_GEMM;
+    const int64_t mt = (c.T + kGT - 1) / kGT;
+    int64_t ns = (256 + mt - 1) / mt;
+    ns = std::min<int64_t>(ns, std::max(1, nk / 4));
+    p.per = (int)((nk + ns - 1) / ns);
+    p.nsplit = (nk + p.per - 1) / p.per;
+    return p;
+  }
+  p.kind = RK_WIDE;
+  const int ns = route_nsplit_wide(c.T, c.H, c.E);
+  p.per = (nk + ns - 1) / ns;
+  p.nsplit = (nk + p.per - 1) / p.per;
+  return p;
+}
+
+template <int NB>
+hipError_t launch_route_gemm(const moe_config& c, const void* x, const void* w, int per, int nsplit, float* part,
+                             hipStream_t s) {
+  dim3 grid((unsigned)((c.T + kGT - 1) / kGT), (unsigned)nsplit);
+  hipLaunchKernelGGL(route_gemm_kernel<NB>, grid, dim3(kGThreads), 0, s, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(w), (int)c.T, (int)c.H, (int)c.E, per, part);
   return hipGetLastError();
 }
 
-template <int NBW>
-hipError_t launch_route_split_n(const moe_config& c, const void* x, const void* w, const float* bias,
-                                const RouteSel& rs, int32_t* idx, float* tw, float* part, hipStream_t s) {
-  if constexpr (NBW <= 2)
-    if (route_rbt(c.T, c.E) == 4) return launch_route_split_t<NBW, 4>(c, x, w, bias, rs, idx, tw, part, s);
-  if constexpr (NBW <= 4)
-    if (route_rbt(c.T, c.E) == 2) return launch_route_split_t<NBW, 2>(c, x, w, bias, rs, idx, tw, part, s);
-  return launch_route_split_t<NBW, 1>(c, x, w, bias, rs, idx, tw, part, s);
+template <int NBW, int RBT>
+hipError_t launch_route_wide(const moe_config& c, const void* x, const void* w, int per, int nsplit, float* part,
+                             hipStream_t s) {
+  dim3 grid((unsigned)((c.T + RBT * kRBM - 1) / (RBT * kRBM)), (unsigned)nsplit);
+  hipLaunchKernelGGL((route_partial_bf16_kernel<NBW, RBT>), grid, dim3(kRThreads), 0, s,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), (int)c.T, (int)c.H,
+                     (int)c.E, per, part);
+  return hipGetLastError();
 }
 
 }  // namespace
 
+int route_partial_slices(const moe_config& c) { return c.dtype == MOE_BF16 ? route_plan(c).nsplit : 0; }
+
 size_t route_scratch_bytes(const moe_config& c) {
   if (c.dtype != MOE_BF16) return 0;
   const int64_t Epad = (c.E + 31) / 32 * 32;
-  return (size_t)route_nsplit(c.T, c.H, c.E) * c.T * Epad * 4;
+  return (size_t)route_plan(c).nsplit * c.T * Epad * 4;
 }
 
-hipError_t launch_route_split(const moe_config& c, const void* x, const void* w, const float* bias,
-                              const RouteSel& rs, int32_t* topk_idx, float* topk_w, void* scratch,
-                              hipStream_t s) {
-  if (c.dtype != MOE_BF16) return launch_route(c, x, w, bias, rs, topk_idx, topk_w, s);
-  float* part = static_cast<float*>(scratch);
-  if (c.E <= 128) return launch_route_split_n<1>(c, x, w, bias, rs, topk_idx, topk_w, part, s);
-  if (c.E <= 256) return launch_route_split_n<2>(c, x, w, bias, rs, topk_idx, topk_w, part, s);
-  if (c.E <= 512) return launch_route_split_n<4>(c, x, w, bias, rs, topk_idx, topk_w, part, s);
-  return launch_route_split_n<8>(c, x, w, bias, rs, topk_idx, topk_w, part, s);
+hipError_t launch_route_partials(const moe_config& c, const void* x, const void* w, float* part, hipStream_t s) {
+  const RoutePlan p = route_plan(c);
+  if (p.kind == RK_GEMV) {
+    dim3 grid((unsigned)((c.E + 15) / 16), (unsigned)p.nsplit);
+    hipLaunchKernelGGL(route_gemv_kernel, grid, dim3(kVWaves * 64), 0, s, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(w), (int)c.T, (int)c.H, (int)c.E, p.nsplit, part);
+    return hipGetLastError();
+  }
+  if (p.kind == RK_GEMM) {
+    if (c.E <= 32) return launch_route_gemm<1>(c, x, w, p.per, p.nsplit, part, s);
+    if (c.E <= 64) return launch_route_gemm<2>(c, x, w, p.per, p.nsplit, part, s);
+    if (c.E <= 128) return launch_route_gemm<4>(c, x, w, p.per, p.nsplit, part, s);
+    return launch_route_gemm<8>(c, x, w, p.per, p.nsplit, part, s);
+  }
+  const int rbt = route_rbt(c.T, c.E);
+  if (c.E <= 512)
+    return rbt == 2 ? launch_route_wide<4, 2>(c, x, w, p.per, p.nsplit, part, s)
+                    : launch_route_wide<4, 1>(c, x, w, p.per, p.nsplit, part, s);
+  return launch_route_wide<8, 1>(c, x, w, p.per, p.nsplit, part, s);
 }
 
 hipError_t launch_route(const moe_config& c, const void* x, const void* w, const float* bias, const RouteSel& rs,
