@@ -426,6 +426,7 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
   g.N = c->I;
   g.a_rows = c->T;
   g.out = at(ws, L.h);
+  g.nt_out = true;
   HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) {
     return q == nullptr ? launch_gateup(a, c->dtype, s) : launch_gateup_fp8(a, s);
   }));
@@ -448,6 +449,7 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
   g.N = c->H;
   g.a_rows = L.rows;
   g.out = at(ws, L.y_perm);
+  g.nt_out = (int64_t)L.rows * c->H * (int64_t)esize(c) > kLastLevelCacheBytes;
   HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) {
     return q == nullptr ? launch_down(a, c->dtype, s) : launch_down_fp8(a, s);
   }));
@@ -634,6 +636,7 @@ moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void*
   g.N = c->I;
   g.a_rows = c->T;
   g.out = at(ws, L.h);
+  g.nt_out = true;
   HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) { return launch_gateup(a, c->dtype, s); }));
   g.A = at(ws, L.h);
   g.gather = nullptr;
@@ -645,6 +648,7 @@ moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void*
   g.N = c->H;
   g.a_rows = L.rows;
   g.out = at(ws, L.y_perm);
+  g.nt_out = (int64_t)L.rows * c->H * (int64_t)esize(c) > kLastLevelCacheBytes;
   HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) { return launch_down(a, c->dtype, s); }));
   const void* ysh = c->n_shared ? static_cast<const void*>(at(ws, L.y_perm + (size_t)R * c->H * esize(c))) : nullptr;
   // weight of a chosen pair: its gate score times routed_scaling_factor

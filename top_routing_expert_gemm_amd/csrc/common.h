@@ -190,6 +190,10 @@ struct GemmArgs {
   void* out;                // [rows, N]
   int bm;                   // chunk height the list was cut to (selects the kernel)
   int64_t a_rows = 0;       // rows of A addressable through `gather` / the row space
+  // Output stores bypass the caches (written once, read once by the next pass):
+  // set for h, and for y_perm when it is larger than the last-level cache
+  // (smaller ones are read back from it by the combine).
+  bool nt_out = false;
   // FP8 weights (w0/w1/ws0/ws1 then hold E4M3 codes): float32 scales per
   // kFp8Block x kFp8Block block, [E, N/128, K/128] and [N/128, K/128] (shared)
   const float* sc0 = nullptr;
@@ -198,6 +202,9 @@ struct GemmArgs {
   const float* ssc1 = nullptr;
 };
 
+// Last-level (MALL) cache size of the MI355X: outputs larger than this are
+// stored non-temporally.
+constexpr int64_t kLastLevelCacheBytes = int64_t(256) << 20;
 hipError_t launch_gateup(const GemmArgs& a, int dtype, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, int dtype, hipStream_t s);
 

@@ -142,6 +142,16 @@ __device__ __forceinline__ void tile_of(int L, int n_tiles, const Chunk* chunks,
   ci = base + q % cnt;
 }
 
+// One 16-byte piece of an output row from the epilogue's LDS staging tile;
+// `nt`: non-temporal store (the cache policy of data written once and read
+// once later, by the next pass).
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_out(uint16_t* dst, const uint16_t* src, bool nt) {
+  const v4u32 v = *reinterpret_cast<const v4u32*>(src);
+  if (nt) __builtin_nontemporal_store(v, reinterpret_cast<v4u32*>(dst));
+  else *reinterpret_cast<v4u32*>(dst) = v;
+}
+
 // silu(g) = g / (1 + e^-g), with e^-g = 2^(-g log2 e) from the hardware base-2
 // exponential and the quotient from the hardware reciprocal (each within about
 // one ulp in fp32): five instructions per value instead of a correctly rounded
@@ -422,8 +432,7 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bf16(GemmArgs a, int n_tiles)
         const int row = wrow0 + pass * 32 + lr;
         const int64_t n = n0 + c16 * 8;
         if (row < ch.nrows && n < N)
-          *reinterpret_cast<uint4*>(out + ((int64_t)ch.row0 + row) * N + n) =
-              *reinterpret_cast<const uint4*>(tile + lr * LDSR + c16 * 8);
+          store_out(out + ((int64_t)ch.row0 + row) * N + n, tile + lr * LDSR + c16 * 8, a.nt_out);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass overwrites the region
     }
@@ -762,8 +771,7 @@ __device__ __forceinline__ void rs_wave(const GemmArgs& a, const Chunk& ch, int 
         const int row = rowb + lr;
         const int64_t n = n0 + c16 * 8;
         if (row < ch.nrows && n < N)
-          *reinterpret_cast<uint4*>(out + ((int64_t)ch.row0 + row) * N + n) =
-              *reinterpret_cast<const uint4*>(tile + lr * LDSR + c16 * 8);
+          store_out(out + ((int64_t)ch.row0 + row) * N + n, tile + lr * LDSR + c16 * 8, a.nt_out);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block overwrites the region
     }
@@ -1118,8 +1126,7 @@ __device__ __forceinline__ void ws_wave(const GemmArgs& a, const Chunk& ch, int 
         const int row = rowb + lr;
         const int64_t n = n0 + c16 * 8;
         if (row < ch.nrows && n < N)
-          *reinterpret_cast<uint4*>(out + ((int64_t)ch.row0 + row) * N + n) =
-              *reinterpret_cast<const uint4*>(tile + lr * LDSR + c16 * 8);
+          store_out(out + ((int64_t)ch.row0 + row) * N + n, tile + lr * LDSR + c16 * 8, a.nt_out);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next block overwrites the region
     }
