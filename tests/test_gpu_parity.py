@@ -47,6 +47,15 @@ SMALL = {
                                    logit_skew=True, n_shared=1, I_shared=256, cfg_id=115),
     "bf16_h320_i64_skew": MoEShape("bf16_h320_i64_skew", T=1500, H=320, I=64, E=16, k=2, gate=GATE_SOFTMAX,
                                    logit_skew=True, n_shared=1, I_shared=64, cfg_id=116),
+    # capacity at most 160 rows and no shared expert: one list of 160-row chunks,
+    # gate/up on the 160 x 512 tile.  Capacity exactly 160 (skewed router: many
+    # experts full, 5 row blocks), H = 320 (5 K steps, two weight stages: an odd
+    # count), I = 320 (a second n-tile mostly past N); then capacity 128, k = 2,
+    # H = 384 (6 K steps), I = 192 (one n-tile, a quarter of it past N)
+    "bf16_capacity_160_tile": MoEShape("bf16_capacity_160_tile", T=2048, H=320, I=320, E=16, k=1,
+                                       renormalize=False, capacity_factor=1.25, logit_skew=True, cfg_id=117),
+    "bf16_capacity_128_k2": MoEShape("bf16_capacity_128_k2", T=1024, H=384, I=192, E=24, k=2,
+                                     capacity_factor=1.5, cfg_id=118),
     "fp32_tiny": WORKLOADS[TINY],
     "fp32_sigmoid_shared_capacity": MoEShape("fp32_sigmoid_shared_capacity", T=200, H=192, I=128, E=8, k=3,
                                              gate=GATE_SIGMOID, capacity_factor=1.0, n_shared=1, I_shared=128,

@@ -41,6 +41,13 @@ struct Chunk {
 #endif
 constexpr int kGemmBMrs = 256;
 constexpr int kGemmBMdl = 320;
+// Chunk height of layers whose routed groups hold at most this many rows (an
+// expert capacity) and that have no shared expert: one list of 160-row chunks,
+// whose gate/up pass runs a 160 x 512 tile.
+#ifndef MOE_GEMM_WN
+#define MOE_GEMM_WN 1
+#endif
+constexpr int kGemmBMwn = 160;
 // M-tile height of the fp32 grouped GEMM.
 constexpr int kGemmBMf32 = 64;
 // Row chunks of the bf16 weight-streaming path used for small batches (decode).
@@ -69,7 +76,8 @@ int64_t max_chunks(int64_t rows_max, int64_t E, int64_t shared_rows, int bm);
 // max_a / max_b: capacities of the two lists.  group_max (-1: unknown) bounds
 // the rows of one routed group: at most 256 rows, every group takes the
 // 256-row list (and so does the shared group, which never makes the other list
-// on its own), so the 320-row list is left out and its launches skipped.
+// on its own), so the 320-row list is left out and its launches skipped; at
+// most 160 rows with no shared rows, the one list is cut to 160-row chunks.
 struct ChunkPlan {
   ChunkCut cut;
   int64_t max_a, max_b;
@@ -86,6 +94,7 @@ inline ChunkPlan chunk_plan(const moe_config& c, int64_t routed, int64_t shared,
              rows * c.I * 2 < lim && c.H * c.I * 2 < lim) {
     bm_a = kGemmBMrs;
     bm_b = (group_max >= 0 && group_max <= kGemmBMrs) ? 0 : kGemmBMdl;
+    if (MOE_GEMM_WN && group_max >= 0 && group_max <= kGemmBMwn && shared == 0) bm_a = kGemmBMwn;
   }
   p.max_a = max_chunks(routed, c.E, shared, bm_a);
   p.max_b = bm_b ? max_chunks(routed, c.E, shared, bm_b) : 0;

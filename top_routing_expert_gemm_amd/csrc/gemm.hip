@@ -878,43 +878,72 @@ bool rs_fits(const GemmArgs& a) {
 // next substep's operands are read into the registers the current ones free:
 // B block 0 half-way through, each A block after its last use, B block 1 at
 // the end.
-constexpr int WWM = 2;             // wave rows
-constexpr int WWN = 4;             // wave columns
-constexpr int WNT = 64 * WWM * WWN;
+constexpr int WNT = 512;           // eight waves, two per SIMD
 constexpr int WRB = 5;             // 32-row blocks per wave (at most)
 constexpr int WNB = 2;             // 32-column blocks per wave
-constexpr int WBM = 32 * WRB * WWM;  // 320
-constexpr int WBN = 32 * WNB * WWN;  // 256
-constexpr int WNAL = WBM / 64;     // A loads per lane per K step (64 rows each)
-constexpr int WNBL = WBN / 64;     // B loads per lane per K step
-constexpr int WBST = 3;            // weight stages
-static_assert(kGemmBMdl == WBM, "chunk lists are cut to the tile height");
-static_assert(WBM * 128 + WBST * WBN * 128 <= 160 * 1024, "LDS");
-static_assert(WNAL * 64 * 8 * 16 == WBM * 128 && WNBL * 64 * 8 * 16 == WBN * 128, "one 16-byte piece per lane per load");
+// Tile shapes: V = 0 is the 320 x 256 tile (2 x 4 waves, three weight stages
+// issued two K steps ahead); V = 1 is a 160 x 512 tile (1 x 8 waves, two 64 KB
+// weight stages issued one step ahead) for lists whose chunks all hold at most
+// 160 rows (capacity-limited layers): such a chunk fills only half of a
+// 320-row tile, and twice the columns halve the token-row bytes fetched per
+// weight byte.
+template <int V>
+struct Ws {
+  static constexpr int WM = V == 0 ? 2 : 1;      // wave rows
+  static constexpr int WN = 8 / WM;              // wave columns
+  static constexpr int ST = V == 0 ? 3 : 2;      // weight stages
+  static constexpr int BM = 32 * WRB * WM;       // 320 / 160 tile rows
+  static constexpr int BN = 32 * WNB * WN;       // 256 / 512 tile columns
+  static constexpr int AL = (BM + 63) / 64;      // 64-row A groups (loads per lane per K step, at most)
+  static constexpr int BL = BN / 64;             // 64-row B groups (loads per lane per K step)
+  static constexpr int AS = WM * 256;            // LDS distance (16-byte slots) between a wave's row blocks
+  static_assert(AL * 64 * 128 + ST * BN * 128 <= 160 * 1024, "LDS");
+  static_assert(WM * WN * 64 == WNT, "eight waves");
+};
+constexpr int WBM = Ws<0>::BM;
+constexpr int kWideRows = Ws<1>::BM;
+static_assert(kGemmBMdl == WBM && kGemmBMwn == kWideRows, "chunk lists are cut to the tile height");
 
 // Distinct objects, so the compiler can tell the direct writes in flight to
 // one stage from the reads of another.
-__shared__ __attribute__((aligned(1024))) u32x4 sWA[WBM * 8];
-__shared__ __attribute__((aligned(1024))) u32x4 sWB0[WBN * 8];
-__shared__ __attribute__((aligned(1024))) u32x4 sWB1[WBN * 8];
-__shared__ __attribute__((aligned(1024))) u32x4 sWB2[WBN * 8];
-template <int B>
-__device__ __forceinline__ u32x4* stWB() {
-  if constexpr (B == 0) return sWB0;
-  else if constexpr (B == 1) return sWB1;
-  else return sWB2;
+__shared__ __attribute__((aligned(1024))) u32x4 sWA[Ws<0>::AL * 512];
+__shared__ __attribute__((aligned(1024))) u32x4 sWB0[Ws<0>::BL * 512];
+__shared__ __attribute__((aligned(1024))) u32x4 sWB1[Ws<0>::BL * 512];
+__shared__ __attribute__((aligned(1024))) u32x4 sWB2[Ws<0>::BL * 512];
+__shared__ __attribute__((aligned(1024))) u32x4 sVA[Ws<1>::AL * 512];
+__shared__ __attribute__((aligned(1024))) u32x4 sVB0[Ws<1>::BL * 512];
+__shared__ __attribute__((aligned(1024))) u32x4 sVB1[Ws<1>::BL * 512];
+template <int V>
+__device__ __forceinline__ u32x4* wsA() {
+  if constexpr (V == 0) return sWA;
+  else return sVA;
+}
+template <int V, int B>
+__device__ __forceinline__ u32x4* wsB() {
+  if constexpr (V == 0) {
+    if constexpr (B == 0) return sWB0;
+    else if constexpr (B == 1) return sWB1;
+    else return sWB2;
+  } else {
+    if constexpr (B == 0) return sVB0;
+    else return sVB1;
+  }
 }
 
+// Sized for both tile shapes (the unused entries of the smaller one are never
+// touched, so they cost no registers).
+constexpr int kWsMaxAL = Ws<0>::AL > Ws<1>::AL ? Ws<0>::AL : Ws<1>::AL;
+constexpr int kWsMaxBL = Ws<0>::BL > Ws<1>::BL ? Ws<0>::BL : Ws<1>::BL;
 struct WsRegs {
-  u32x4 a[WNAL];
+  u32x4 a[kWsMaxAL];
 };
 
 struct WsSrc {
   __amdgpu_buffer_rsrc_t ra;   // A rows
   __amdgpu_buffer_rsrc_t rb;   // this wave's weight matrix (gate/up: gate for waves 0-3, up for 4-7)
-  uint32_t aoff[WNAL];         // per-lane byte offset of A piece i at k = 0
+  uint32_t aoff[kWsMaxAL];     // per-lane byte offset of A piece i at k = 0
   uint32_t boff;               // per-lane byte offset of the (source-swizzled) piece within a B row group
-  uint32_t bgrp[WNBL];         // byte offset of B row group j within the matrix
+  uint32_t bgrp[kWsMaxBL];     // byte offset of B row group j within the matrix
   int wave;
 };
 
@@ -924,45 +953,51 @@ struct WsOps {
 };
 
 // Token rows of A group i (tile rows 64 i + lane row) of K step kt into registers.
+template <int V>
 __device__ __forceinline__ void ws_load_a(WsRegs& r, const WsSrc& s, int kt, int i) {
   r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, s.aoff[i], kt * (RBK * 2), 0);
 }
 // Weights of B row group j of K step kt straight into stage B (rows 64 j +
 // 8 wave .. + 8: one 1 KB block per wave).
-template <int B>
+template <int V, int B>
 __device__ __forceinline__ void ws_load_b(const WsSrc& s, int kt, int j) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rb, (lds_void*)(stWB<B>() + j * 512 + s.wave * 64), 16, s.boff,
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rb, (lds_void*)(wsB<V, B>() + j * 512 + s.wave * 64), 16, s.boff,
                                            (int)s.bgrp[j] + kt * (RBK * 2), 0, kNonTemporal);
 }
 
-// One 16-wide substep SS of K step t, reading weight stage BS:
+// One 16-wide substep SS of K step t, reading weight stage BS (ST stages):
 //   SS 0, first half (MFMAs (a, 0) for every row block a): the loads of the
-//         token rows of step t + 1 (LA) and then of the weights of step t + 2
-//         into stage (BS + 2) % 3 (LB), each fenced so the issue order holds;
+//         token rows of step t + 1 (LA) and then of the weights of step
+//         t + ST - 1 into stage (BS + ST - 1) % ST, the stage step t - 1 used
+//         (LB), each fenced so the issue order holds;
 //   SS 3 (NEXT): the first barrier (every wave is done reading step t's token
 //         rows: its last reads were in SS 2), then the first half carrying the
 //         stores of step t + 1's token rows, then the second barrier, after
 //         waiting for all of this wave's loads but the weights of step t + 2
-//         (issued last): step t + 1 is complete in LDS;
+//         (three stages: issued last): step t + 1 is complete in LDS;
 //   then B block 0 of the next substep (step t + 1's stage in SS 3), and the
 //   second half, MFMAs (a, 1), each followed by the read of the next
 //   substep's A block a; last, B block 1 of the next substep.
-template <int MODE, int SS, int BS, int NAL, int NRB, bool LA, bool LB, bool NEXT>
-__device__ __forceinline__ void ws_substep(f32x16 (&acc)[WRB][WNB], WsRegs& R, WsOps (&op)[2], const WsSrc& src,
-                                           int t, int wr, const int (&ra)[4], const int (&rb)[4]) {
+template <int V, int MODE, int SS, int BS, int NAL, int NRB, bool LA, bool LB, bool NEXT>
+__device__ __forceinline__ void ws_substep(f32x16 (&acc)[WRB][WNB], WsRegs& R, WsOps (&op)[2],
+                                           const WsSrc& src, int t, int wr, const int (&ra)[4],
+                                           const int (&rb)[4]) {
+  using S = Ws<V>;
   constexpr int NA0 = (SS == 0 && LA) ? NAL : 0;
-  constexpr int P = SS == 0 ? NA0 + (LB ? WNBL : 0) : ((SS == 3 && NEXT) ? NAL : 0);  // first-half side operations
+  constexpr int P = SS == 0 ? NA0 + (LB ? S::BL : 0) : ((SS == 3 && NEXT) ? NAL : 0);  // first-half side operations
   constexpr bool RD = SS < 3 || NEXT;  // operands of the next substep are read here
-  const u32x4* Lb = stWB<SS < 3 ? BS : (BS + 1) % WBST>();
+  const u32x4* Lb = wsB<V, SS < 3 ? BS : (BS + 1) % S::ST>();
+  u32x4* La = wsA<V>();
   constexpr int sr = (SS + 1) & 3;
+  constexpr int BN_ = (BS + S::ST - 1) % S::ST;  // stage of the weights loaded here
   WsOps& cur = op[SS & 1];
   WsOps& nxt = op[(SS & 1) ^ 1];
   auto side = [&](int q) {
     if constexpr (SS == 0) {
-      if (q < NA0) ws_load_a(R, src, t + 1, q);
-      else ws_load_b<(BS + 2) % WBST>(src, t + 2, q - NA0);
+      if (q < NA0) ws_load_a<V>(R, src, t + 1, q);
+      else ws_load_b<V, BN_>(src, t + Ws<V>::ST - 1, q - NA0);
     } else {
-      sWA[q * 512 + wr] = R.a[q];
+      La[q * 512 + wr] = R.a[q];
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -987,78 +1022,97 @@ __device__ __forceinline__ void ws_substep(f32x16 (&acc)[WRB][WNB], WsRegs& R, W
     }
   }
   if constexpr (SS == 3 && NEXT) {
-    stage_barrier<LB ? WNBL : 0>();
+    stage_barrier<(LB && S::ST == 3) ? S::BL : 0>();
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (RD && NRB > 0) nxt.b[0] = __builtin_bit_cast(bf16x8, Lb[rb[sr]]);
 #pragma unroll
   for (int m = 0; m < NRB; ++m) {
     acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[m], cur.b[1], acc[m][1], 0, 0, 0);
-    if constexpr (RD) nxt.a[m] = __builtin_bit_cast(bf16x8, sWA[ra[sr] + m * 512]);
+    if constexpr (RD) nxt.a[m] = __builtin_bit_cast(bf16x8, La[ra[sr] + m * S::AS]);
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (RD && NRB > 0) nxt.b[1] = __builtin_bit_cast(bf16x8, Lb[rb[sr] + 256]);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MODE, int BS, int NAL, int NRB, bool LA, bool LB, bool NEXT>
-__device__ __forceinline__ void ws_step(f32x16 (&acc)[WRB][WNB], WsRegs& R, WsOps (&op)[2], const WsSrc& src, int t,
-                                        int wr, const int (&ra)[4], const int (&rb)[4]) {
-  ws_substep<MODE, 0, BS, NAL, NRB, LA, LB, NEXT>(acc, R, op, src, t, wr, ra, rb);
-  ws_substep<MODE, 1, BS, NAL, NRB, LA, LB, NEXT>(acc, R, op, src, t, wr, ra, rb);
-  ws_substep<MODE, 2, BS, NAL, NRB, LA, LB, NEXT>(acc, R, op, src, t, wr, ra, rb);
-  ws_substep<MODE, 3, BS, NAL, NRB, LA, LB, NEXT>(acc, R, op, src, t, wr, ra, rb);
+template <int V, int MODE, int BS, int NAL, int NRB, bool LA, bool LB, bool NEXT>
+__device__ __forceinline__ void ws_step(f32x16 (&acc)[WRB][WNB], WsRegs& R, WsOps (&op)[2], const WsSrc& src,
+                                        int t, int wr, const int (&ra)[4], const int (&rb)[4]) {
+  ws_substep<V, MODE, 0, BS, NAL, NRB, LA, LB, NEXT>(acc, R, op, src, t, wr, ra, rb);
+  ws_substep<V, MODE, 1, BS, NAL, NRB, LA, LB, NEXT>(acc, R, op, src, t, wr, ra, rb);
+  ws_substep<V, MODE, 2, BS, NAL, NRB, LA, LB, NEXT>(acc, R, op, src, t, wr, ra, rb);
+  ws_substep<V, MODE, 3, BS, NAL, NRB, LA, LB, NEXT>(acc, R, op, src, t, wr, ra, rb);
 }
 
-// The K loop over nk >= 2 steps, R3 = (nk - 2) % 3: steps 0 .. nk - 3 load both
-// operands ahead (the loop, unrolled by the three weight stages, then R3 more),
-// step nk - 2 loads only the token rows of the last step, step nk - 1 nothing.
-template <int MODE, int NAL, int NRB, int R3>
+// The K loop over nk >= 2 steps.  Three weight stages, R = (nk - 2) % 3: steps
+// 0 .. nk - 3 load both operands ahead (the loop, unrolled by the three
+// stages, then R more), step nk - 2 loads only the token rows of the last
+// step, step nk - 1 nothing.  Two stages, R = (nk - 1) % 2: steps 0 .. nk - 2
+// load both operands of the next step (the loop unrolled by two, then R more),
+// step nk - 1 nothing.  Step t reads weight stage t % ST.
+template <int V, int MODE, int NAL, int NRB, int R>
 __device__ __forceinline__ void ws_kloop(f32x16 (&acc)[WRB][WNB], const WsSrc& src, int nk, int wr,
                                          const int (&ra)[4], const int (&rb)[4]) {
-  WsRegs R;
+  using S = Ws<V>;
+  WsRegs Rg;
   WsOps op[2];
+  u32x4* La = wsA<V>();
 #pragma unroll
   for (int i = 0; i < NAL; ++i) {
-    ws_load_a(R, src, 0, i);
+    ws_load_a<V>(Rg, src, 0, i);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int j = 0; j < WNBL; ++j) {
-    ws_load_b<0>(src, 0, j);
+  for (int j = 0; j < S::BL; ++j) {
+    ws_load_b<V, 0>(src, 0, j);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (S::ST == 3) {
 #pragma unroll
-  for (int j = 0; j < WNBL; ++j) {
-    ws_load_b<1>(src, 1, j);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < S::BL; ++j) {
+      ws_load_b<V, 1>(src, 1, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 #pragma unroll
-  for (int i = 0; i < NAL; ++i) sWA[i * 512 + wr] = R.a[i];
-  stage_barrier<WNBL>();  // token rows and weights of step 0 in LDS; step 1's weights may be in flight
+  for (int i = 0; i < NAL; ++i) La[i * 512 + wr] = Rg.a[i];
+  // token rows and weights of step 0 in LDS (three stages: step 1's weights may be in flight)
+  stage_barrier<S::ST == 3 ? S::BL : 0>();
   if constexpr (NRB > 0) {
-    op[0].b[0] = __builtin_bit_cast(bf16x8, sWB0[rb[0]]);
+    const u32x4* L0 = wsB<V, 0>();
+    op[0].b[0] = __builtin_bit_cast(bf16x8, L0[rb[0]]);
 #pragma unroll
-    for (int m = 0; m < NRB; ++m) op[0].a[m] = __builtin_bit_cast(bf16x8, sWA[ra[0] + m * 512]);
-    op[0].b[1] = __builtin_bit_cast(bf16x8, sWB0[rb[0] + 256]);
+    for (int m = 0; m < NRB; ++m) op[0].a[m] = __builtin_bit_cast(bf16x8, La[ra[0] + m * S::AS]);
+    op[0].b[1] = __builtin_bit_cast(bf16x8, L0[rb[0] + 256]);
   }
   int t = 0;
-  for (; t + 3 <= nk - 2; t += 3) {
-    ws_step<MODE, 0, NAL, NRB, true, true, true>(acc, R, op, src, t, wr, ra, rb);
-    ws_step<MODE, 1, NAL, NRB, true, true, true>(acc, R, op, src, t + 1, wr, ra, rb);
-    ws_step<MODE, 2, NAL, NRB, true, true, true>(acc, R, op, src, t + 2, wr, ra, rb);
+  if constexpr (S::ST == 3) {
+    for (; t + 3 <= nk - 2; t += 3) {
+      ws_step<V, MODE, 0, NAL, NRB, true, true, true>(acc, Rg, op, src, t, wr, ra, rb);
+      ws_step<V, MODE, 1, NAL, NRB, true, true, true>(acc, Rg, op, src, t + 1, wr, ra, rb);
+      ws_step<V, MODE, 2, NAL, NRB, true, true, true>(acc, Rg, op, src, t + 2, wr, ra, rb);
+    }
+    if constexpr (R >= 1) ws_step<V, MODE, 0, NAL, NRB, true, true, true>(acc, Rg, op, src, t, wr, ra, rb);
+    if constexpr (R >= 2) ws_step<V, MODE, 1, NAL, NRB, true, true, true>(acc, Rg, op, src, t + 1, wr, ra, rb);
+    ws_step<V, MODE, R % 3, NAL, NRB, true, false, true>(acc, Rg, op, src, t + R, wr, ra, rb);
+    ws_step<V, MODE, (R + 1) % 3, NAL, NRB, false, false, false>(acc, Rg, op, src, t + R + 1, wr, ra, rb);
+  } else {
+    for (; t + 2 <= nk - 1; t += 2) {
+      ws_step<V, MODE, 0, NAL, NRB, true, true, true>(acc, Rg, op, src, t, wr, ra, rb);
+      ws_step<V, MODE, 1, NAL, NRB, true, true, true>(acc, Rg, op, src, t + 1, wr, ra, rb);
+    }
+    if constexpr (R >= 1) ws_step<V, MODE, 0, NAL, NRB, true, true, true>(acc, Rg, op, src, t, wr, ra, rb);
+    ws_step<V, MODE, R % 2, NAL, NRB, false, false, false>(acc, Rg, op, src, t + R, wr, ra, rb);
   }
-  if constexpr (R3 >= 1) ws_step<MODE, 0, NAL, NRB, true, true, true>(acc, R, op, src, t, wr, ra, rb);
-  if constexpr (R3 >= 2) ws_step<MODE, 1, NAL, NRB, true, true, true>(acc, R, op, src, t + 1, wr, ra, rb);
-  ws_step<MODE, R3 % WBST, NAL, NRB, true, false, true>(acc, R, op, src, t + R3, wr, ra, rb);
-  ws_step<MODE, (R3 + 1) % WBST, NAL, NRB, false, false, false>(acc, R, op, src, t + R3 + 1, wr, ra, rb);
 }
 
 // K loop and epilogue of one wave, which multiplies NRB row blocks (tile rows
-// (2a + wm) * 32 .. + 32); NAL 64-row A groups are fetched for the workgroup.
-template <int MODE, int NAL, int NRB, int R3>
+// (WM a + wm) * 32 .. + 32); NAL 64-row A groups are fetched for the workgroup.
+template <int V, int MODE, int NAL, int NRB, int R>
 __device__ __forceinline__ void ws_wave(const GemmArgs& a, const Chunk& ch, int nt, const WsSrc& src, int wave,
                                         int wm, int wn, int lane, int wr) {
+  using S = Ws<V>;
   const int64_t N = a.N;
   const int nk = (int)(a.K / RBK);
   int ra[4], rb[4];
@@ -1077,22 +1131,30 @@ __device__ __forceinline__ void ws_wave(const GemmArgs& a, const Chunk& ch, int 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  ws_kloop<MODE, NAL, NRB, R3>(acc, src, nk, wr, ra, rb);
+  ws_kloop<V, MODE, NAL, NRB, R>(acc, src, nk, wr, ra, rb);
 
   // ---- epilogue: as the 256-row register-staged kernel, through a 16 KB
-  // wave-private LDS region (two per 32 KB weight stage, waves 6-7 in the token
-  // row buffer; free once every wave is past the K loop)
+  // wave-private LDS region (free once every wave is past the K loop): 320 x
+  // 256, two per 32 KB weight stage and waves 6-7 in the token row buffer;
+  // 160 x 512, four per 64 KB weight stage
   rs_barrier();
   if constexpr (NRB > 0) {
     constexpr int NJ = MODE == MODE_GATEUP ? 1 : WNB;  // 32-column output blocks of this wave
     constexpr int LDSR = NJ * 32 + 8;                   // padded LDS row (elements)
     constexpr int CPRW = NJ * 4;                        // 16-byte chunks per output row
-    static_assert(32 * LDSR * 2 <= 16 * 1024 && 2 * 16 * 1024 <= WBN * 128 && 2 * 16 * 1024 <= WBM * 128,
-                  "epilogue region");
-    u32x4* reg = wave < 2 ? sWB0 : wave < 4 ? sWB1 : wave < 6 ? sWB2 : sWA;
-    uint16_t* tile = reinterpret_cast<uint16_t*>(reg) + (wave & 1) * (16 * 1024 / 2);
+    static_assert(32 * LDSR * 2 <= 16 * 1024, "epilogue region");
+    uint16_t* tile;
+    if constexpr (V == 0) {
+      static_assert(2 * 16 * 1024 <= S::BN * 128 && 2 * 16 * 1024 <= S::AL * 64 * 128, "epilogue region");
+      u32x4* reg = wave < 2 ? sWB0 : wave < 4 ? sWB1 : wave < 6 ? sWB2 : sWA;
+      tile = reinterpret_cast<uint16_t*>(reg) + (wave & 1) * (16 * 1024 / 2);
+    } else {
+      static_assert(4 * 16 * 1024 <= S::BN * 128, "epilogue region");
+      u32x4* reg = wave < 4 ? sVB0 : sVB1;
+      tile = reinterpret_cast<uint16_t*>(reg) + (wave & 3) * (16 * 1024 / 2);
+    }
     uint16_t* out = static_cast<uint16_t*>(a.out);
-    const int64_t n0 = MODE == MODE_GATEUP ? (int64_t)nt * 128 + wn * 32 : (int64_t)nt * WBN + wn * 64;
+    const int64_t n0 = MODE == MODE_GATEUP ? (int64_t)nt * (S::BN / 2) + wn * 32 : (int64_t)nt * S::BN + wn * 64;
     const bool odd = l32 & 1;
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
@@ -1118,7 +1180,7 @@ __device__ __forceinline__ void ws_wave(const GemmArgs& a, const Chunk& ch, int 
             *reinterpret_cast<uint32_t*>(tile + lr * LDSR + jj * 32 + (l32 & ~1)) = w;
           }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
-      const int rowb = (2 * i + wm) * 32;
+      const int rowb = (S::WM * i + wm) * 32;
 #pragma unroll
       for (int q = 0; q < 32 * CPRW / kWave; ++q) {
         const int idx = q * kWave + lane;
@@ -1133,12 +1195,13 @@ __device__ __forceinline__ void ws_wave(const GemmArgs& a, const Chunk& ch, int 
   }
 }
 
-template <int MODE, int NA, int R3>
+template <int V, int MODE, int NA, int R>
 __device__ __forceinline__ void ws_run(const GemmArgs& a, const Chunk& ch, int nt) {
+  using S = Ws<V>;
   constexpr int NAL = (NA + 1) / 2;  // 64-row A groups fetched
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / S::WN, wn = wave % S::WN;
   const bool shared = ch.group == a.E;
   const int64_t K = a.K, N = a.N;
 
@@ -1151,7 +1214,7 @@ __device__ __forceinline__ void ws_run(const GemmArgs& a, const Chunk& ch, int n
   src.wave = wave;
   src.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), (short)0, -1, kBufFlags);
 #pragma unroll
-  for (int i = 0; i < WNAL; ++i) {
+  for (int i = 0; i < S::AL; ++i) {
     const int rc = min(i * 64 + lrow, ch.nrows - 1);
     const int64_t row = (int64_t)ch.row0 + rc;
     int64_t sr = row;
@@ -1167,42 +1230,68 @@ __device__ __forceinline__ void ws_run(const GemmArgs& a, const Chunk& ch, int n
     const bool up = wave >= 4;
     W = static_cast<const uint16_t*>(up ? (shared ? a.ws1 : a.w1) : (shared ? a.ws0 : a.w0)) + goff;
 #pragma unroll
-    for (int j = 0; j < WNBL; ++j) src.bgrp[j] = (uint32_t)(min((int64_t)nt * 128 + j * 32, N - 32) * K * 2);
+    for (int j = 0; j < S::BL; ++j)
+      src.bgrp[j] = (uint32_t)(min((int64_t)nt * (S::BN / 2) + j * 32, N - 32) * K * 2);
     src.boff = (uint32_t)(((lrow & 31) * K + bchunk * 8) * 2);
   } else {
     W = static_cast<const uint16_t*>(shared ? a.ws0 : a.w0) + goff;
     // a group past N is clamped to the last 64 rows (loaded, never stored); N is a multiple of 64
 #pragma unroll
-    for (int j = 0; j < WNBL; ++j) src.bgrp[j] = (uint32_t)(min((int64_t)nt * WBN + j * 64, N - 64) * K * 2);
+    for (int j = 0; j < S::BL; ++j) src.bgrp[j] = (uint32_t)(min((int64_t)nt * S::BN + j * 64, N - 64) * K * 2);
     src.boff = (uint32_t)((lrow * K + bchunk * 8) * 2);
   }
   src.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W), (short)0, -1, kBufFlags);
 
-  if (wm == 0) ws_wave<MODE, NAL, (NA + 1) / 2, R3>(a, ch, nt, src, wave, wm, wn, lane, wr);
-  else ws_wave<MODE, NAL, NA / 2, R3>(a, ch, nt, src, wave, wm, wn, lane, wr);
+  if constexpr (S::WM == 1) {
+    ws_wave<V, MODE, NAL, NA, R>(a, ch, nt, src, wave, wm, wn, lane, wr);
+  } else {
+    if (wm == 0) ws_wave<V, MODE, NAL, (NA + 1) / 2, R>(a, ch, nt, src, wave, wm, wn, lane, wr);
+    else ws_wave<V, MODE, NAL, NA / 2, R>(a, ch, nt, src, wave, wm, wn, lane, wr);
+  }
 }
 
-template <int MODE, int R3>
-__global__ __launch_bounds__(WNT) void grouped_gemm_ws(GemmArgs a, int n_tiles) {
-  const int V = *a.n_chunks * n_tiles;
+template <int MODE, int V, int R>
+__device__ __forceinline__ void ws_tile(const GemmArgs& a, int n_tiles) {
+  const int nv = *a.n_chunks * n_tiles;
   int L;
-  if (!xcd_map_cyclic(blockIdx.x, V, SUPER * n_tiles, L)) return;
+  if (!xcd_map_cyclic(blockIdx.x, nv, SUPER * n_tiles, L)) return;
   int ci, nt;
   tile_of(L, n_tiles, a.chunks, ci, nt);
   const Chunk ch = a.chunks[ci];
-  switch ((ch.nrows + 31) / 32) {
-    case 1: ws_run<MODE, 1, R3>(a, ch, nt); break;
-    case 2: ws_run<MODE, 2, R3>(a, ch, nt); break;
-    case 3: ws_run<MODE, 3, R3>(a, ch, nt); break;
-    case 4: ws_run<MODE, 4, R3>(a, ch, nt); break;
-    case 5: ws_run<MODE, 5, R3>(a, ch, nt); break;
-    case 6: ws_run<MODE, 6, R3>(a, ch, nt); break;
-    case 7: ws_run<MODE, 7, R3>(a, ch, nt); break;
-    case 8: ws_run<MODE, 8, R3>(a, ch, nt); break;
-    case 9: ws_run<MODE, 9, R3>(a, ch, nt); break;
-    default: ws_run<MODE, 10, R3>(a, ch, nt); break;
+  if constexpr (V == 0) {
+    switch ((ch.nrows + 31) / 32) {
+      case 1: ws_run<V, MODE, 1, R>(a, ch, nt); break;
+      case 2: ws_run<V, MODE, 2, R>(a, ch, nt); break;
+      case 3: ws_run<V, MODE, 3, R>(a, ch, nt); break;
+      case 4: ws_run<V, MODE, 4, R>(a, ch, nt); break;
+      case 5: ws_run<V, MODE, 5, R>(a, ch, nt); break;
+      case 6: ws_run<V, MODE, 6, R>(a, ch, nt); break;
+      case 7: ws_run<V, MODE, 7, R>(a, ch, nt); break;
+      case 8: ws_run<V, MODE, 8, R>(a, ch, nt); break;
+      case 9: ws_run<V, MODE, 9, R>(a, ch, nt); break;
+      default: ws_run<V, MODE, 10, R>(a, ch, nt); break;
+    }
+    static_assert(Ws<0>::BM / 32 == 10, "row-block dispatch");
+  } else {
+    switch ((ch.nrows + 31) / 32) {
+      case 1: ws_run<V, MODE, 1, R>(a, ch, nt); break;
+      case 2: ws_run<V, MODE, 2, R>(a, ch, nt); break;
+      case 3: ws_run<V, MODE, 3, R>(a, ch, nt); break;
+      case 4: ws_run<V, MODE, 4, R>(a, ch, nt); break;
+      default: ws_run<V, MODE, 5, R>(a, ch, nt); break;
+    }
+    static_assert(Ws<1>::BM / 32 == 5, "row-block dispatch");
   }
-  static_assert(WBM / 32 == 10, "row-block dispatch");
+}
+
+// The 320 x 256 tile (R = (nk - 2) % 3) and the 160 x 512 tile (R = (nk - 1) % 2).
+template <int MODE, int R>
+__global__ __launch_bounds__(WNT) void grouped_gemm_ws(GemmArgs a, int n_tiles) {
+  ws_tile<MODE, 0, R>(a, n_tiles);
+}
+template <int MODE, int R>
+__global__ __launch_bounds__(WNT) void grouped_gemm_wn(GemmArgs a, int n_tiles) {
+  ws_tile<MODE, 1, R>(a, n_tiles);
 }
 
 // ------------------------------------------------------ bf16 streaming path
@@ -1417,6 +1506,14 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
     const int n_wt = (int)(a.N / 16);
     const int64_t grid = (a.max_chunks * n_wt + SW - 1) / SW;
     hipLaunchKernelGGL(grouped_stream_bf16<MODE>, dim3((unsigned)grid), dim3(SW * 64), 0, s, a, n_wt);
+  } else if (dtype == MOE_BF16 && MODE == MODE_GATEUP && a.bm == kWideRows && rs_fits(a)) {
+    constexpr int BN = Ws<1>::BN;
+    const int n_tiles = (int)((a.N + BN / 2 - 1) / (BN / 2));
+    const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
+    if ((a.K / RBK - 1) % 2)
+      hipLaunchKernelGGL((grouped_gemm_wn<MODE, 1>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles);
+    else
+      hipLaunchKernelGGL((grouped_gemm_wn<MODE, 0>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles);
   } else if (dtype == MOE_BF16 && a.bm == RBM && rs_fits(a)) {
     const int n_tiles = (int)(MODE == MODE_GATEUP ? (a.N + 127) / 128 : (a.N + RBN - 1) / RBN);
     const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
@@ -1425,7 +1522,8 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
     else
       hipLaunchKernelGGL((grouped_gemm_rs<MODE, false>), dim3((unsigned)grid), dim3(RNT), 0, s, a, n_tiles);
   } else if (dtype == MOE_BF16 && MOE_GEMM_WS && a.bm == WBM && rs_fits(a)) {
-    const int n_tiles = (int)(MODE == MODE_GATEUP ? (a.N + 127) / 128 : (a.N + WBN - 1) / WBN);
+    constexpr int BN = Ws<0>::BN;
+    const int n_tiles = (int)(MODE == MODE_GATEUP ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN);
     const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
     switch ((a.K / RBK - 2) % 3) {
       case 0: hipLaunchKernelGGL((grouped_gemm_ws<MODE, 0>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles); break;
@@ -1450,12 +1548,14 @@ hipError_t launch_gateup(const GemmArgs& a, int dtype, hipStream_t s) { return l
 // The down pass (K = I) runs the 256-row list's chunks on the 320-row kernel
 // as well (they have at most 256 rows): measured 1-2% faster there on the
 // DeepSeek-V3 and Mixtral shapes, where the gate/up pass (K = H) is 8% faster
-// with the 256-row kernel taking them.
+// with the 256-row kernel taking them.  The 160-row list's chunks go there
+// too: a 160 x 512 down tile would leave half the CUs of a capacity-limited
+// layer idle (H / 512 n-tiles per expert).
 #ifndef MOE_DOWN_ON_WS
 #define MOE_DOWN_ON_WS 1
 #endif
 hipError_t launch_down(const GemmArgs& a, int dtype, hipStream_t s) {
-  if (MOE_DOWN_ON_WS && MOE_GEMM_WS && dtype == MOE_BF16 && a.bm == kGemmBMrs && rs_fits(a)) {
+  if (MOE_DOWN_ON_WS && MOE_GEMM_WS && dtype == MOE_BF16 && (a.bm == kGemmBMrs || a.bm == kGemmBMwn) && rs_fits(a)) {
     GemmArgs b = a;
     b.bm = kGemmBMdl;
     return launch_gemm<MODE_DOWN>(b, dtype, s);
