@@ -16,6 +16,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kNumCUs = 256;      // MI355X compute units (32 per XCD)
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kMaxK = 16;
 constexpr int kMaxE = 1024;

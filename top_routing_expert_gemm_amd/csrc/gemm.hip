@@ -1251,10 +1251,10 @@ __device__ __forceinline__ void ws_run(const GemmArgs& a, const Chunk& ch, int n
 }
 
 template <int MODE, int V, int R>
-__device__ __forceinline__ void ws_tile(const GemmArgs& a, int n_tiles) {
+__device__ __forceinline__ void ws_tile(const GemmArgs& a, int n_tiles, int p) {
   const int nv = *a.n_chunks * n_tiles;
   int L;
-  if (!xcd_map_cyclic(blockIdx.x, nv, SUPER * n_tiles, L)) return;
+  if (!xcd_map_cyclic(p, nv, SUPER * n_tiles, L)) return;
   int ci, nt;
   tile_of(L, n_tiles, a.chunks, ci, nt);
   const Chunk ch = a.chunks[ci];
@@ -1287,11 +1287,26 @@ __device__ __forceinline__ void ws_tile(const GemmArgs& a, int n_tiles) {
 // The 320 x 256 tile (R = (nk - 2) % 3) and the 160 x 512 tile (R = (nk - 1) % 2).
 template <int MODE, int R>
 __global__ __launch_bounds__(WNT) void grouped_gemm_ws(GemmArgs a, int n_tiles) {
-  ws_tile<MODE, 0, R>(a, n_tiles);
+  ws_tile<MODE, 0, R>(a, n_tiles, blockIdx.x);
 }
+#ifndef MOE_WN_PERSIST
+#define MOE_WN_PERSIST 1
+#endif
+// The 160 x 512 tile's K loops are short (capacity-limited layers have narrow
+// H), so a workgroup's dispatch and set-up are a large share of a tile: one
+// workgroup per CU walks the tiles p = blockIdx.x, + gridDim.x, ... (gridDim.x
+// a multiple of the XCD count, so each workgroup keeps to its XCD's tiles).
 template <int MODE, int R>
 __global__ __launch_bounds__(WNT) void grouped_gemm_wn(GemmArgs a, int n_tiles) {
-  ws_tile<MODE, 1, R>(a, n_tiles);
+  if constexpr (MOE_WN_PERSIST) {
+    const int nv = *a.n_chunks * n_tiles;
+    for (int p = blockIdx.x; p < nv; p += gridDim.x) {
+      ws_tile<MODE, 1, R>(a, n_tiles, p);
+      __syncthreads();  // the epilogue's LDS reads are done before the next tile's loads land
+    }
+  } else {
+    ws_tile<MODE, 1, R>(a, n_tiles, blockIdx.x);
+  }
 }
 
 // ------------------------------------------------------ bf16 streaming path
@@ -1307,6 +1322,15 @@ __global__ __launch_bounds__(WNT) void grouped_gemm_wn(GemmArgs a, int n_tiles) 
 #endif
 #ifndef MOE_STREAM_SP
 #define MOE_STREAM_SP 4
+#endif
+// Down pass: wave gw takes its K blocks from block gw * ROT (mod K / SKB) on.
+// Its weight rows are I = 2048 elements, 4 KB apart, and the waves, all in
+// step, would otherwise read the same offset of every 4 KB row at once;
+// starting each wave one block further spreads them (decode down pass 538 ->
+// 504 us).  The gate/up rows (H = 7168, 14 KB) stream faster in step (992
+// against 1027 us rotated), so that pass is left as it is.
+#ifndef MOE_STREAM_ROT
+#define MOE_STREAM_ROT 1
 #endif
 constexpr int SW = 4;                 // waves per workgroup
 constexpr int SKB = MOE_STREAM_SKB;   // K per block (SKB / 32 MFMA substeps)
@@ -1347,11 +1371,17 @@ __global__ __launch_bounds__(SW * 64) void grouped_stream_bf16(GemmArgs a, int n
 
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const int nkb = (int)(K / SKB);  // K is a multiple of 64; a 64-wide tail block is handled below
+  const int rot = (MODE == MODE_DOWN && nkb > 0) ? (int)(((int64_t)gw * MOE_STREAM_ROT) % nkb) : 0;
+  auto koff = [&](int b) {  // K offset of the wave's b-th block: the blocks taken from block rot on, wrapping
+    int r = b + rot;
+    r -= r >= nkb ? nkb : 0;
+    return (int64_t)r * SKB;
+  };
   uint4 ra[SP][NV], rb0[SP][NV], rb1[SP][NV];
   if (nkb > 0) {  // (a K shorter than one block has only the tail below)
 #pragma unroll
   for (int p = 0; p < SP; ++p) {
-    const int64_t ko = (int64_t)min(p, nkb - 1) * SKB;
+    const int64_t ko = koff(min(p, nkb - 1));
     ldv(ra[p], pa + ko);
     ldv(rb0[p], p0 + ko);
     if (MODE == MODE_GATEUP) ldv(rb1[p], p1 + ko);
@@ -1369,7 +1399,7 @@ __global__ __launch_bounds__(SW * 64) void grouped_stream_bf16(GemmArgs a, int n
           if (MODE == MODE_GATEUP)
             acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, rb1[p][s2]), acc1, 0, 0, 0);
         }
-        const int64_t ko = (int64_t)min(kb + SP, nkb - 1) * SKB;
+        const int64_t ko = koff(min(kb + SP, nkb - 1));
         ldv(ra[p], pa + ko);
         ldv(rb0[p], p0 + ko);
         if (MODE == MODE_GATEUP) ldv(rb1[p], p1 + ko);
@@ -1507,13 +1537,17 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
     const int64_t grid = (a.max_chunks * n_wt + SW - 1) / SW;
     hipLaunchKernelGGL(grouped_stream_bf16<MODE>, dim3((unsigned)grid), dim3(SW * 64), 0, s, a, n_wt);
   } else if (dtype == MOE_BF16 && MODE == MODE_GATEUP && a.bm == kWideRows && rs_fits(a)) {
-    constexpr int BN = Ws<1>::BN;
-    const int n_tiles = (int)((a.N + BN / 2 - 1) / (BN / 2));
-    const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
-    if ((a.K / RBK - 1) % 2)
-      hipLaunchKernelGGL((grouped_gemm_wn<MODE, 1>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles);
-    else
-      hipLaunchKernelGGL((grouped_gemm_wn<MODE, 0>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles);
+    if constexpr (MODE == MODE_GATEUP) {  // (the down pass takes the 320-row kernel)
+      constexpr int BN = Ws<1>::BN;
+      const int n_tiles = (int)((a.N + BN / 2 - 1) / (BN / 2));
+      int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
+      if (MOE_WN_PERSIST) grid = std::min<int64_t>(grid, kNumCUs);
+      static_assert(kNumCUs % kXcds == 0, "persistent grid");
+      if ((a.K / RBK - 1) % 2)
+        hipLaunchKernelGGL((grouped_gemm_wn<MODE, 1>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles);
+      else
+        hipLaunchKernelGGL((grouped_gemm_wn<MODE, 0>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles);
+    }
   } else if (dtype == MOE_BF16 && a.bm == RBM && rs_fits(a)) {
     const int n_tiles = (int)(MODE == MODE_GATEUP ? (a.N + 127) / 128 : (a.N + RBN - 1) / RBN);
     const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
