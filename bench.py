@@ -80,24 +80,37 @@ def traffic_entry(kernel_ms):
     return t.get("hbm_bytes_per_launch")
 
 
-def timed_forward(moe, torch, cfg, dev, x, y, ws, route, steps, warmup):
-    """Warmup, then `steps` timed moe_forward calls with stage events; returns (seconds, stage ms lists,
-    whole-step ms list from the first to the last event of each step)."""
+STAGES = ["route", "dispatch", "gateup", "down", "combine"]
+ALL_MARKS = tuple(range(len(STAGES) + 1))
+GEMM_MARKS = (2, 3, 4)   # the gate/up and down passes' boundaries
+
+
+def timed_forward(moe, torch, cfg, dev, x, y, ws, route, steps, warmup, marks=ALL_MARKS):
+    """Warmup, then `steps` timed moe_forward calls; returns (seconds, stage ms lists, whole-step ms list).
+    Events are recorded on the layer's stream only at the stage boundaries in `marks` (0 = before routing,
+    2 = before gate/up, 3 = before down, 4 = before combine, 5 = after it): each recorded event holds the
+    next launch until the previous one has finished, which costs a few microseconds, so a run records only
+    the boundaries it reports.  Stage lists cover the stages whose two boundaries are both marked; the
+    whole-step list needs marks 0 and 5."""
+    marks = set(marks)
     for _ in range(warmup):
         moe.forward(cfg, dev, x, y, ws, route_out=route)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.STAGE_EVENTS)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) if j in marks else None for j in range(moe.STAGE_EVENTS)]
+           for _ in range(steps)]
     for row in evs:   # materialise the HIP events before they are handed to the library
         for e in row:
-            e.record()
+            if e is not None:
+                e.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        moe.forward(cfg, dev, x, y, ws, route_out=route, events=evs[i])
+        moe.forward(cfg, dev, x, y, ws, route_out=route, events=evs[i] if marks else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    names = ["route", "dispatch", "gateup", "down", "combine"]
-    stages = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)] for j, n in enumerate(names)}
-    per_step = [evs[i][0].elapsed_time(evs[i][len(names)]) for i in range(steps)]
+    stages = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]
+              for j, n in enumerate(STAGES) if j in marks and j + 1 in marks}
+    per_step = ([evs[i][0].elapsed_time(evs[i][len(STAGES)]) for i in range(steps)]
+                if 0 in marks and len(STAGES) in marks else [])
     return t1 - t0, stages, per_step
 
 
@@ -233,7 +246,8 @@ def variants(moe, torch, np, s, dev, x, y, ws, steps, warmup):
     cfgn = moe.config_from_shape(sn)
     route = {"scores": torch.empty((s.T, s.E), dtype=torch.float32, device="cuda"),
              "counts": torch.empty((s.E,), dtype=torch.int32, device="cuda")}
-    secs, st, _ = timed_forward(moe, torch, cfgn, devn, x, y, ws, route, steps, warmup)
+    secs, _, _ = timed_forward(moe, torch, cfgn, devn, x, y, ws, route, steps, warmup, marks=())
+    _, st, _ = timed_forward(moe, torch, cfgn, devn, x, y, ws, route, steps, 1, marks=(0, 1))
     res["noaux_tc"] = {"workload": sn.name, "ms_per_step": secs / steps * 1e3, "tokens_per_s": s.T * steps / secs,
                        "route_ms": float(np.mean(st["route"])), "n_group": sn.n_group, "topk_group": sn.topk_group,
                        "note": "step includes writing the [T, E] float32 scores"}
@@ -289,8 +303,9 @@ def layer_roofline(s, counts, R, ms_step, ms_gemm, esz):
 
 
 def other_workloads(moe, torch, np, names, steps, warmup):
-    """The other layer workloads at full size, each timed like the main one (stage
-    events in every step), with their place against both roofs."""
+    """The other layer workloads at full size, each timed without events (the
+    step time), then with events at every stage boundary (the stage times), with
+    their place against both roofs."""
     from synth import WORKLOADS, make_inputs
     from synth.device import bits, upload
     res = {}
@@ -304,7 +319,8 @@ def other_workloads(moe, torch, np, names, steps, warmup):
         ws = torch.empty(moe.workspace_size(cfg), dtype=torch.uint8, device="cuda")
         route = {"counts": torch.empty((s.E,), dtype=torch.int32, device="cuda"),
                  "offsets": torch.empty((s.E + 1,), dtype=torch.int32, device="cuda")}
-        secs, st, per_step = timed_forward(moe, torch, cfg, dev, dev["x"], y, ws, route, steps, warmup)
+        secs, _, _ = timed_forward(moe, torch, cfg, dev, dev["x"], y, ws, route, steps, warmup, marks=())
+        _, st, per_step = timed_forward(moe, torch, cfg, dev, dev["x"], y, ws, route, steps, 1)
         counts = bits(route["counts"])
         R = int(bits(route["offsets"])[-1])
         avg = {n: float(np.mean(v)) for n, v in st.items()}
@@ -317,8 +333,7 @@ def other_workloads(moe, torch, np, names, steps, warmup):
                                    "max": float(np.max(per_step))},
                 "dropped_assignments": int(s.T * s.k - R)}
         if esz == 2:
-            line["roofline"] = layer_roofline(s, counts, R, float(np.median(per_step)),
-                                              avg["gateup"] + avg["down"], esz)
+            line["roofline"] = layer_roofline(s, counts, R, ms, avg["gateup"] + avg["down"], esz)
         else:
             line["roofline"] = {"bound": "launch", "note": "correctness workload: a few microseconds of work "
                                                            "per stage, launch latency dominates"}
@@ -396,7 +411,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    secs, st, per_step = timed_forward(moe, torch, cfg, dev, x, y, ws, route, a.steps, a.warmup)
+    # the timed steps record only the GEMM passes' boundaries (the roofline's launch times); a second run
+    # with every stage boundary gives the stage breakdown
+    secs, st, _ = timed_forward(moe, torch, cfg, dev, x, y, ws, route, a.steps, a.warmup, marks=GEMM_MARKS)
+    _, st_all, per_step = timed_forward(moe, torch, cfg, dev, x, y, ws, route, a.steps, 1)
     ms_step = secs / a.steps * 1e3
     tokens_per_s = s.T * a.steps / secs
     print(f"[bench] {a.steps} steps in {secs:.3f} s", file=sys.stderr, flush=True)
@@ -450,9 +468,11 @@ def main():
         "roofline": roof,
         "grouped_gemm": {"tflops": gemm_tflops, "frac_mfma_peak": gemm_tflops / PEAK_BF16_TFLOPS,
                          "flops": fl_gateup + fl_down, "ms": avg["gateup"] + avg["down"]},
-        "stages_ms": avg,
+        "stages_ms": {n: float(np.mean(v)) for n, v in st_all.items()},
         "step_ms_events": {"median": float(np.median(per_step)), "min": float(np.min(per_step)),
-                           "max": float(np.max(per_step))},
+                           "max": float(np.max(per_step)),
+                           "note": "a separate run with an event at every stage boundary (stages_ms); the "
+                                   "events add a few microseconds each to the step"},
         "routing": {"kept_rows": R, "max_rows_per_expert": int(counts.max()), "min_rows_per_expert": int(counts.min())},
     }
 
@@ -467,7 +487,8 @@ def main():
         ws5 = torch.empty(moe.workspace_size(cfg5), dtype=torch.uint8, device="cuda")
         r5 = {"counts": torch.empty((s5.E,), dtype=torch.int32, device="cuda")}
         steps5 = max(a.steps, 20)
-        secs5, st5, _ = timed_forward(moe, torch, cfg5, dev5, dev5["x"], y5, ws5, r5, steps5, a.warmup)
+        secs5, _, _ = timed_forward(moe, torch, cfg5, dev5, dev5["x"], y5, ws5, r5, steps5, a.warmup, marks=())
+        _, st5, _ = timed_forward(moe, torch, cfg5, dev5, dev5["x"], y5, ws5, r5, steps5, 1)
         c5 = bits(r5["counts"])
         touched = int((c5 > 0).sum())
         per_expert = 3 * s5.H * s5.I * 2

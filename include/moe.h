@@ -239,7 +239,9 @@ moe_status moe_forward_noalloc(const moe_config *cfg, const moe_weights *w, cons
 /* moe_forward that also records `events` (an array of MOE_STAGE_EVENTS hipEvent_t
  * created by the caller, or NULL) on `stream` around its stages, for timing:
  * [0] before route, [1] after route, [2] after dispatch, [3] after gate/up,
- * [4] after down, [5] after combine. */
+ * [4] after down, [5] after combine.  A NULL entry is not recorded; each recorded
+ * event holds the next launch until the previous one has finished, so a caller
+ * timing the whole step records only the boundaries it needs. */
 #define MOE_STAGE_EVENTS 6
 moe_status moe_forward_timed(const moe_config *cfg, const moe_weights *w, const void *x,
                              void *y, moe_route_out *route_out, void *ws, size_t ws_bytes,

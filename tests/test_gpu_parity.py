@@ -204,6 +204,31 @@ def test_expert_ffn_stream_multichunk():
     check_rows(widen_out(yp)[:48], want, BF16, "stream multichunk")
 
 
+def test_expert_ffn_160_row_list_long_groups():
+    """A capacity of at most 160 rows and no shared expert cut the chunk list to 160 rows (the 160 x 512
+    gate/up tile).  moe_expert_ffn takes the caller's offsets, which may hold groups longer than the capacity:
+    they must be cut into several 160-row chunks (here 161, 400 and 480 rows next to 1, 159 and 160)."""
+    s = MoEShape("wide_long_groups", T=1024, H=256, I=320, E=6, k=2, capacity_factor=0.45, cfg_id=141)
+    cfg = moe.config_from_shape(s)
+    assert moe.capacity(cfg) <= 160
+    inp = make_inputs(s)
+    dev = upload(inp)
+    loads = np.array([161, 1, 400, 159, 480, 160], dtype=np.int64)
+    offsets = np.concatenate([[0], np.cumsum(loads)])
+    R = int(offsets[-1])
+    assert R <= s.T * s.k
+    rng = np.random.default_rng(11)
+    from synth import f32_to_bf16_bits
+    xp_host = f32_to_bf16_bits(rng.normal(size=(s.T * s.k, s.H)).astype(np.float32))
+    xp = to_torch(xp_host, "cuda")
+    off = torch.from_numpy(offsets.astype(np.int32)).cuda()
+    yp = torch.zeros((s.T * s.k, s.H), dtype=torch.bfloat16, device="cuda")
+    moe.expert_ffn(cfg, xp, off, dev["w_gate"], dev["w_up"], dev["w_down"], yp, workspace(cfg))
+    torch.cuda.synchronize()
+    want = ref.grouped_expert_ffn(xp_host[:R], offsets, inp.w_gate, inp.w_up, inp.w_down)
+    check_rows(widen_out(yp)[:R], want, BF16, "160-row list, long groups")
+
+
 @pytest.mark.parametrize("dtype", [BF16, F32])
 def test_combine_stage(dtype):
     rng = np.random.default_rng(5)
