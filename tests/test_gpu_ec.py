@@ -81,6 +81,9 @@ CASES = {
     # C = 300: every group, the shared one too, in the 320-row chunk list
     "bf16_C300": MoEShape("bf16_C300", T=1200, H=256, I=128, E=8, k=2, gate=GATE_SIGMOID, n_shared=1,
                           I_shared=128, cfg_id=407),
+    # C = 128 with no shared expert: one list of 160-row chunks, gate/up on the 160 x 512 tile
+    "bf16_C128_wide_tile": MoEShape("bf16_C128_wide_tile", T=2048, H=256, I=256, E=16, k=2, gate=GATE_SIGMOID,
+                                    capacity_factor=0.5, cfg_id=408),
     "deepseek_v3_ec_narrow_experts": MoEShape("deepseek_v3_ec_narrow_experts", T=8192, H=7168, I=64, E=256, k=8,
                                               gate=GATE_SIGMOID, routed_scaling_factor=2.5, n_shared=1,
                                               I_shared=64, cfg_id=405),
