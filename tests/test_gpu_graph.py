@@ -60,6 +60,22 @@ def test_forward_graph_replays(T):
                    [y, r["topk_idx"], r["topk_w"], r["counts"], r["row_of_slot"]])
 
 
+def test_forward_160_row_list_graph_replays():
+    """Capacity 128, no shared expert: the 160-row chunk list, whose gate/up kernel
+    (160 x 512 tile) is persistent, runs inside the graph."""
+    s = MoEShape("graph_cap128", T=4096, H=256, I=256, E=16, k=1, capacity_factor=0.5, logit_skew=True,
+                 renormalize=False, cfg_id=706)
+    inp = make_inputs(s)
+    dev = upload(inp)
+    cfg = moe.config_from_shape(s)
+    assert moe.capacity(cfg) <= 160
+    y = torch.empty((s.T, s.H), dtype=torch.bfloat16, device="cuda")
+    r = alloc_route(s)
+    ws = workspace(cfg)
+    replay_matches(lambda: moe.forward(cfg, dev, dev["x"], y, ws, route_out=r),
+                   [y, r["topk_idx"], r["topk_w"], r["counts"], r["row_of_slot"]])
+
+
 def test_forward_two_lists_graph_replays():
     """Loads around 512 rows per expert: both chunk lists of each GEMM pass hold
     work (the 256-row and the 320-row kernel both run inside the graph)."""

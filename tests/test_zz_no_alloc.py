@@ -60,6 +60,12 @@ PAIRS = {
                 MoEShape("na_prefill_300", T=300, H=256, I=320, E=8, k=2, gate=GATE_SIGMOID,
                          routed_scaling_factor=2.5, n_shared=1, I_shared=320, capacity_factor=0.9, cfg_id=704,
                          weight_cfg_id=703)),
+    # capacity at most 160 rows and no shared expert: the one 160-row chunk list
+    # (gate/up on the 160 x 512 tile); capacities 128, then 32
+    "capacity_160_list": (MoEShape("na_cap_4096", T=4096, H=256, I=256, E=16, k=1, capacity_factor=0.5,
+                                   logit_skew=True, renormalize=False, cfg_id=706),
+                          MoEShape("na_cap_1000", T=1000, H=256, I=256, E=16, k=1, capacity_factor=0.5,
+                                   logit_skew=True, renormalize=False, cfg_id=707, weight_cfg_id=706)),
 }
 
 
