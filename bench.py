@@ -114,6 +114,17 @@ def timed_forward(moe, torch, cfg, dev, x, y, ws, route, steps, warmup, marks=AL
     return t1 - t0, stages, per_step
 
 
+def copy_calibration(torch, mib):
+    """One plain device copy of `mib` MiB (none for 0): the reference of known size for the byte counters."""
+    if mib <= 0:
+        return
+    src = torch.ones(mib * 2 ** 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def event_ms(torch, fn, steps, warmup):
     """Mean milliseconds of fn() over `steps` calls, timed with events on the current stream."""
     for _ in range(warmup):
@@ -382,6 +393,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.lib()
     if a.workload is not None and a.workload != DS_PREFILL:
+        copy_calibration(torch, a.copy_calibration_mib)
         print(json.dumps({"workload_only": other_workloads(moe, torch, np, [a.workload], a.steps, a.warmup)}))
         return
     s = WORKLOADS[DS_PREFILL]
@@ -403,13 +415,7 @@ def main():
              "row_of_slot": torch.empty((s.T, s.k), dtype=torch.int32, device="cuda"),
              "token_of_row": torch.empty((s.T * s.k,), dtype=torch.int32, device="cuda")}
 
-    if a.copy_calibration_mib > 0:
-        n = a.copy_calibration_mib * 2 ** 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(torch, a.copy_calibration_mib)
 
     # the timed steps record only the GEMM passes' boundaries (the roofline's launch times); a second run
     # with every stage boundary gives the stage breakdown
