@@ -140,7 +140,7 @@ def event_ms(torch, fn, steps, warmup):
 
 
 def achievable(moe, torch):
-    """Peaks this box reaches on plain work, next to the published ones: a 2 GiB
+    """Peaks this GPU reaches on plain work, next to the published ones: a 2 GiB
     device copy (torch copy_: read + write bytes), the library's MFMA-only
     calibration kernel (bf16 MFMAs on register operands, no memory traffic), and a
     dense bf16 GEMM of the gate/up shape with every token on one expert
