@@ -1293,9 +1293,10 @@ __global__ __launch_bounds__(WNT) void grouped_gemm_ws(GemmArgs a, int n_tiles) 
 #define MOE_WN_PERSIST 1
 #endif
 // The 160 x 512 tile's K loops are short (capacity-limited layers have narrow
-// H), so a workgroup's dispatch and set-up are a large share of a tile: one
-// workgroup per CU walks the tiles p = blockIdx.x, + gridDim.x, ... (gridDim.x
-// a multiple of the XCD count, so each workgroup keeps to its XCD's tiles).
+// H), so a tile's start-up weighs more than in the long-K tiles: one workgroup
+// per CU walks the tiles p = blockIdx.x, + gridDim.x, ... (gridDim.x a
+// multiple of the XCD count, so each workgroup keeps to its XCD's tiles), which
+// saves the workgroup launches (about 1% of the Switch-style gate/up pass).
 template <int MODE, int R>
 __global__ __launch_bounds__(WNT) void grouped_gemm_wn(GemmArgs a, int n_tiles) {
   if constexpr (MOE_WN_PERSIST) {
