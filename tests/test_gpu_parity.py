@@ -56,6 +56,11 @@ SMALL = {
                                        renormalize=False, capacity_factor=1.25, logit_skew=True, cfg_id=117),
     "bf16_capacity_128_k2": MoEShape("bf16_capacity_128_k2", T=1024, H=384, I=192, E=24, k=2,
                                      capacity_factor=1.5, cfg_id=118),
+    # many small routed groups (list A) and a shared expert of 1100 rows (four
+    # 275-row chunks of list B): the down pass spans enough tiles to run both
+    # lists in one launch
+    "bf16_down_one_launch": MoEShape("bf16_down_one_launch", T=1100, H=1024, I=256, E=512, k=8, gate=GATE_SIGMOID,
+                                     routed_scaling_factor=2.5, n_shared=1, I_shared=256, cfg_id=119),
     "fp32_tiny": WORKLOADS[TINY],
     "fp32_sigmoid_shared_capacity": MoEShape("fp32_sigmoid_shared_capacity", T=200, H=192, I=128, E=8, k=3,
                                              gate=GATE_SIGMOID, capacity_factor=1.0, n_shared=1, I_shared=128,

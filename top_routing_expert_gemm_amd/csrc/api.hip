@@ -145,6 +145,24 @@ hipError_t each_list(GemmArgs g, const ChunkPlan& p, Chunk* chunks, int32_t* nch
   return launch(g);
 }
 
+// The down pass (bf16 or fp32 weights) over the chunk lists of plan p: both
+// lists in one launch where the 320-row kernel takes the pass, else each list
+// on its own launch.
+hipError_t down_lists(GemmArgs g, const ChunkPlan& p, Chunk* chunks, int32_t* nch, int dtype, hipStream_t s) {
+  if (p.cut.bm_b != 0) {
+    GemmArgs b = g;
+    b.chunks = chunks;
+    b.n_chunks = nch;
+    b.chunks_b = chunks + p.cut.off_b;
+    b.n_chunks_b = nch + 1;
+    b.max_chunks = p.max_a + p.max_b;
+    b.bm = kGemmBMdl;
+    hipError_t e = hipSuccess;
+    if (launch_down_both(b, dtype, s, e)) return e;
+  }
+  return each_list(g, p, chunks, nch, [&](const GemmArgs& a) { return launch_down(a, dtype, s); });
+}
+
 }  // namespace
 
 extern "C" {
@@ -307,7 +325,7 @@ moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t
   g.K = c->I;
   g.N = c->H;
   g.out = y_perm;
-  HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) { return launch_down(a, c->dtype, s); }));
+  HIP_TRY(down_lists(g, L.plan, chunks, nch, c->dtype, s));
   return MOE_OK;
 }
 
@@ -450,9 +468,10 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
   g.a_rows = L.rows;
   g.out = at(ws, L.y_perm);
   g.nt_out = (int64_t)L.rows * c->H * (int64_t)esize(c) > kLastLevelCacheBytes;
-  HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) {
-    return q == nullptr ? launch_down(a, c->dtype, s) : launch_down_fp8(a, s);
-  }));
+  if (q == nullptr)
+    HIP_TRY(down_lists(g, L.plan, chunks, nch, c->dtype, s));
+  else
+    HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) { return launch_down_fp8(a, s); }));
   HIP_TRY(mark(4));
   const void* ysh = c->n_shared ? static_cast<const void*>(at(ws, L.y_perm + (size_t)Tk * c->H * esize(c))) : nullptr;
   HIP_TRY(launch_combine(at(ws, L.y_perm), r.row_of_slot, r.topk_w, ysh, y, c->T, c->H, c->k, c->dtype, s));
@@ -649,7 +668,7 @@ moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void*
   g.a_rows = L.rows;
   g.out = at(ws, L.y_perm);
   g.nt_out = (int64_t)L.rows * c->H * (int64_t)esize(c) > kLastLevelCacheBytes;
-  HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) { return launch_down(a, c->dtype, s); }));
+  HIP_TRY(down_lists(g, L.plan, chunks, nch, c->dtype, s));
   const void* ysh = c->n_shared ? static_cast<const void*>(at(ws, L.y_perm + (size_t)R * c->H * esize(c))) : nullptr;
   // weight of a chosen pair: its gate score times routed_scaling_factor
   HIP_TRY(launch_combine(at(ws, L.y_perm), o.row_of_pair, o.scores, ysh, y, c->T, c->H, c->E, c->dtype, s,

@@ -189,6 +189,10 @@ struct GemmArgs {
   int64_t shared_row0;      // first row of the shared group in the row space (gather mode)
   const Chunk* chunks;
   const int32_t* n_chunks;  // device count of valid chunks
+  // A second chunk list run in the same launch after the first (the down pass
+  // over both lists), or NULL; max_chunks then bounds both lists together.
+  const Chunk* chunks_b = nullptr;
+  const int32_t* n_chunks_b = nullptr;
   int64_t max_chunks;       // grid bound
   const void* w0;           // gate (gate/up pass) or down weights, [E, N, K]
   const void* w1;           // up weights (gate/up pass)
@@ -217,6 +221,11 @@ struct GemmArgs {
 constexpr int64_t kLastLevelCacheBytes = int64_t(256) << 20;
 hipError_t launch_gateup(const GemmArgs& a, int dtype, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, int dtype, hipStream_t s);
+// The down pass over both chunk lists in one launch of the 320-row kernel
+// (a.chunks / a.n_chunks, then a.chunks_b / a.n_chunks_b; a.max_chunks bounds
+// both).  False, with nothing launched, where that kernel does not take the
+// pass (then each list is launched on its own).
+bool launch_down_both(const GemmArgs& a, int dtype, hipStream_t s, hipError_t& err);
 
 // FP8 (E4M3) weights, bf16 activations, batches of <= kGemvMaxT tokens.
 constexpr int kFp8Block = 128;

@@ -1250,14 +1250,23 @@ __device__ __forceinline__ void ws_run(const GemmArgs& a, const Chunk& ch, int n
   }
 }
 
-template <int MODE, int V, int R>
+// Tile p of a launch over one chunk list, or (TWO) over both: list A's tiles,
+// then list B's.  The down pass runs both lists on this kernel; as one launch
+// it ends on one partly filled round of tiles instead of one per list.
+template <int MODE, int V, int R, bool TWO = false>
 __device__ __forceinline__ void ws_tile(const GemmArgs& a, int n_tiles, int p) {
-  const int nv = *a.n_chunks * n_tiles;
+  const int nva = *a.n_chunks * n_tiles;
+  const int nv = TWO ? nva + *a.n_chunks_b * n_tiles : nva;
   int L;
   if (!xcd_map_cyclic(p, nv, SUPER * n_tiles, L)) return;
+  const Chunk* list = a.chunks;
+  if (TWO && L >= nva) {
+    list = a.chunks_b;
+    L -= nva;
+  }
   int ci, nt;
-  tile_of(L, n_tiles, a.chunks, ci, nt);
-  const Chunk ch = a.chunks[ci];
+  tile_of(L, n_tiles, list, ci, nt);
+  const Chunk ch = list[ci];
   if constexpr (V == 0) {
     switch ((ch.nrows + 31) / 32) {
       case 1: ws_run<V, MODE, 1, R>(a, ch, nt); break;
@@ -1288,6 +1297,10 @@ __device__ __forceinline__ void ws_tile(const GemmArgs& a, int n_tiles, int p) {
 template <int MODE, int R>
 __global__ __launch_bounds__(WNT) void grouped_gemm_ws(GemmArgs a, int n_tiles) {
   ws_tile<MODE, 0, R>(a, n_tiles, blockIdx.x);
+}
+template <int R>
+__global__ __launch_bounds__(WNT) void grouped_gemm_ws2(GemmArgs a, int n_tiles) {
+  ws_tile<MODE_DOWN, 0, R, true>(a, n_tiles, blockIdx.x);
 }
 #ifndef MOE_WN_PERSIST
 #define MOE_WN_PERSIST 1
@@ -1596,6 +1609,34 @@ hipError_t launch_down(const GemmArgs& a, int dtype, hipStream_t s) {
     return launch_gemm<MODE_DOWN>(b, dtype, s);
   }
   return launch_gemm<MODE_DOWN>(a, dtype, s);
+}
+
+#ifndef MOE_DOWN_ONE_LAUNCH
+#define MOE_DOWN_ONE_LAUNCH 1
+#endif
+// One launch pays where a pass spans many rounds of tiles over the CUs: two
+// launches end on two partly filled rounds (the DeepSeek-V3-shaped down pass:
+// 13.6 + 17.3 rounds, 2.27 -> 2.23 ms as one launch).  A pass of a round or two
+// per list keeps each launch's tiles in step, so that the n-tiles of a chunk
+// share its token rows in L2; merged, the second round starts staggered (the
+// Mixtral-shaped down pass, one round per list: 0.825 -> 0.85 ms).  The host
+// bound on the tile count decides.
+constexpr int64_t kOneLaunchMinRounds = 8;
+bool launch_down_both(const GemmArgs& a, int dtype, hipStream_t s, hipError_t& err) {
+  if (!(MOE_DOWN_ONE_LAUNCH && MOE_DOWN_ON_WS && MOE_GEMM_WS && dtype == MOE_BF16 && a.chunks_b != nullptr &&
+        rs_fits(a)))
+    return false;
+  constexpr int BN = Ws<0>::BN;
+  const int n_tiles = (int)((a.N + BN - 1) / BN);
+  if (a.max_chunks * n_tiles < kOneLaunchMinRounds * kNumCUs) return false;
+  const int64_t grid = ((a.max_chunks * n_tiles + kXcds - 1) / kXcds) * kXcds;
+  switch ((a.K / RBK - 2) % 3) {
+    case 0: hipLaunchKernelGGL((grouped_gemm_ws2<0>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles); break;
+    case 1: hipLaunchKernelGGL((grouped_gemm_ws2<1>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles); break;
+    default: hipLaunchKernelGGL((grouped_gemm_ws2<2>), dim3((unsigned)grid), dim3(WNT), 0, s, a, n_tiles); break;
+  }
+  err = hipGetLastError();
+  return true;
 }
 
 }  // namespace moe
