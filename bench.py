@@ -285,6 +285,43 @@ def variants(moe, torch, np, s, dev, x, y, ws, steps, warmup):
     return res
 
 
+def gateup_roofline(s, counts, R, ms_gateup, ms_down, traffic):
+    """The gate/up stage (the dominant kernel work) against both published roofs.
+
+    flops: 2 (R + shared rows) H 2I.  Algorithmic bytes: the touched experts' gate
+    and up weights once, x once, h written once.  Its intensity below the ridge
+    (2.5 PFLOP/s over 8 TB/s) puts it on the HBM side, and achieved / peak / frac
+    are then in GB/s against 8 TB/s; the MFMA side is kept beside it, and the
+    down pass's rate after it."""
+    rows = R + s.T * s.n_shared
+    fl_gateup = 2.0 * rows * s.H * 2 * s.I
+    fl_down = 2.0 * rows * s.I * s.H
+    touched = int((counts > 0).sum()) + s.n_shared
+    by_gateup = float(touched * 2 * s.I * s.H * 2 + s.T * s.H * 2 + rows * s.I * 2)
+    gateup_tflops = fl_gateup / (ms_gateup * 1e-3) / 1e12
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    gateup_gbps = by_gateup / (ms_gateup * 1e-3) / 1e9
+    intensity = fl_gateup / by_gateup
+    hbm_bound = intensity < ridge
+    return {"bound": "hbm" if hbm_bound else "mfma",
+            "kernel": "gate/up+SwiGLU grouped GEMM stage: grouped_gemm_rs<0> (256-row chunk list) + "
+                      "grouped_gemm_ws<0> (320-row chunk list), one launch each",
+            "achieved": gateup_gbps if hbm_bound else gateup_tflops,
+            "peak": PEAK_HBM_GBPS if hbm_bound else PEAK_BF16_TFLOPS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": gateup_gbps / PEAK_HBM_GBPS if hbm_bound else gateup_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "avg_launch_ms": ms_gateup,
+            "intensity_flop_per_byte": intensity, "ridge_flop_per_byte": ridge,
+            "mfma_side": {"flops_per_launch": fl_gateup, "achieved_TFLOPs": gateup_tflops,
+                          "frac_mfma_peak": gateup_tflops / PEAK_BF16_TFLOPS},
+            "hbm_side": {"algorithmic_bytes_per_launch": by_gateup, "achieved_GBps": gateup_gbps,
+                         "frac_hbm_peak": gateup_gbps / PEAK_HBM_GBPS},
+            "down_pass": {"flops_per_launch": fl_down, "avg_launch_ms": ms_down,
+                          "achieved_TFLOPs": fl_down / (ms_down * 1e-3) / 1e12,
+                          "frac_mfma_peak": fl_down / (ms_down * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
+
+
 def layer_roofline(s, counts, R, ms_step, ms_gemm, esz):
     """Algorithmic work of one layer step and where it sits against both published roofs.
 
@@ -427,41 +464,13 @@ def main():
 
     counts = bits(route["counts"])
     R = int(bits(route["offsets"])[-1])
-    rows = R + s.T * s.n_shared
-    fl_gateup = 2.0 * rows * s.H * 2 * s.I
-    fl_down = 2.0 * rows * s.I * s.H
-    # algorithmic bytes of the gate/up stage: the touched experts' gate and up
-    # weights once, x once, h written once
-    touched = int((counts > 0).sum()) + s.n_shared
-    by_gateup = float(touched * 2 * s.I * s.H * 2 + s.T * s.H * 2 + rows * s.I * 2)
     avg = {n: float(np.mean(v)) for n, v in st.items()}
-    gateup_tflops = fl_gateup / (avg["gateup"] * 1e-3) / 1e12
+    roof = gateup_roofline(s, counts, R, avg["gateup"], avg["down"], traffic_entry(avg["gateup"]))
+    gateup_tflops = roof["mfma_side"]["achieved_TFLOPs"]
+    traffic = roof["traffic"]
+    fl_gateup = roof["mfma_side"]["flops_per_launch"]
+    fl_down = roof["down_pass"]["flops_per_launch"]
     gemm_tflops = (fl_gateup + fl_down) / ((avg["gateup"] + avg["down"]) * 1e-3) / 1e12
-    traffic = traffic_entry(avg["gateup"])
-    # the gate/up stage against both published roofs: its intensity (flops over its
-    # algorithmic bytes) below the ridge puts it on the HBM side, and frac is then
-    # the HBM fraction; the MFMA fraction is kept beside it
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
-    gateup_gbps = by_gateup / (avg["gateup"] * 1e-3) / 1e9
-    intensity = fl_gateup / by_gateup
-    hbm_bound = intensity < ridge
-    roof = {"bound": "hbm" if hbm_bound else "mfma",
-            "kernel": "gate/up+SwiGLU grouped GEMM stage: grouped_gemm_rs<0> (256-row chunk list) + "
-                      "grouped_gemm_ws<0> (320-row chunk list), one launch each",
-            "achieved": gateup_gbps if hbm_bound else gateup_tflops,
-            "peak": PEAK_HBM_GBPS if hbm_bound else PEAK_BF16_TFLOPS,
-            "unit": "GB/s" if hbm_bound else "TFLOP/s",
-            "frac": gateup_gbps / PEAK_HBM_GBPS if hbm_bound else gateup_tflops / PEAK_BF16_TFLOPS,
-            "traffic": traffic,
-            "avg_launch_ms": avg["gateup"],
-            "intensity_flop_per_byte": intensity, "ridge_flop_per_byte": ridge,
-            "mfma_side": {"flops_per_launch": fl_gateup, "achieved_TFLOPs": gateup_tflops,
-                          "frac_mfma_peak": gateup_tflops / PEAK_BF16_TFLOPS},
-            "hbm_side": {"algorithmic_bytes_per_launch": by_gateup, "achieved_GBps": gateup_gbps,
-                         "frac_hbm_peak": gateup_gbps / PEAK_HBM_GBPS},
-            "down_pass": {"flops_per_launch": fl_down, "avg_launch_ms": avg["down"],
-                          "achieved_TFLOPs": fl_down / (avg["down"] * 1e-3) / 1e12,
-                          "frac_mfma_peak": fl_down / (avg["down"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}}
 
     out = {
         "metric": "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), DeepSeek-V3 shape",

@@ -65,3 +65,36 @@ def test_shared_expert_and_untouched_experts_are_counted():
     assert r["algorithmic_bytes"] == by
     assert r["grouped_gemm_flops"] == 2 * rows * 3 * 128 * 256
     assert r["touched_experts"] == 2
+
+
+def test_gateup_stage_of_the_deepseek_v3_prefill_is_hbm_bound():
+    # T 8192, H 7168, I 2048, E 256, top-8, one shared expert; all 65536 routed rows kept, every expert touched
+    s = shape(8192, 7168, 2048, 256, 8, 1)
+    counts = np.full(256, 256)
+    r = bench.gateup_roofline(s, counts, 65536, ms_gateup=4.0, ms_down=2.0, traffic=None)
+    rows = 65536 + 8192                                   # 73,728
+    fl = 2 * rows * 7168 * 2 * 2048                       # 4,329,327,034,368
+    weights = 257 * 2 * 2048 * 7168 * 2                   # gate and up of 257 experts: 15,091,105,792
+    by = weights + 8192 * 7168 * 2 + rows * 2048 * 2      # + x once + h written once
+    assert by == 15_510_536_192
+    assert r["mfma_side"]["flops_per_launch"] == fl == 4_329_327_034_368
+    assert r["hbm_side"]["algorithmic_bytes_per_launch"] == by
+    assert r["intensity_flop_per_byte"] == pytest.approx(279.12, abs=0.01)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert r["achieved"] == pytest.approx(by / 4.0e-3 / 1e9)
+    assert r["frac"] == pytest.approx(r["achieved"] / 8000.0)
+    assert r["mfma_side"]["achieved_TFLOPs"] == pytest.approx(fl / 4.0e-3 / 1e12)
+    assert r["down_pass"]["flops_per_launch"] == 2 * rows * 2048 * 7168
+    assert r["down_pass"]["frac_mfma_peak"] == pytest.approx(2 * rows * 2048 * 7168 / 2.0e-3 / 1e12 / 2500.0)
+    assert r["traffic"] is None
+
+
+def test_gateup_stage_above_the_ridge_is_priced_against_mfma():
+    # Mixtral-shaped: 8192 rows over 8 experts, I 14336 -> far above the ridge
+    s = shape(4096, 4096, 14336, 8, 2, 0)
+    r = bench.gateup_roofline(s, np.full(8, 1024), 8192, ms_gateup=1.0, ms_down=0.5, traffic=123.0)
+    fl = 2 * 8192 * 4096 * 2 * 14336
+    assert r["intensity_flop_per_byte"] > 312.5
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+    assert r["frac"] == pytest.approx(fl / 1.0e-3 / 1e12 / 2500.0)
+    assert r["traffic"] == 123.0
