@@ -1327,38 +1327,54 @@ __global__ __launch_bounds__(WNT) void grouped_gemm_wn(GemmArgs a, int n_tiles) 
 // Small batches (decode): every expert group has at most 16 rows, so the work is
 // streaming each touched expert's weights once.  One wave owns 16 output columns
 // (16 weight rows; gate/up: 16 gate + the same 16 up rows) of one chunk and runs
-// v_mfma_f32_16x16x32_bf16 with the token rows padded to 16.  No LDS and no
-// barriers: each lane streams 32 contiguous bytes of its weight row per 64-wide
-// K block straight into registers, with SP blocks in flight, so many waves per
-// CU keep a deep queue of HBM reads.  The token rows (A) are tiny and cached.
-#ifndef MOE_STREAM_SKB
-#define MOE_STREAM_SKB 64
-#endif
+// v_mfma_f32_16x16x32_bf16 with the token rows padded to 16.  No barriers: the
+// waves never share data.
+//
+// Weight loads: a large buffer read with the non-temporal hint streams at about
+// 7.1 TB/s on this device against 6.2-6.3 TB/s without it, but only when every
+// load instruction covers whole 128-byte lines; the MFMA operand layout (a lane
+// holds 16 bytes of one of 16 rows, four lanes per row per instruction) covers
+// half lines, and half-line non-temporal reads fall to about 5 TB/s.  So each
+// lane loads one 16-byte piece of a whole line (eight lanes per row, eight rows
+// per instruction, two instructions per 16 rows of a 64-wide K block), SP
+// blocks in flight in registers; a block is then written to the wave's own LDS
+// rows and read back in the operand layout.  The 16-byte slots of each 128-byte
+// LDS row are XOR-swizzled by row / 2, so both the stores and the operand reads
+// of any 16 lanes fall on 64 distinct banks.  The token rows (A) are tiny and
+// cached: plain loads, straight into the operand layout.
 #ifndef MOE_STREAM_SP
 #define MOE_STREAM_SP 4
 #endif
-// Down pass: wave gw takes its K blocks from block gw * ROT (mod K / SKB) on.
+// Down pass: wave gw takes its K blocks from block gw * ROT (mod K / 64) on.
 // Its weight rows are I = 2048 elements, 4 KB apart, and the waves, all in
 // step, would otherwise read the same offset of every 4 KB row at once;
-// starting each wave one block further spreads them (decode down pass 538 ->
-// 504 us).  The gate/up rows (H = 7168, 14 KB) stream faster in step (992
-// against 1027 us rotated), so that pass is left as it is.
+// starting each wave one block further spreads them.  The gate/up rows (H =
+// 7168, 14 KB) stream faster in step, so that pass is left as it is.
 #ifndef MOE_STREAM_ROT
 #define MOE_STREAM_ROT 1
 #endif
+#ifndef MOE_STREAM_NT
+#define MOE_STREAM_NT 1
+#endif
 constexpr int SW = 4;                 // waves per workgroup
-constexpr int SKB = MOE_STREAM_SKB;   // K per block (SKB / 32 MFMA substeps)
+constexpr int SKB = 64;               // K per block: one 128-byte line of a weight row
 constexpr int SP = MOE_STREAM_SP;     // K blocks in flight per wave
-constexpr int NV = SKB / 32;          // 16-byte loads per lane per matrix per block
-static_assert(SKB == 64 || SKB == 128, "SKB");
 
-__device__ __forceinline__ void ldv(uint4 (&r)[NV], const uint16_t* p) {
-#pragma unroll
-  for (int i = 0; i < NV; ++i) r[i] = *reinterpret_cast<const uint4*>(p + 8 * i);
+// One 16-byte piece of a weight line, read once.
+__device__ __forceinline__ uint4 ldw(const uint16_t* p) {
+  if (MOE_STREAM_NT) {
+    const v4u32 v = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  return *reinterpret_cast<const uint4*>(p);
 }
+// LDS slot of 16-byte piece c of staged row r (16 rows x 8 slots per matrix).
+__device__ __forceinline__ int stream_slot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 template <int MODE>
 __global__ __launch_bounds__(SW * 64) void grouped_stream_bf16(GemmArgs a, int n_wt) {
+  constexpr int M = MODE == MODE_GATEUP ? 2 : 1;  // weight matrices per block
+  __shared__ uint4 stage[SW][M][16 * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int V = *a.n_chunks * n_wt;
   const int gw = blockIdx.x * SW + wave;
@@ -1369,76 +1385,82 @@ __global__ __launch_bounds__(SW * 64) void grouped_stream_bf16(GemmArgs a, int n
   const int64_t K = a.K, N = a.N;
   const int r16 = lane & 15, g4 = lane >> 4;
 
-  // A: token row r16 of the chunk (clamped); lane group g4 covers k = (SKB/4) g4 .. + SKB/4 of each block
+  // A: token row r16 of the chunk (clamped); substep s takes k = 32 s + 8 g4 .. + 8 of each block
   const int rc = min(r16, ch.nrows - 1);
   const int64_t row = (int64_t)ch.row0 + rc;
   int64_t src = row;
   if (a.gather != nullptr) src = shared ? row - a.shared_row0 : (int64_t)a.gather[row];
-  const uint16_t* pa = static_cast<const uint16_t*>(a.A) + src * K + g4 * (SKB / 4);
-  // B: weight row n = 16 nt + r16 (N is a multiple of 64)
+  const uint16_t* pa = static_cast<const uint16_t*>(a.A) + src * K + 8 * g4;
+  // B: load i (0, 1) of a block takes row 16 nt + 8 i + (lane >> 3), piece lane & 7 (N is a multiple of 64)
+  const int brow = lane >> 3, bpc = lane & 7;
   const int64_t goff = shared ? 0 : (int64_t)ch.group * N * K;
-  const int64_t n = (int64_t)nt * 16 + r16;
-  const uint16_t* p0 = static_cast<const uint16_t*>(shared ? a.ws0 : a.w0) + goff + n * K + g4 * (SKB / 4);
-  const uint16_t* p1 = MODE == MODE_GATEUP
-                           ? static_cast<const uint16_t*>(shared ? a.ws1 : a.w1) + goff + n * K + g4 * (SKB / 4)
-                           : p0;
+  const int64_t n = (int64_t)nt * 16 + brow;
+  const uint16_t* pb[M];
+  pb[0] = static_cast<const uint16_t*>(shared ? a.ws0 : a.w0) + goff + n * K + 8 * bpc;
+  if constexpr (M == 2) pb[1] = static_cast<const uint16_t*>(shared ? a.ws1 : a.w1) + goff + n * K + 8 * bpc;
 
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const int nkb = (int)(K / SKB);  // K is a multiple of 64; a 64-wide tail block is handled below
+  f32x4 acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nkb = (int)(K / SKB);  // K is a multiple of 64
   const int rot = (MODE == MODE_DOWN && nkb > 0) ? (int)(((int64_t)gw * MOE_STREAM_ROT) % nkb) : 0;
   auto koff = [&](int b) {  // K offset of the wave's b-th block: the blocks taken from block rot on, wrapping
     int r = b + rot;
     r -= r >= nkb ? nkb : 0;
     return (int64_t)r * SKB;
   };
-  uint4 ra[SP][NV], rb0[SP][NV], rb1[SP][NV];
-  if (nkb > 0) {  // (a K shorter than one block has only the tail below)
+  uint4 ra[SP][2], rb[SP][M][2];
+  auto load = [&](int p, int b) {
+    const int64_t ko = koff(b);
 #pragma unroll
-  for (int p = 0; p < SP; ++p) {
-    const int64_t ko = koff(min(p, nkb - 1));
-    ldv(ra[p], pa + ko);
-    ldv(rb0[p], p0 + ko);
-    if (MODE == MODE_GATEUP) ldv(rb1[p], p1 + ko);
-  }
-  for (int kb0 = 0; kb0 < nkb; kb0 += SP) {
+    for (int s2 = 0; s2 < 2; ++s2) ra[p][s2] = *reinterpret_cast<const uint4*>(pa + ko + 32 * s2);
 #pragma unroll
-    for (int p = 0; p < SP; ++p) {
-      const int kb = kb0 + p;
-      if (kb < nkb) {
-        // substep s: lane group g4 supplies k = (SKB/4) g4 + 8 s .. +8 of this block, for A and B alike
+    for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int s2 = 0; s2 < NV; ++s2) {
-          const bf16x8 av = __builtin_bit_cast(bf16x8, ra[p][s2]);
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, rb0[p][s2]), acc0, 0, 0, 0);
-          if (MODE == MODE_GATEUP)
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, rb1[p][s2]), acc1, 0, 0, 0);
-        }
-        const int64_t ko = koff(min(kb + SP, nkb - 1));
-        ldv(ra[p], pa + ko);
-        ldv(rb0[p], p0 + ko);
-        if (MODE == MODE_GATEUP) ldv(rb1[p], p1 + ko);
+      for (int i = 0; i < 2; ++i) rb[p][m][i] = ldw(pb[m] + 8 * i * K + ko);
+  };
+  // store slots of this lane's two pieces, read slots of its two operand pieces
+  const int wslot0 = stream_slot(brow, bpc), wslot1 = stream_slot(8 + brow, bpc);
+  const int rslot0 = stream_slot(r16, g4), rslot1 = stream_slot(r16, 4 + g4);
+  // One block: stage its weight lines, read them back as operands, multiply.
+  // Blocks past the end (K / 64 not a multiple of SP) multiply a zero A operand.
+  auto block = [&](int p, int kb) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      stage[wave][m][wslot0] = rb[p][m][0];
+      stage[wave][m][wslot1] = rb[p][m][1];
+    }
+    const bool live = kb < nkb;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint4 a4 = live ? ra[p][s2] : make_uint4(0u, 0u, 0u, 0u);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a4);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint4 bv = stage[wave][m][s2 ? rslot1 : rslot0];
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bv), acc[m], 0, 0, 0);
       }
     }
-  }
-  }
-  if constexpr (SKB == 128) {
-    if (K % SKB != 0) {  // one 64-wide tail block: lane group g4 takes k = 16 g4 .. +16 of it
-      const int64_t kt = (int64_t)nkb * SKB;
-      const uint16_t* ta = pa - g4 * (SKB / 4) + kt + g4 * 16;
-      const uint16_t* t0 = p0 - g4 * (SKB / 4) + kt + g4 * 16;
-      const uint16_t* t1 = p1 - g4 * (SKB / 4) + kt + g4 * 16;
+  };
+  if (nkb > 0) {
+    // SP blocks in flight: the steady loop refills each register set as soon
+    // as its block is used, unconditionally (so the compiler's wait counts are
+    // exact); the last SP blocks issue no loads.
+    const int last = (nkb - 1) / SP * SP;  // first block of the last round
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ta + 8 * s2));
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            av, __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(t0 + 8 * s2)), acc0, 0, 0, 0);
-        if (MODE == MODE_GATEUP)
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              av, __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(t1 + 8 * s2)), acc1, 0, 0, 0);
+    for (int p = 0; p < SP; ++p) load(p, min(p, nkb - 1));
+    for (int kb0 = 0; kb0 < last; kb0 += SP) {
+#pragma unroll
+      for (int p = 0; p < SP; ++p) {
+        block(p, kb0 + p);
+        load(p, min(kb0 + p + SP, nkb - 1));
       }
     }
+#pragma unroll
+    for (int p = 0; p < SP; ++p) block(p, last + p);
   }
   // lane holds output column 16 nt + r16 for token rows 4 g4 + q
+  const int64_t ncol = (int64_t)nt * 16 + r16;
   uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -1446,9 +1468,9 @@ __global__ __launch_bounds__(SW * 64) void grouped_stream_bf16(GemmArgs a, int n
     if (rr >= ch.nrows) continue;
     const int64_t orow = (int64_t)ch.row0 + rr;
     if (MODE == MODE_GATEUP)
-      out[orow * N + n] = f32_to_bf16(silu_f(acc0[q]) * acc1[q]);
+      out[orow * N + ncol] = f32_to_bf16(silu_f(acc[0][q]) * acc[M - 1][q]);
     else
-      out[orow * N + n] = f32_to_bf16(acc0[q]);
+      out[orow * N + ncol] = f32_to_bf16(acc[0][q]);
   }
 }
 
