@@ -99,10 +99,10 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T* __restrict__
 #define MOE_FP8_FP 2
 #endif
 #ifndef MOE_FP8_NCG_GU
-#define MOE_FP8_NCG_GU 2
+#define MOE_FP8_NCG_GU 1
 #endif
 #ifndef MOE_FP8_NCG_DN
-#define MOE_FP8_NCG_DN 4
+#define MOE_FP8_NCG_DN 2
 #endif
 constexpr int FW = MOE_FP8_FW;  // waves per workgroup
 constexpr int FP = MOE_FP8_FP;  // K blocks in flight per wave
