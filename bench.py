@@ -141,7 +141,8 @@ def event_ms(torch, fn, steps, warmup):
 
 def achievable(moe, torch):
     """Peaks this GPU reaches on plain work, next to the published ones: a 2 GiB
-    device copy (torch copy_: read + write bytes), the library's MFMA-only
+    device copy (torch copy_: read + write bytes), the library's read-only stream
+    over 8 GiB (non-temporal whole-line loads), the library's MFMA-only
     calibration kernel (bf16 MFMAs on register operands, no memory traffic), and a
     dense bf16 GEMM of the gate/up shape with every token on one expert
     (torch.matmul -> hipBLASLt)."""
@@ -182,7 +183,8 @@ def achievable(moe, torch):
             "dense_bf16_gemm_TFLOPs": 2.0 * m * kk * nn / (ms_mm * 1e-3) / 1e12,
             "dense_gemm_shape": [m, kk, nn],
             "note": "copy counts bytes read + written; the read stream is moe_hbm_read_peak over 8 GiB (4096 "
-                    "workgroups, 32 KiB blocks, loads of the next block issued before the current one is used); "
+                    "workgroups, 32 KiB blocks, non-temporal 16-byte loads, those of the next block issued before the current "
+                    "one is used); "
                     "the MFMA loop is moe_mfma_peak (v_mfma_f32_32x32x16_bf16 "
                     "on registers, 2048 workgroups x 4 waves x 4 chains), with one fixed operand pair or with eight "
                     "hashed pairs in turn (varied: inputs toggle as on real data); GEMM is torch.matmul "

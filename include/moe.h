@@ -335,7 +335,8 @@ moe_status moe_mfma_peak(int64_t iters, int32_t varied, float *sink, int64_t *fl
 /* The rate at which the device reads HBM with no arithmetic to speak of: one
  * launch of 4096 workgroups reads `bytes` of buf (device) once, as 32 KiB
  * blocks, block b by workgroup b mod 4096, each block one contiguous sweep of
- * 16-byte loads.  sink (device, uint32, 4096 entries) receives in entry w the
+ * 16-byte non-temporal loads (the fastest read pattern measured: every wave
+ * load whole 128-byte lines, not kept in the caches).  sink (device, uint32, 4096 entries) receives in entry w the
  * XOR of every 32-bit word of the blocks w, w + 4096, w + 8192, ... (0 when
  * there are none), so the loads cannot be dropped and the result can be
  * checked.  The caller times the launch (events on `stream`); the buffer
