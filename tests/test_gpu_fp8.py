@@ -126,6 +126,10 @@ CASES = {
     "fp8_decode_T5_softmax": MoEShape("fp8_decode_T5_softmax", T=5, H=384, I=128, E=8, k=3, cfg_id=602),
     "fp8_decode_T1": MoEShape("fp8_decode_T1", T=1, H=256, I=256, E=4, k=2, gate=GATE_SIGMOID, n_shared=1,
                               I_shared=256, cfg_id=603),
+    # two 128-wide K blocks in flight: H / 128 = 5 and I / 128 = 3 run the steady loop and then a last
+    # round with one padded block past K
+    "fp8_decode_T16_ragged_k": MoEShape("fp8_decode_T16_ragged_k", T=16, H=640, I=384, E=16, k=4,
+                                        gate=GATE_SIGMOID, n_shared=1, I_shared=384, cfg_id=606),
 }
 
 

@@ -77,6 +77,11 @@ SMALL = {
                                        gate=GATE_SIGMOID, routed_scaling_factor=2.5, n_shared=1, I_shared=256,
                                        cfg_id=111),
     "bf16_decode_T5_softmax": MoEShape("bf16_decode_T5_softmax", T=5, H=192, I=64, E=8, k=3, cfg_id=112),
+    # the streaming kernels keep four 64-wide K blocks in flight: H / 64 = 9 and I / 64 = 6 run the
+    # steady loop and then a last round with padded blocks past K (H = 192, I = 64 above are shorter
+    # than one round)
+    "bf16_decode_T16_ragged_k": MoEShape("bf16_decode_T16_ragged_k", T=16, H=576, I=384, E=16, k=4,
+                                         gate=GATE_SIGMOID, n_shared=1, I_shared=384, cfg_id=125),
 }
 
 
