@@ -11,14 +11,16 @@
 //   E4M3 code nearest to the float32 quotient w / scale, ties to the even code
 //   (a software encoder with exactly that rounding; |w / scale| <= 448 up to
 //   one rounding, saturated).
-// * grouped_stream_fp8: the bf16 decode kernel's layout with weights read as
-//   bytes.  One wave owns NCG groups of 16 output columns of one chunk; per
-//   128-wide K block a lane streams 32 contiguous code bytes of each of its
-//   weight rows, converts them exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8 with
-//   scale 1) and runs four v_mfma_f32_16x16x32_bf16 into a block partial, which
-//   is added to the result times the block's scale.  The token rows' fragments
-//   are loaded once per block for all NCG groups.  Half the HBM bytes of bf16
-//   weights per token.
+// * grouped_stream_fp8: the bf16 decode kernel's scheme with weights read as
+//   bytes.  One wave owns NCG groups of 16 output columns of one chunk; each
+//   128-wide K block of a code row is one 128-byte line, loaded whole
+//   (non-temporal, eight lanes per row) and passed through the wave's own LDS
+//   rows; from there a lane takes 32 code bytes of its operand row, converts
+//   them exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8 with scale 1) and runs
+//   four v_mfma_f32_16x16x32_bf16 into a block partial, which is added to the
+//   result times the block's scale.  The token rows' fragments are loaded once
+//   per block for all NCG groups.  Half the HBM bytes of bf16 weights per
+//   token.
 #include "common.h"
 
 namespace moe {

@@ -24,8 +24,12 @@
 //   grouped_gemm_bf16 320 x 256 tile, eight waves, both operands straight to
 //                     LDS (the 320-row list where the others' 32-bit offsets do
 //                     not fit or K < 128);
-//   grouped_stream_bf16  batches of <= 16 tokens: weights streamed into
-//                     registers, no LDS (decode);
+//   grouped_gemm_wn   160 x 512 tile, eight waves, one persistent workgroup
+//                     per CU (gate/up of lists whose chunks hold <= 160 rows);
+//   grouped_stream_bf16  batches of <= 16 tokens: each wave streams 16 weight
+//                     rows in whole 128-byte lines (non-temporal loads) and
+//                     turns them into MFMA operands through its own LDS rows,
+//                     no barriers (decode);
 //   grouped_gemm_f32  fp32 SIMT tiles.
 // In every bf16 tile kernel a wave owns matching gate and up columns in the
 // gate/up pass, so each lane holds gate and up of the same (row, i) and applies
