@@ -285,139 +285,329 @@ hipError_t launch_route_f32(const moe_config& c, const void* x, const void* w, c
 // not used).  The select step (dispatch.hip) adds the slices in slice order, so
 // the sums are reproducible.
 
-// Large batches, E <= 256: one workgroup = 256 tokens x all experts over one
-// slice of H.  Four waves, one per SIMD; wave w computes tokens 64 w .. + 64 (two
-// 32-row blocks) against every 32-expert block (NB of them), so the whole tile's
-// 256 x 32 NB accumulators live in the workgroup's registers.  Both operand
-// tiles go through LDS (double buffered, 128-byte rows, 16-byte chunks
-// XOR-swizzled by row): every thread fetches the next K step's 16-byte pieces
-// into registers while the current step is multiplied, then stores them; one
-// barrier per step.  Per step the workgroup moves 32 KB of token rows and
-// 4 NB KB of router weights for 256 x 32 NB x 64 multiply-adds: a 256-token
-// tile reads the router weights once per 256 tokens, twice fewer times than
-// 128-token tiles.
-constexpr int kGT = 256;     // tokens per workgroup
-constexpr int kGThreads = 256;
+// Large batches, E <= 256: one workgroup = 128 tokens x all experts over one
+// slice of H.  128-token tiles take half the K slices that 256-token tiles
+// would need to cover the chip, which halves the float32 partial logits
+// written here and read back by the select step (at 8192 tokens, 256 experts:
+// 34 MB in 4 slices instead of 67 MB in 8).
+//
+// Eight waves, two per SIMD, in two roles:
+//   * four MFMA waves in a 2 x 2 grid (4 x 1 when the experts fit one 32-wide
+//     block): a wave multiplies 64 tokens (two 32-row blocks) by half of the
+//     32-expert blocks, so the tile's 128 x 32 NB accumulators live in their
+//     registers.  They load the router weights (a few MB, served by L2)
+//     straight to LDS, two K steps ahead, each wave load one 1 KB block of
+//     eight rows with the swizzle applied on the source side.
+//   * four loader waves stream the token rows (read once, from HBM) into
+//     kLoadSets register sets, kLoadSets - 1 K steps ahead, and store each
+//     step's rows to LDS one step before it is used.
+// The token-row stream needs many bytes in flight per CU to run at HBM speed,
+// and a wave's vector-memory counter completes in issue order: in one wave,
+// each step's wait for its weights would also wait for every older token-row
+// load.  Split over two kinds of waves, the weight waits of the MFMA waves
+// leave the loader waves' deep queue alone.
+// LDS: three buffers of token rows (16 KB) and of weights (32 NB KB), 128-byte
+// rows, 16-byte chunks XOR-swizzled by row.  Each 64-wide step is four 16-wide
+// substeps; the MFMA waves read the next substep's operands between the current
+// substep's MFMAs (two operand register sets).  One barrier per step, which
+// both roles reach: it sits before the last substep's MFMAs, when every MFMA
+// wave has finished reading the step's buffers, and after the loader waves
+// have stored the next step's rows.  Loads past the slice are clamped to its
+// last step (issued, never used), so every step issues the same loads and
+// every wait is an exact count.
+typedef uint32_t rv4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void rlds_void;
+constexpr int kGT = 128;                   // tokens per workgroup
+constexpr int kGThreads = 512;             // four MFMA waves, then four loader waves
+constexpr int kGNA = kGT * 8 / 256;        // token-row pieces per loader lane per step (4)
+constexpr int kLoadSets = 6;               // loader register sets (token rows of 6 K steps)
+constexpr int kRBufFlags = 0x00020000;     // raw buffer resource word 3 (gfx9 family)
+
+__shared__ __attribute__((aligned(1024))) rv4 gA0[kGT * 8];
+__shared__ __attribute__((aligned(1024))) rv4 gA1[kGT * 8];
+__shared__ __attribute__((aligned(1024))) rv4 gA2[kGT * 8];
+__shared__ __attribute__((aligned(1024))) rv4 gB0[256 * 8];
+__shared__ __attribute__((aligned(1024))) rv4 gB1[256 * 8];
+__shared__ __attribute__((aligned(1024))) rv4 gB2[256 * 8];
+template <int U>
+__device__ __forceinline__ rv4* g_a() {
+  if constexpr (U == 0) return gA0;
+  else if constexpr (U == 1) return gA1;
+  else return gA2;
+}
+template <int U>
+__device__ __forceinline__ rv4* g_b() {
+  if constexpr (U == 0) return gB0;
+  else if constexpr (U == 1) return gB1;
+  else return gB2;
+}
+
+// Wave grid of a tile with NB 32-expert blocks: WT x WN MFMA waves, each RB
+// token blocks of 32 rows x NBW expert blocks.
+template <int NB>
+struct RgShape {
+  static constexpr int WN = NB >= 2 ? 2 : 1;
+  static constexpr int WT = 4 / WN;
+  static constexpr int RB = kGT / WT / 32;
+  static constexpr int NBW = NB / WN;
+  static_assert(WT * RB * 32 == kGT && WN * NBW == NB, "wave grid");
+};
 
 template <int NB>
-__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void route_gemm_kernel(
+struct RgOps {
+  bf16x8 a[RgShape<NB>::RB];
+  bf16x8 b[RgShape<NB>::NBW];
+};
+
+// Sized for the largest expert tile (entries a smaller tile does not use are
+// never touched, so they cost no registers).
+struct RgCtx {
+  __amdgpu_buffer_rsrc_t rx;   // token rows of this tile (base: its first row)
+  __amdgpu_buffer_rsrc_t rw;   // router weights
+  uint32_t aoff[kGNA];         // loader lane: byte offset of token-row piece i at k = 0
+  int aslot[kGNA];             // loader lane: LDS slot of token-row piece i
+  uint32_t boff[8];            // MFMA lane: byte offset of this wave's weight block j at k = 0
+  int ra[4], rb[4];            // MFMA lane: LDS slot of its first A / B operand row, per substep
+  int wave;                    // wave index within its role
+};
+
+// Wait until at most N vector-memory loads of this wave are outstanding (the
+// LDS and export counters are not waited on).
+template <int N>
+__device__ __forceinline__ void rg_wait_vm() {
+  static_assert(N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// Wait for all but N vector-memory loads and for every LDS operation of this
+// wave, then barrier.
+template <int N>
+__device__ __forceinline__ void rg_barrier() {
+  static_assert(N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---- loader waves ----
+__device__ __forceinline__ void rg_load_rows(rv4 (&r)[kGNA], const RgCtx& c, int kt) {
+#pragma unroll
+  for (int i = 0; i < kGNA; ++i) {
+    r[i] = __builtin_amdgcn_raw_buffer_load_b128(c.rx, c.aoff[i], kt * (kRBK * 2), 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+template <int U>
+__device__ __forceinline__ void rg_store_rows(const rv4 (&r)[kGNA], const RgCtx& c) {
+#pragma unroll
+  for (int i = 0; i < kGNA; ++i) g_a<U>()[c.aslot[i]] = r[i];
+}
+// Loader step R of the unrolled loop (relative step r = R mod kLoadSets): the
+// rows of step r + 1 (set (R + 1) mod kLoadSets, complete once at most the
+// (kLoadSets - 1) kGNA loads issued after them are outstanding) go to token
+// buffer (r + 1) mod 3, which was last read in step r - 2; the set is refilled
+// with step r + 1 + kLoadSets; barrier.
+template <int R>
+__device__ __forceinline__ void rg_loader_step(rv4 (&set)[kLoadSets][kGNA], const RgCtx& c, int t, int kl) {
+  constexpr int J = (R + 1) % kLoadSets;
+  rg_wait_vm<(kLoadSets - 1) * kGNA>();
+  rg_store_rows<(R + 1) % 3>(set[J], c);
+  __builtin_amdgcn_sched_barrier(0);
+  rg_load_rows(set[J], c, min(t + 1 + kLoadSets, kl));
+  rg_barrier<(kLoadSets - 1) * kGNA + kGNA>();
+}
+// The first n (< kLoadSets) loader steps of an unrolled group, for the steps left after the loop.
+template <int R>
+__device__ __forceinline__ void rg_loader_tail(rv4 (&set)[kLoadSets][kGNA], const RgCtx& c, int t, int kl, int n) {
+  if constexpr (R < kLoadSets) {
+    if (R < n) {
+      rg_loader_step<R>(set, c, t + R, kl);
+      rg_loader_tail<R + 1>(set, c, t, kl, n);
+    }
+  }
+}
+
+// ---- MFMA waves ----
+template <int NB, int U>
+__device__ __forceinline__ void rg_load_b(const RgCtx& c, int kt, int j) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rw, (rlds_void*)(g_b<U>() + (c.wave * NB + j) * 64), 16, c.boff[j],
+                                           kt * (kRBK * 2), 0, 0);
+}
+// Operand q of substep s from buffers U: q < RB the token blocks, then the expert blocks.
+template <int NB, int U>
+__device__ __forceinline__ void rg_read(RgOps<NB>& o, const RgCtx& c, int s, int q) {
+  constexpr int RB = RgShape<NB>::RB;
+  if (q < RB) o.a[q] = __builtin_bit_cast(bf16x8, g_a<U>()[c.ra[s] + q * 256]);
+  else o.b[q - RB] = __builtin_bit_cast(bf16x8, g_b<U>()[c.rb[s] + (q - RB) * 256]);
+}
+
+// Substep SS of the step in buffers U:
+//   SS 0: weights of step t + 2 into weight buffer (U + 2) mod 3 (last read in
+//         step t - 1), spread between the MFMAs;
+//   SS 3: barrier (the weights of step t + 1 are in: only the NB loads of SS 0
+//         may be outstanding; the loader waves have stored its token rows),
+//         then the MFMAs with the first operand reads of step t + 1.
+template <int NB, int U, int SS>
+__device__ __forceinline__ void rg_substep(f32x16 (&acc)[RgShape<NB>::RB][RgShape<NB>::NBW], RgOps<NB> (&op)[2],
+                                           const RgCtx& c, int t, int kl) {
+  constexpr int RB = RgShape<NB>::RB;
+  constexpr int NQ = RB + RgShape<NB>::NBW;          // operand reads per substep
+  constexpr int NM = RB * RgShape<NB>::NBW;          // MFMAs per substep
+  constexpr int NS = SS == 0 ? NB : 0;               // weight loads
+  constexpr int RU = SS == 3 ? (U + 1) % 3 : U;      // buffers of the next substep's operands
+  const int sn = (SS + 1) & 3;
+  RgOps<NB>& cur = op[SS & 1];
+  RgOps<NB>& nxt = op[(SS & 1) ^ 1];
+  if constexpr (SS == 3) rg_barrier<NB>();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const int n = m / RB, j = m % RB;
+    acc[j][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[j], cur.b[n], acc[j][n], 0, 0, 0);
+#pragma unroll
+    for (int q = m * NS / NM; q < (m + 1) * NS / NM; ++q) {
+      rg_load_b<NB, (U + 2) % 3>(c, min(t + 2, kl), q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = m * NQ / NM; q < (m + 1) * NQ / NM; ++q) rg_read<NB, RU>(nxt, c, sn, q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int NB, int U>
+__device__ __forceinline__ void rg_step(f32x16 (&acc)[RgShape<NB>::RB][RgShape<NB>::NBW], RgOps<NB> (&op)[2],
+                                        const RgCtx& c, int t, int kl) {
+  rg_substep<NB, U, 0>(acc, op, c, t, kl);
+  rg_substep<NB, U, 1>(acc, op, c, t, kl);
+  rg_substep<NB, U, 2>(acc, op, c, t, kl);
+  rg_substep<NB, U, 3>(acc, op, c, t, kl);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void route_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int T, int H, int E, int steps_per_split,
     float* __restrict__ part) {
-  constexpr int EB = NB * 32;              // experts of the tile
-  constexpr int NA = kGT * 8 / kGThreads;  // 16-byte A pieces per thread per step (8)
-  constexpr int NBL = EB * 8 / kGThreads;  // B pieces per thread per step (NB)
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kGT * kRBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][EB * kRBK];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  static_assert(NB * 32 <= 256, "expert tile");
+  using SH = RgShape<NB>;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int t0 = blockIdx.x * kGT;
   const int ks = blockIdx.y;
   const int nk = H / kRBK;
   const int kb = ks * steps_per_split, ke = min(kb + steps_per_split, nk);
+  const int kl = ke - 1;
   const int Epad = (E + 31) / 32 * 32;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // loader: thread -> row tid / 8 + 32 i, 16-byte chunk tid % 8 (stored at its swizzled slot)
-  const int lr = tid >> 3, lc = tid & 7;
-  const uint16_t* ap[NA];
-  const uint16_t* bp[NBL];
-  int aslot[NA], bslot[NBL];
+  RgCtx c;
+  c.wave = wid & 3;
+  if (wid >= 4) {
+    // loader wave l: pieces i = token rows 32 l + 8 i + lane / 8, logical chunk lane % 8
+    c.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + (int64_t)t0 * H), (short)0, -1, kRBufFlags);
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int r = lr + 32 * i;
-    ap[i] = x + (int64_t)min(t0 + r, T - 1) * H + lc * 8;
-    aslot[i] = r * kRBK + ((lc ^ rswz(r)) * 8);
-  }
-#pragma unroll
-  for (int i = 0; i < NBL; ++i) {
-    const int r = lr + 32 * i;
-    bp[i] = w + (int64_t)min(r, E - 1) * H + lc * 8;
-    bslot[i] = r * kRBK + ((lc ^ rswz(r)) * 8);
-  }
-
-  f32x16 acc[2][NB];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int n = 0; n < NB; ++n)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[j][n][v] = 0.f;
-
-  // two register sets: set P holds K step kt + 2 (issued during step kt), set
-  // 1 - P step kt + 1 (issued during the previous step), stored to LDS at the
-  // end of step kt; refills past the slice are clamped to its last step (loaded,
-  // never used), so every step issues the same loads and the wait before each
-  // store is an exact count
-  uint4 ra[2][NA], rbv[2][NBL];
-  auto load = [&](int set, int kt) {
-    const int kc = min(kt, ke - 1) * kRBK;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) ra[set][i] = ldg16(ap[i] + kc);
-#pragma unroll
-    for (int i = 0; i < NBL; ++i) rbv[set][i] = ldg16(bp[i] + kc);
-  };
-  auto store = [&](int set, int buf) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) *reinterpret_cast<uint4*>(&sA[buf][aslot[i]]) = ra[set][i];
-#pragma unroll
-    for (int i = 0; i < NBL; ++i) *reinterpret_cast<uint4*>(&sB[buf][bslot[i]]) = rbv[set][i];
-  };
-  const int l32 = lane & 31, h = lane >> 5;
-  auto compute = [&](int buf) {
-    const uint16_t* A = sA[buf];
-    const uint16_t* B = sB[buf];
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      // substep s2, lane half h: k = 32 h + 8 s2 .. + 8 of the step, for A and B alike
-      const int c = h * 4 + s2;
-      bf16x8 av[2], bv[NB];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wave * 64 + j * 32 + l32;
-        av[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(A + r * kRBK + ((c ^ rswz(r)) * 8)));
-      }
-#pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const int r = n * 32 + l32;
-        bv[n] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(B + r * kRBK + ((c ^ rswz(r)) * 8)));
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int n = 0; n < NB; ++n) acc[j][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], bv[n], acc[j][n], 0, 0, 0);
+    for (int i = 0; i < kGNA; ++i) {
+      const int row = 32 * c.wave + 8 * i + (lane >> 3), ch = lane & 7;
+      c.aoff[i] = (uint32_t)(((min(t0 + row, T - 1) - t0) * H + ch * 8) * 2);
+      c.aslot[i] = row * 8 + (ch ^ rswz(row));
     }
-  };
-  load(0, kb);
-  load(1, kb + 1);
-  store(0, 0);
-  __syncthreads();
-  int kt = kb;
-  for (; kt + 1 < ke; kt += 2) {  // the fences keep each refill issued before the step's MFMAs
-    load(0, kt + 2);
+    rv4 set[kLoadSets][kGNA];
+#pragma unroll
+    for (int s = 0; s < kLoadSets; ++s) rg_load_rows(set[s], c, min(kb + s, kl));
+    rg_wait_vm<(kLoadSets - 1) * kGNA>();
+    rg_store_rows<0>(set[0], c);
     __builtin_amdgcn_sched_barrier(0);
-    compute(0);
-    store(1, 1);
-    __syncthreads();
-    load(1, kt + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1);
-    store(0, 0);
-    __syncthreads();
+    rg_load_rows(set[0], c, min(kb + kLoadSets, kl));
+    rg_barrier<kLoadSets * kGNA>();
+    int t = kb;
+    static_assert(kLoadSets == 6 && kLoadSets % 3 == 0, "the unrolled loop below");
+    for (; t + 6 <= ke; t += 6) {
+      rg_loader_step<0>(set, c, t, kl);
+      rg_loader_step<1>(set, c, t + 1, kl);
+      rg_loader_step<2>(set, c, t + 2, kl);
+      rg_loader_step<3>(set, c, t + 3, kl);
+      rg_loader_step<4>(set, c, t + 4, kl);
+      rg_loader_step<5>(set, c, t + 5, kl);
+    }
+    rg_loader_tail<0>(set, c, t, kl, ke - t);
+    rg_wait_vm<0>();
+    return;
   }
-  if (kt < ke) compute(0);
 
-  // lane holds expert column l32 of each block and token rows 8 g + 4 h + q
-  float* out = part + (int64_t)ks * T * Epad;
+  // MFMA wave (tw, ew): token rows tw * 32 RB .., expert blocks ew * NBW ..;
+  // weight loads: wave load j fills rows 8 (wave NB + j) .. + 8; lane -> row +
+  // lane / 8, physical slot lane % 8, loaded from the logical chunk that belongs there
+  c.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(w), (short)0, -1, kRBufFlags);
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NB; ++j) {
+    const int r = 8 * (c.wave * NB + j) + (lane >> 3);
+    const int ch = (lane & 7) ^ rswz(r);
+    c.boff[j] = (uint32_t)((min(r, E - 1) * H + ch * 8) * 2);
+  }
+  const int tw = c.wave % SH::WT, ew = c.wave / SH::WT;
+  const int l32 = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const int e = n * 32 + l32;
-      if (e >= Epad) continue;
+  for (int s = 0; s < 4; ++s) {
+    // lane -> row l32 of each 32-row block, logical chunk 4 h + s in substep s
+    const int cs = (4 * h + s) ^ rswz(l32);
+    c.ra[s] = (tw * SH::RB * 32 + l32) * 8 + cs;
+    c.rb[s] = (ew * SH::NBW * 32 + l32) * 8 + cs;
+  }
+
+  f32x16 acc[SH::RB][SH::NBW];
+#pragma unroll
+  for (int j = 0; j < SH::RB; ++j)
+#pragma unroll
+    for (int m = 0; m < SH::NBW; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][m][v] = 0.f;
+
+  RgOps<NB> op[2];
+  // prologue: weights of steps kb and kb + 1 into buffers 0 and 1
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    rg_load_b<NB, 0>(c, kb, j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    rg_load_b<NB, 1>(c, min(kb + 1, kl), j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  rg_barrier<NB>();
+#pragma unroll
+  for (int q = 0; q < SH::RB + SH::NBW; ++q) rg_read<NB, 0>(op[0], c, 0, q);
+
+  int t = kb;
+  for (; t + 3 <= ke; t += 3) {
+    rg_step<NB, 0>(acc, op, c, t, kl);
+    rg_step<NB, 1>(acc, op, c, t + 1, kl);
+    rg_step<NB, 2>(acc, op, c, t + 2, kl);
+  }
+  if (t < ke) rg_step<NB, 0>(acc, op, c, t, kl);
+  if (t + 1 < ke) rg_step<NB, 1>(acc, op, c, t + 1, kl);
+  // the clamped weight loads of the last steps may still be writing LDS
+  rg_wait_vm<0>();
+
+  // lane holds expert column l32 of each block and token rows 8 g + 4 h + q.
+  // Buffer stores over this slice's [T, Epad] partials: the resource's size
+  // ends at row T, so the hardware drops the stores of rows past the batch.
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(part + (int64_t)ks * T * Epad, (short)0,
+                                                                      T * Epad * 4, kRBufFlags);
+#pragma unroll
+  for (int j = 0; j < SH::RB; ++j)
+#pragma unroll
+    for (int m = 0; m < SH::NBW; ++m) {
+      const int e0 = (ew * SH::NBW + m) * 32;
+      if (e0 >= Epad) continue;  // the tile's blocks past E + padding
+      const uint32_t o = (uint32_t)(((t0 + (tw * SH::RB + j) * 32 + 4 * h) * Epad + e0 + l32) * 4);
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int t = t0 + wave * 64 + j * 32 + 8 * g + 4 * h + q;
-          if (t < T) out[(int64_t)t * Epad + e] = acc[j][n][4 * g + q];
+          // the element is read into a scalar first: a bit cast of the vector-element expression itself
+          // compiled to element 0 for every (g, q)
+          const float v = acc[j][m][4 * g + q];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ro, o + (uint32_t)((8 * g + q) * Epad * 4), 0, 0);
         }
     }
 }
@@ -516,7 +706,7 @@ RoutePlan route_plan(const moe_config& c) {
     return p;
   }
   if (c.E <= 256) {
-    // one 256-token workgroup per CU in all, each slice at least four K steps long
+    // one 128-token workgroup per CU in all, each slice at least four K steps long
     p.kind = RK_GEMM;
     const int64_t mt = (c.T + kGT - 1) / kGT;
     int64_t ns = (256 + mt - 1) / mt;
