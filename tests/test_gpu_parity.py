@@ -61,6 +61,15 @@ SMALL = {
     # lists in one launch
     "bf16_down_one_launch": MoEShape("bf16_down_one_launch", T=1100, H=1024, I=256, E=512, k=8, gate=GATE_SIGMOID,
                                      routed_scaling_factor=2.5, n_shared=1, I_shared=256, cfg_id=119),
+    # the split-K router of batches above 16 tokens (128-token tiles; loader waves hold six K steps of
+    # token rows in flight, the MFMA waves two of router weights): 100 experts (four 32-expert blocks, the
+    # last padded to 128 columns), a ragged last token tile and one slice of 7 K steps (the loaders'
+    # unrolled loop once, then a one-step tail); 200 experts (eight blocks, the last one wholly past the
+    # padded width of 224 and not stored) over five slices of 5, 5, 5, 5 and 1 K steps
+    "bf16_router_E100": MoEShape("bf16_router_E100", T=1037, H=448, I=64, E=100, k=6, gate=GATE_SIGMOID,
+                                 routed_scaling_factor=2.5, cfg_id=126),
+    "bf16_router_E200_slices": MoEShape("bf16_router_E200_slices", T=4100, H=1344, I=64, E=200, k=8,
+                                        cfg_id=127),
     "fp32_tiny": WORKLOADS[TINY],
     "fp32_sigmoid_shared_capacity": MoEShape("fp32_sigmoid_shared_capacity", T=200, H=192, I=128, E=8, k=3,
                                              gate=GATE_SIGMOID, capacity_factor=1.0, n_shared=1, I_shared=128,
