@@ -50,7 +50,7 @@ Layout layout(const moe_config* c) {
   L.dscratch = take(dispatch_scratch_bytes(c->T, c->k, c->E));
   L.rscratch = take(route_scratch_bytes(*c));
   L.chunks = take((size_t)(L.plan.max_a + L.plan.max_b) * sizeof(Chunk));
-  L.n_chunks = take(8);
+  L.n_chunks = take(16);  // list sizes: gate/up A, B; down A, B
   L.h = take((size_t)L.rows * c->I * esize(c));
   L.y_perm = take((size_t)L.rows * c->H * esize(c));
   L.total = off;
@@ -91,7 +91,7 @@ LayoutEC layout_ec(const moe_config* c) {
   L.token_of_row = take((size_t)R * 4);
   L.row_of_pair = take((size_t)c->T * c->E * 4);
   L.chunks = take((size_t)(L.plan.max_a + L.plan.max_b) * sizeof(Chunk));
-  L.n_chunks = take(8);
+  L.n_chunks = take(16);  // list sizes: gate/up A, B; down A, B
   L.h = take((size_t)L.rows * c->I * esize(c));
   L.y_perm = take((size_t)L.rows * c->H * esize(c));
   L.total = off;
@@ -145,7 +145,8 @@ hipError_t each_list(GemmArgs g, const ChunkPlan& p, Chunk* chunks, int32_t* nch
   return launch(g);
 }
 
-// The down pass (bf16 or fp32 weights) over the chunk lists of plan p: both
+// The down pass (bf16 or fp32 weights) over the chunk lists of plan p (nch:
+// the down pass's two list sizes, which place the shared group's chunks): both
 // lists in one launch where the 320-row kernel takes the pass, else each list
 // on its own launch.
 hipError_t down_lists(GemmArgs g, const ChunkPlan& p, Chunk* chunks, int32_t* nch, int dtype, hipStream_t s) {
@@ -325,7 +326,7 @@ moe_status moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t
   g.K = c->I;
   g.N = c->H;
   g.out = y_perm;
-  HIP_TRY(down_lists(g, L.plan, chunks, nch, c->dtype, s));
+  HIP_TRY(down_lists(g, L.plan, chunks, nch + 2, c->dtype, s));
   return MOE_OK;
 }
 
@@ -469,9 +470,9 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
   g.out = at(ws, L.y_perm);
   g.nt_out = (int64_t)L.rows * c->H * (int64_t)esize(c) > kLastLevelCacheBytes;
   if (q == nullptr)
-    HIP_TRY(down_lists(g, L.plan, chunks, nch, c->dtype, s));
+    HIP_TRY(down_lists(g, L.plan, chunks, nch + 2, c->dtype, s));
   else
-    HIP_TRY(each_list(g, L.plan, chunks, nch, [&](const GemmArgs& a) { return launch_down_fp8(a, s); }));
+    HIP_TRY(each_list(g, L.plan, chunks, nch + 2, [&](const GemmArgs& a) { return launch_down_fp8(a, s); }));
   HIP_TRY(mark(4));
   const void* ysh = c->n_shared ? static_cast<const void*>(at(ws, L.y_perm + (size_t)Tk * c->H * esize(c))) : nullptr;
   HIP_TRY(launch_combine(at(ws, L.y_perm), r.row_of_slot, r.topk_w, ysh, y, c->T, c->H, c->k, c->dtype, s));
@@ -668,7 +669,7 @@ moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void*
   g.a_rows = L.rows;
   g.out = at(ws, L.y_perm);
   g.nt_out = (int64_t)L.rows * c->H * (int64_t)esize(c) > kLastLevelCacheBytes;
-  HIP_TRY(down_lists(g, L.plan, chunks, nch, c->dtype, s));
+  HIP_TRY(down_lists(g, L.plan, chunks, nch + 2, c->dtype, s));
   const void* ysh = c->n_shared ? static_cast<const void*>(at(ws, L.y_perm + (size_t)R * c->H * esize(c))) : nullptr;
   // weight of a chosen pair: its gate score times routed_scaling_factor
   HIP_TRY(launch_combine(at(ws, L.y_perm), o.row_of_pair, o.scores, ysh, y, c->T, c->H, c->E, c->dtype, s,

@@ -168,7 +168,9 @@ hipError_t launch_route_dispatch(const moe_config& c, const void* x, const void*
 
 // Histogram + scan + capacity + row maps; also writes the chunk lists of the
 // routed groups (and the shared group when shared_rows > 0, starting at
-// shared_row0 in the row space); n_chunks[0..1] receive the list sizes.
+// shared_row0 in the row space); n_chunks[0..1] receive the list sizes of the
+// gate/up pass, n_chunks[2..3] those of the down pass (the shared group's chunks
+// can sit in a different list in each).
 hipError_t launch_dispatch(int64_t T, int64_t k, int64_t E, int64_t cap, const int32_t* topk_idx,
                            int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
                            int32_t* token_of_row, void* scratch, Chunk* chunks, int32_t* n_chunks,

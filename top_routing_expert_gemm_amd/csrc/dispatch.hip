@@ -160,27 +160,39 @@ __device__ void emit_chunks(int e_valid, int load, int row0, int E, const ChunkC
     total_b = incl_b;
   }
   __syncthreads();
-  // the shared group follows its own cost, except that it never makes list B
-  // on its own: a launch of only its few chunks would leave most CUs idle
-  const bool sh_a = takes_list_a(shared_rows, cut) || total_b == 0;
-  const int64_t sbm = sh_a ? cut.bm_a : cut.bm_b;
-  const int nsh = (int)((shared_rows + sbm - 1) / sbm);
-  const int sbase = sh_a ? total_a : total_b;
-  Chunk* slist = sh_a ? chunks : chunks + cut.off_b;
-  for (int c = tid; c < nsh; c += kScanThreads) {
-    const int64_t r0 = c * shared_rows / nsh, r1 = (c + 1) * shared_rows / nsh;
-    Chunk ck;
-    ck.group = E;
-    ck.row0 = (int)(shared_row0 + r0);
-    ck.nrows = (int)(r1 - r0);
-    ck.gfirst = sbase;
-    ck.gcount = nsh;
-    ck.pad[0] = ck.pad[1] = ck.pad[2] = 0;
-    slist[sbase + c] = ck;
-  }
+  // The shared group.  Its chunks share one weight tile per n-tile, which the
+  // tile order streams once per group of chunks, so the 320-row list's fewer
+  // weight streams buy it little: the gate/up pass takes it as chunks of list A
+  // (the 256-row kernel has the higher rate per row).  The down pass (the
+  // 320-row kernel over both lists) takes it as fewer, taller chunks of list B.
+  // Both sets of chunks are written, each at the end of its list, and the
+  // counts tell the passes apart: n_chunks[0..1] (gate/up) count list A with
+  // them and list B without, n_chunks[2..3] (down) the other way round.  With
+  // one list, or no routed group in list B (a launch of only the shared chunks
+  // would leave most CUs idle), list A holds them for both passes.
+  const bool split = cut.bm_b != 0 && total_b > 0;
+  const int nsa = (int)((shared_rows + cut.bm_a - 1) / cut.bm_a);
+  const int nsb = split ? (int)((shared_rows + cut.bm_b - 1) / cut.bm_b) : 0;
+  auto put = [&](Chunk* list, int base, int nsh) {
+    for (int c = tid; c < nsh; c += kScanThreads) {
+      const int64_t r0 = c * shared_rows / nsh, r1 = (c + 1) * shared_rows / nsh;
+      Chunk ck;
+      ck.group = E;
+      ck.row0 = (int)(shared_row0 + r0);
+      ck.nrows = (int)(r1 - r0);
+      ck.gfirst = base;
+      ck.gcount = nsh;
+      ck.pad[0] = ck.pad[1] = ck.pad[2] = 0;
+      list[base + c] = ck;
+    }
+  };
+  put(chunks, total_a, nsa);
+  if (split) put(chunks + cut.off_b, total_b, nsb);
   if (tid == 0) {
-    n_chunks[0] = total_a + (sh_a ? nsh : 0);
-    if (cut.bm_b != 0) n_chunks[1] = total_b + (sh_a ? 0 : nsh);
+    n_chunks[0] = total_a + nsa;
+    n_chunks[1] = cut.bm_b != 0 ? total_b : 0;
+    n_chunks[2] = split ? total_a : total_a + nsa;
+    n_chunks[3] = split ? total_b + nsb : n_chunks[1];
   }
 }
 
