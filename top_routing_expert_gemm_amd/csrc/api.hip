@@ -107,6 +107,30 @@ inline char* at(P* base, size_t off) {
 
 inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 
+// Compute units of the current device (queried once per device; 0 if the query fails).
+int device_cus() {
+  constexpr int kDevs = 64;
+  static std::once_flag once[kDevs];
+  static int cus[kDevs];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
+  std::call_once(once[dev], [dev] {
+    int v = 0;
+    cus[dev] = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? v : 0;
+  });
+  return cus[dev];
+}
+
+// The chunk cut of plan p with what the dispatch step needs to place the shared
+// group's gate/up chunks: the device's compute units and the gate/up pass's
+// tiles per chunk (128 output columns each, gate and up side by side).
+ChunkCut rounds_cut(const ChunkPlan& p, const moe_config* c) {
+  ChunkCut cut = p.cut;
+  cut.cus = device_cus();
+  cut.nt = (int)((c->I + 127) / 128);
+  return cut;
+}
+
 moe_status check_ws(const moe_config* c, void* ws, size_t ws_bytes) {
   if (ws == nullptr) return MOE_ERR_WORKSPACE;
   if (ws_bytes < layout(c).total) return MOE_ERR_WORKSPACE;
@@ -286,7 +310,7 @@ moe_status moe_dispatch(const moe_config* c, const int32_t* topk_idx, const void
   const Layout L = layout(c);
   HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), topk_idx, counts, offsets, row_of_slot, token_of_row,
                           at(ws, L.dscratch), reinterpret_cast<Chunk*>(at(ws, L.chunks)),
-                          reinterpret_cast<int32_t*>(at(ws, L.n_chunks)), L.plan.cut, 0, 0, S(stream)));
+                          reinterpret_cast<int32_t*>(at(ws, L.n_chunks)), rounds_cut(L.plan, c), 0, 0, S(stream)));
   if (x_perm != nullptr)
     HIP_TRY(launch_gather(x, token_of_row, offsets, c->E, c->T * c->k, c->H, c->dtype, x_perm, S(stream)));
   return MOE_OK;
@@ -411,14 +435,14 @@ static moe_status forward_impl(const moe_config* c, const moe_weights* w, const 
   if (c->dtype == MOE_BF16) {
     HIP_TRY(launch_route_dispatch(*c, x, w->w_router, w->router_bias, route_sel_of(*c, w->score_bias, r.scores),
                                   r.topk_idx, r.topk_w, at(ws, L.rscratch), cap_of(c), r.counts, r.offsets,
-                                  r.row_of_slot, r.token_of_row, at(ws, L.dscratch), chunks, nch, L.plan.cut, sh, Tk,
+                                  r.row_of_slot, r.token_of_row, at(ws, L.dscratch), chunks, nch, rounds_cut(L.plan, c), sh, Tk,
                                   s, [&] { return mark(1); }));
   } else {
     HIP_TRY(launch_route(*c, x, w->w_router, w->router_bias, route_sel_of(*c, w->score_bias, r.scores),
                          r.topk_idx, r.topk_w, s));
     HIP_TRY(mark(1));
     HIP_TRY(launch_dispatch(c->T, c->k, c->E, cap_of(c), r.topk_idx, r.counts, r.offsets, r.row_of_slot,
-                            r.token_of_row, at(ws, L.dscratch), chunks, nch, L.plan.cut, sh, Tk, s));
+                            r.token_of_row, at(ws, L.dscratch), chunks, nch, rounds_cut(L.plan, c), sh, Tk, s));
   }
   HIP_TRY(mark(2));
   GemmArgs g{};
@@ -642,7 +666,7 @@ moe_status moe_forward_ec(const moe_config* c, const moe_weights* w, const void*
                              reinterpret_cast<int32_t*>(at(ws, L.topk_idx)), reinterpret_cast<float*>(at(ws, L.topk_w)),
                              at(ws, L.rscratch), s));
   HIP_TRY(launch_ec_select(o.scores, c->T, c->E, L.C, o.token_of_row, o.row_of_pair, s));
-  HIP_TRY(launch_chunks_uniform(c->E, L.C, sh, R, chunks, nch, L.plan.cut, s));
+  HIP_TRY(launch_chunks_uniform(c->E, L.C, sh, R, chunks, nch, rounds_cut(L.plan, c), s));
   GemmArgs g{};
   g.A = x;
   g.gather = o.token_of_row;

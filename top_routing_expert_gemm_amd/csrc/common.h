@@ -55,14 +55,23 @@ constexpr int kGemmBMf32 = 64;
 constexpr int kGemvBM = 16;
 constexpr int64_t kGemvMaxT = 16;
 
+// Chunks of one group that the GEMM tile order interleaves per n-tile (they
+// share each weight tile, read once into one XCD's L2).
+constexpr int kChunkSuper = 4;
+
 // How the dispatch step cuts expert groups into row chunks: one list of bm_a-row
 // chunks (bm_b == 0), or two lists, A of bm_a-row chunks at chunks[0] and B of
 // bm_b-row chunks at chunks[off_b], each group going to the list where it costs
-// less (decided on the device from its row count).
+// less (decided on the device from its row count).  cus (the device's compute
+// units) and nt (gate/up tiles per chunk) let the dispatch step place the
+// shared group's gate/up chunks so that both lists end on nearly full rounds
+// of tiles (0: unknown, the shared group's gate/up chunks all go to list A).
 struct ChunkCut {
   int bm_a;
   int bm_b;
   int64_t off_b;
+  int cus = 0;
+  int nt = 0;
 };
 
 // Max chunk-list entries for `rows_max` routed rows over E groups (+ shared rows).

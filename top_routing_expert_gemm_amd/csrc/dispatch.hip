@@ -162,35 +162,90 @@ __device__ void emit_chunks(int e_valid, int load, int row0, int E, const ChunkC
   __syncthreads();
   // The shared group.  Its chunks share one weight tile per n-tile, which the
   // tile order streams once per group of chunks, so the 320-row list's fewer
-  // weight streams buy it little: the gate/up pass takes it as chunks of list A
-  // (the 256-row kernel has the higher rate per row).  The down pass (the
-  // 320-row kernel over both lists) takes it as fewer, taller chunks of list B.
-  // Both sets of chunks are written, each at the end of its list, and the
-  // counts tell the passes apart: n_chunks[0..1] (gate/up) count list A with
-  // them and list B without, n_chunks[2..3] (down) the other way round.  With
-  // one list, or no routed group in list B (a launch of only the shared chunks
-  // would leave most CUs idle), list A holds them for both passes.
+  // weight streams buy it little; the down pass (the 320-row kernel over both
+  // lists) takes it as fewer, taller chunks of list B, the gate/up pass mostly
+  // as chunks of list A (the 256-row kernel has the higher rate per row).  Each
+  // gate/up launch ends on a partly filled round of tiles, so the gate/up pass
+  // takes the first j of list B's shared chunks as well, and list A covers
+  // the rows after them: j is the count (0 .. all, in whole groups of
+  // kChunkSuper chunks) that minimises the rounds
+  // of tiles of both launches (cus compute units, nt tiles per chunk), each
+  // round weighted by its kernel's cost per chunk (22 : 25, as above).
+  // Layout: list A = [routed A][shared rows rb .. R in nsa chunks], list B =
+  // [routed B][shared rows 0 .. R in nsb chunks, the first j one weight-sharing
+  // group, the rest another].  Counts: n_chunks[0..1] (gate/up) total_a + nsa,
+  // total_b + j; n_chunks[2..3] (down) total_a, total_b + nsb.  With one list,
+  // or no routed group in list B (a launch of only the shared chunks would
+  // leave most CUs idle), list A holds the shared chunks for both passes.
   const bool split = cut.bm_b != 0 && total_b > 0;
-  const int nsa = (int)((shared_rows + cut.bm_a - 1) / cut.bm_a);
-  const int nsb = split ? (int)((shared_rows + cut.bm_b - 1) / cut.bm_b) : 0;
-  auto put = [&](Chunk* list, int base, int nsh) {
-    for (int c = tid; c < nsh; c += kScanThreads) {
-      const int64_t r0 = c * shared_rows / nsh, r1 = (c + 1) * shared_rows / nsh;
+  const int64_t R = shared_rows;
+  const int nsb = split ? (int)((R + cut.bm_b - 1) / cut.bm_b) : 0;
+  // One wave evaluates the candidates on wave-uniform (scalar) values and
+  // hands j to the others through LDS.
+  __shared__ int sh_j;
+  if (tid < kWave) {
+    int j = 0;
+    const int ta = __builtin_amdgcn_readfirstlane(total_a), tb = __builtin_amdgcn_readfirstlane(total_b);
+    if (split && R > 0 && cut.cus > 0 && cut.nt > 0) {
+      // Exact integers with no division inside the loop: as jj grows,
+      // floor(jj R / nsb) advances by R / nsb plus a carried remainder, and
+      // the chunk and round counts move by steps that a comparison finds.
+      // Ties keep the smaller j.
+      const int r32 = (int)R, q0 = r32 / nsb, m0 = r32 % nsb, nt = cut.nt, cus = cut.cus, bma = cut.bm_a;
+      int fl = 0, rem = 0;                                  // floor(jj R / nsb) = fl
+      int na = (r32 + bma - 1) / bma;                       // shared chunks in list A
+      int ra_rounds = ((ta + na) * nt + cus - 1) / cus;
+      int rb_rounds = (tb * nt + cus - 1) / cus;
+      int best = -1;
+      for (int jj = 0; jj <= nsb; ++jj) {
+        if (jj > 0) {
+          fl += q0;
+          rem += m0;
+          if (rem >= nsb) {
+            ++fl;
+            rem -= nsb;
+          }
+        }
+        const int ra = r32 - fl;
+        while (na > 0 && (na - 1) * bma >= ra) --na;
+        while (ra_rounds > 0 && (ra_rounds - 1) * cus >= (ta + na) * nt) --ra_rounds;
+        while (rb_rounds * cus < (tb + jj) * nt) ++rb_rounds;
+        const int cost = 22 * ra_rounds + 25 * rb_rounds;
+        // j whole groups of kChunkSuper chunks (or all of them): the rest of the
+        // shared chunks then start on a group boundary, so the tile order keeps
+        // each of their weight tiles within one XCD
+        if (jj % kChunkSuper != 0 && jj != nsb) continue;
+        if (best < 0 || cost < best) {
+          best = cost;
+          j = jj;
+        }
+      }
+    }
+    if (tid == 0) sh_j = j;
+  }
+  __syncthreads();
+  const int j = sh_j;
+  const int64_t rb = nsb > 0 ? j * R / nsb : 0;  // shared rows the gate/up pass takes from list B
+  const int nsa = (int)((R - rb + cut.bm_a - 1) / cut.bm_a);
+  // chunk c of n over shared rows [lo, hi), in a weight-sharing group of gc chunks from gf
+  auto put = [&](Chunk* list, int base, int n, int64_t lo, int64_t hi, int gf0, int gc0, int gf1, int gc1, int cut_at) {
+    for (int c = tid; c < n; c += kScanThreads) {
+      const int64_t r0 = lo + c * (hi - lo) / n, r1 = lo + (c + 1) * (hi - lo) / n;
       Chunk ck;
       ck.group = E;
       ck.row0 = (int)(shared_row0 + r0);
       ck.nrows = (int)(r1 - r0);
-      ck.gfirst = base;
-      ck.gcount = nsh;
+      ck.gfirst = c < cut_at ? gf0 : gf1;
+      ck.gcount = c < cut_at ? gc0 : gc1;
       ck.pad[0] = ck.pad[1] = ck.pad[2] = 0;
       list[base + c] = ck;
     }
   };
-  put(chunks, total_a, nsa);
-  if (split) put(chunks + cut.off_b, total_b, nsb);
+  put(chunks, total_a, nsa, rb, R, total_a, nsa, total_a, nsa, nsa);
+  if (split) put(chunks + cut.off_b, total_b, nsb, 0, R, total_b, j, total_b + j, nsb - j, j);
   if (tid == 0) {
     n_chunks[0] = total_a + nsa;
-    n_chunks[1] = cut.bm_b != 0 ? total_b : 0;
+    n_chunks[1] = split ? total_b + j : (cut.bm_b != 0 ? total_b : 0);
     n_chunks[2] = split ? total_a : total_a + nsa;
     n_chunks[3] = split ? total_b + nsb : n_chunks[1];
   }

@@ -63,7 +63,7 @@ constexpr int RB = BMW / 32;   // 32-row MFMA blocks per wave (5)
 constexpr int BN = 256;
 constexpr int NT = 512;
 constexpr int NWAVES = NT / 64;
-constexpr int SUPER = 4;       // chunks of one group interleaved per n-tile
+constexpr int SUPER = kChunkSuper;  // chunks of one group interleaved per n-tile
 constexpr int BK = 32;         // K per step (and per B stage)
 constexpr int B_BLK = BN / 16 / NWAVES;   // B blocks (16 rows x 64 B = 1 KB) per wave per stage (2)
 constexpr int A_BLK = BM / 8 / NWAVES;    // A blocks (8 rows x 128 B = 1 KB) per wave per 64-wide A stage (5)
