@@ -168,9 +168,11 @@ __device__ void emit_chunks(int e_valid, int load, int row0, int E, const ChunkC
   // gate/up launch ends on a partly filled round of tiles, so the gate/up pass
   // takes the first j of list B's shared chunks as well, and list A covers
   // the rows after them: j is the count (0 .. all, in whole groups of
-  // kChunkSuper chunks) that minimises the rounds
-  // of tiles of both launches (cus compute units, nt tiles per chunk), each
-  // round weighted by its kernel's cost per chunk (22 : 25, as above).
+  // kChunkSuper chunks, so that the remaining shared chunks start on a group
+  // boundary and the tile order keeps each of their weight tiles within one
+  // XCD) that minimises the rounds of tiles of both launches (cus compute
+  // units, nt tiles per chunk), each round weighted by its kernel's cost per
+  // chunk (22 : 25, as above).
   // Layout: list A = [routed A][shared rows rb .. R in nsa chunks], list B =
   // [routed B][shared rows 0 .. R in nsb chunks, the first j one weight-sharing
   // group, the rest another].  Counts: n_chunks[0..1] (gate/up) total_a + nsa,
@@ -187,37 +189,26 @@ __device__ void emit_chunks(int e_valid, int load, int row0, int E, const ChunkC
     int j = 0;
     const int ta = __builtin_amdgcn_readfirstlane(total_a), tb = __builtin_amdgcn_readfirstlane(total_b);
     if (split && R > 0 && cut.cus > 0 && cut.nt > 0) {
-      // Exact integers with no division inside the loop: as jj grows,
-      // floor(jj R / nsb) advances by R / nsb plus a carried remainder, and
-      // the chunk and round counts move by steps that a comparison finds.
-      // Ties keep the smaller j.
-      const int r32 = (int)R, q0 = r32 / nsb, m0 = r32 % nsb, nt = cut.nt, cus = cut.cus, bma = cut.bm_a;
-      int fl = 0, rem = 0;                                  // floor(jj R / nsb) = fl
-      int na = (r32 + bma - 1) / bma;                       // shared chunks in list A
-      int ra_rounds = ((ta + na) * nt + cus - 1) / cus;
-      int rb_rounds = (tb * nt + cus - 1) / cus;
-      int best = -1;
-      for (int jj = 0; jj <= nsb; ++jj) {
-        if (jj > 0) {
-          fl += q0;
-          rem += m0;
-          if (rem >= nsb) {
-            ++fl;
-            rem -= nsb;
-          }
-        }
-        const int ra = r32 - fl;
-        while (na > 0 && (na - 1) * bma >= ra) --na;
-        while (ra_rounds > 0 && (ra_rounds - 1) * cus >= (ta + na) * nt) --ra_rounds;
-        while (rb_rounds * cus < (tb + jj) * nt) ++rb_rounds;
-        const int cost = 22 * ra_rounds + 25 * rb_rounds;
-        // j whole groups of kChunkSuper chunks (or all of them): the rest of the
-        // shared chunks then start on a group boundary, so the tile order keeps
-        // each of their weight tiles within one XCD
-        if (jj % kChunkSuper != 0 && jj != nsb) continue;
-        if (best < 0 || cost < best) {
-          best = cost;
-          j = jj;
+      // The rounds of list A fall as j grows, those of list B rise, so for
+      // each round count of list B the largest admissible j is the only
+      // candidate: at most a few, each a few exact integer divisions (no
+      // loop over every j on this critical path).  Ties keep the smaller j.
+      const int r32 = (int)R, nt = cut.nt, cus = cut.cus, bma = cut.bm_a;
+      auto cost = [&](int jj) {
+        const int ra = r32 - (int)((int64_t)jj * r32 / nsb);
+        const int na = ta + (ra + bma - 1) / bma;
+        return 22 * ((na * nt + cus - 1) / cus) + 25 * (((tb + jj) * nt + cus - 1) / cus);
+      };
+      int best = cost(0);
+      const int k0 = (tb * nt + cus - 1) / cus, k1 = ((tb + nsb) * nt + cus - 1) / cus;
+      for (int kk = k0; kk <= k1; ++kk) {
+        int jm = min(nsb, kk * cus / nt - tb);
+        if (jm < nsb) jm = jm / kChunkSuper * kChunkSuper;  // whole groups of kChunkSuper (or all)
+        if (jm <= 0) continue;
+        const int cj = cost(jm);
+        if (cj < best) {
+          best = cj;
+          j = jm;
         }
       }
     }
