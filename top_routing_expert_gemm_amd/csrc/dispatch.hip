@@ -22,7 +22,8 @@
 //   3. finalize    every block's workgroup scans the E loads (min(count, cap))
 //                  into offsets itself; rank = block base + local rank; kept iff
 //                  rank < cap; row_of_slot / token_of_row.  The first workgroup
-//                  also writes offsets and the GEMM chunk lists.
+//                  also writes offsets and the GEMM chunk lists (the shared
+//                  group's chunks placed per pass, with four list counts).
 // Batches of at most 1024 assignments do all of it in one workgroup (for the
 // layer's decode batches, together with the router's select step).
 #include <functional>

@@ -6,7 +6,14 @@
 // renormalisation, routed_scaling_factor); amazingdata.cn "moe-routing-hardest"
 // (the routing steps).
 //
-// bf16 path: one workgroup = 32 tokens x all E experts.  The 32 x 64 token tile is
+// Kernels: the fused router of the stage entry point (route_bf16_kernel, below);
+// for the layer, split-K partial logits that the select step (dispatch.hip) adds
+// in slice order: route_gemm_kernel for batches above 16 tokens and E <= 256
+// (128-token tiles, loader waves streaming the token rows, MFMA waves loading the
+// router weights), route_gemv_kernel for batches of <= 16 tokens,
+// route_partial_bf16_kernel for E > 256; route_f32_kernel for fp32.
+//
+// Fused bf16 path: one workgroup = 32 tokens x all E experts.  The 32 x 64 token tile is
 // staged in LDS (double buffered, XOR-swizzled 16-byte chunks) and shared by the
 // four waves; each wave streams its own 32-expert blocks of W_router straight
 // into MFMA operand registers and accumulates z = x . W^T with
