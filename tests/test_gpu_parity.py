@@ -70,6 +70,11 @@ SMALL = {
                                  routed_scaling_factor=2.5, cfg_id=126),
     "bf16_router_E200_slices": MoEShape("bf16_router_E200_slices", T=4100, H=1344, I=64, E=200, k=8,
                                         cfg_id=127),
+    # one partly filled 128-token tile: 17 tokens (the smallest batch above the streaming path) and 40
+    # tokens over three K steps (40 and 48 experts: two 32-expert blocks, the second partly padded)
+    "bf16_router_T17": MoEShape("bf16_router_T17", T=17, H=256, I=64, E=40, k=2, cfg_id=142),
+    "bf16_router_T40": MoEShape("bf16_router_T40", T=40, H=192, I=64, E=48, k=3, gate=GATE_SIGMOID,
+                                routed_scaling_factor=2.5, n_shared=1, I_shared=64, cfg_id=143),
     "fp32_tiny": WORKLOADS[TINY],
     "fp32_sigmoid_shared_capacity": MoEShape("fp32_sigmoid_shared_capacity", T=200, H=192, I=128, E=8, k=3,
                                              gate=GATE_SIGMOID, capacity_factor=1.0, n_shared=1, I_shared=128,
