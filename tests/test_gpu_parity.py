@@ -72,6 +72,15 @@ SMALL = {
                                         cfg_id=127),
     # one partly filled 128-token tile: 17 tokens (the smallest batch above the streaming path) and 40
     # tokens over three K steps (40 and 48 experts: two 32-expert blocks, the second partly padded)
+    # the shared expert's gate/up chunks split between the lists so that both gate/up launches end on
+    # full rounds of tiles (this seed's routing, 256 compute units): 4 experts of 279..317 rows, all
+    # in the 320-row list, and the gate/up pass takes both 320-row shared chunks there (the 256-row
+    # list stays empty); 20 experts, 10 groups per list, the gate/up pass takes 4 of the 8 shared
+    # chunks from the 320-row list and the rest of the shared rows in 256-row chunks
+    "bf16_shared_all_in_b": MoEShape("bf16_shared_all_in_b", T=600, H=128, I=4096, E=4, k=2, n_shared=1,
+                                     I_shared=4096, cfg_id=150),
+    "bf16_shared_split": MoEShape("bf16_shared_split", T=2500, H=128, I=2048, E=20, k=2, gate=GATE_SIGMOID,
+                                  routed_scaling_factor=2.5, n_shared=1, I_shared=2048, cfg_id=150),
     "bf16_router_T17": MoEShape("bf16_router_T17", T=17, H=256, I=64, E=40, k=2, cfg_id=142),
     "bf16_router_T40": MoEShape("bf16_router_T40", T=40, H=192, I=64, E=48, k=3, gate=GATE_SIGMOID,
                                 routed_scaling_factor=2.5, n_shared=1, I_shared=64, cfg_id=143),
